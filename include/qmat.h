@@ -1,0 +1,166 @@
+/*
+ * qmat.h — C ABI of the block-quantized weight matmul for MI355X (gfx950).
+ *
+ * Three operations, all enqueued asynchronously on a caller-supplied HIP
+ * stream:
+ *   qmat_quantize  fp32 matrix  -> packed weight (or activation) blocks
+ *   qmat_gemv      packed W × fp32 x        -> fp32 y        (decode)
+ *   qmat_gemm      packed W × Q8_0 X blocks -> fp32 Y        (prefill)
+ *
+ * Sources. Citations name the web page and the section or table of it
+ * that fixes the fact:
+ *   [LC05] "05. llama.cpp：从 GGUF 文件到本地推理服务" (niuwancheng.cn);
+ *          table in section "量化类型：Q4_K_M 到底是什么" (quant families),
+ *          section "性能直觉：带宽决定 Decode，算力决定 Prefill".
+ *   [LCHW] "llama.cpp 原理：如何在普通硬件跑本地大模型"; section
+ *          "量化：内存真正去哪了" (Q4_0: 32 weights, one fp16 scale,
+ *          18 bytes, 4.5 bits per weight).
+ *   [KVQ]  lpnh.cn KV-cache article; section "kv-mean-center 进阶技巧",
+ *          paragraph "问题" (Q4_0 is symmetric: value ≈ scale × q).
+ *   [BARE] xdnf.cn llama.cpp article; section 3.2 (dequant snippet: low
+ *          nibbles are the first 16 elements of a block, high nibbles the
+ *          last 16; fp16 parameters precede the nibbles).
+ *
+ * Block formats (byte-exact; little-endian; fp16 = IEEE binary16):
+ *   Q4_0  (32 weights, 18 B)  [LCHW], [LC05 table], [KVQ], [BARE 3.2]
+ *         [0:2]  fp16 scale d
+ *         [2:18] 16 code bytes; byte t holds element t in its low nibble
+ *                and element t+16 in its high nibble; code c in [0,15]
+ *                stands for the integer c-8; weight = d*(c-8).
+ *   Q8_0  (32 weights, 34 B)  [LC05 table] ("about 8.5 bits")
+ *         [0:2]  fp16 scale d;  [2:34] int8 q[0..31];  weight = d*q.
+ *   Q4_K  (256 weights = 8 sub-blocks of 32, 144 B)  [LC05 table]
+ *         ("256-weight superblock, eight 32-element sub-blocks, sub-block
+ *         scales themselves quantized to 6 bits"); the byte packing is this
+ *         library's own and is not claimed compatible with GGUF's q4_K:
+ *         [0:2]   fp16 super-scale d
+ *         [2:4]   fp16 super-min  dmin
+ *         [4:16]  96-bit little-endian integer V; 6-bit field f is
+ *                 (V >> 6f) & 63; sc_j = field j, mn_j = field 8+j (j<8)
+ *         [16:144] codes; sub-block j uses bytes 16+16j .. 16+16j+15 with
+ *                 the Q4_0 nibble order; q in [0,15];
+ *                 weight = (d*sc_j)*q - (dmin*mn_j).
+ *
+ * Matrix layout: a [rows][K] matrix is rows*(K/block_elems) blocks, row
+ * after row, blocks running along K, no padding. Rows are therefore
+ * qmat_row_bytes(fmt, K) bytes apart.
+ *
+ * Common contract for every entry point:
+ *   - Pointers W, x, y, blocks, X_q8, Y are DEVICE pointers owned by the
+ *     caller, each 16-byte aligned (QMAT_E_ALIGN otherwise). The library
+ *     keeps no pointer after return and owns no device memory.
+ *   - stream is a hipStream_t (NULL = the legacy default stream). The call
+ *     returns once the work is enqueued; results are ready when the stream
+ *     reaches that point.
+ *   - Argument errors are detected on the host before anything is
+ *     enqueued and are returned synchronously; a failed launch returns
+ *     QMAT_E_HIP. Device faults surface at the caller's next
+ *     synchronisation, as for any HIP kernel.
+ *   - Inputs and outputs must not overlap. Identical inputs give
+ *     bit-identical outputs (no atomics, fixed reduction order).
+ *   - Limits: 0 <= rows, M, N <= 2^31-1; 0 <= K <= 2^31-1; K a multiple of
+ *     qmat_block_elems(fmt); rows*row_bytes must fit in int64. A zero M or
+ *     N enqueues nothing. K == 0 is valid: quantize writes nothing, gemv
+ *     and gemm write zeros (the empty sum).
+ *   - Thread safe; no global mutable state.
+ */
+#ifndef QMAT_H
+#define QMAT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum qmat_fmt {
+  QMAT_Q4_0 = 0,
+  QMAT_Q8_0 = 1,
+  QMAT_Q4_K = 2
+} qmat_fmt;
+
+typedef enum qmat_status {
+  QMAT_OK = 0,
+  QMAT_E_FMT = 1,   /* unknown format, or format not allowed here        */
+  QMAT_E_SHAPE = 2, /* negative size, K not a multiple of the block, or
+                       a size beyond the limits above                    */
+  QMAT_E_NULL = 3,  /* a required pointer is NULL                         */
+  QMAT_E_HIP = 4,   /* the HIP launch itself failed                       */
+  QMAT_E_ALIGN = 5  /* a pointer is not 16-byte aligned                   */
+} qmat_status;
+
+/* Elements per block: 32 (Q4_0, Q8_0), 256 (Q4_K); 0 for an unknown fmt. */
+int64_t qmat_block_elems(int fmt);
+
+/* Bytes per block: 18 (Q4_0) [LCHW], 34 (Q8_0), 144 (Q4_K); 0 if unknown. */
+int64_t qmat_block_bytes(int fmt);
+
+/* Bytes of one packed row of K elements; -1 for an unknown fmt, a negative
+ * K or a K that is not a multiple of the block. */
+int64_t qmat_row_bytes(int fmt, int64_t K);
+
+/* Static English text for a status code (never NULL). */
+const char *qmat_strerror(int status);
+
+/*
+ * qmat_quantize — round-to-nearest block quantization of an fp32 matrix.
+ *   W:      fp32 [rows][K], row-major.
+ *   blocks: output, rows*qmat_row_bytes(fmt,K) bytes in the layout above.
+ *   Rules (per block, fp32 IEEE arithmetic, correctly rounded division,
+ *   rnd = round half away from zero, fp16 = round to nearest even with
+ *   subnormals, codes computed from the stored fp16 scale):
+ *     Q4_0: d = amax/7; D = fp16(d); c = clamp(rnd(w/D),-8,7)+8 (8 if D==0)
+ *           [LCHW] one fp16 scale per 32 weights; [KVQ] symmetric.
+ *     Q8_0: d = amax/127; q = clamp(rnd(w/D),-127,127) (0 if D==0).
+ *           With fmt = QMAT_Q8_0 this is also the activation quantizer
+ *           whose output qmat_gemm consumes.
+ *     Q4_K: per sub-block j: lo = min(0, min w), hi = max w,
+ *           scale_j = (hi-lo)/15, off_j = -lo; d = max scale_j / 63,
+ *           dmin = max off_j / 63 (both stored fp16); sc_j, mn_j =
+ *           clamp(rnd(scale_j/D),0,63), clamp(rnd(off_j/Dmin),0,63);
+ *           q = clamp(rnd((w + Dmin*mn_j)/(D*sc_j)),0,15) (0 if D*sc_j==0).
+ *           [LC05 table] two-level scaling with 6-bit sub-block scales.
+ *   Non-finite inputs or a scale above 65504 give unspecified bytes (never
+ *   a fault).
+ */
+int qmat_quantize(int fmt, const float *W, void *blocks, int64_t rows,
+                  int64_t K, void *stream);
+
+/*
+ * qmat_gemv — decode-time matrix-vector product (one token):
+ *   y[m] = sum_k dequant(W)[m][k] * x[k],  m < M.
+ *   [LC05 "带宽决定 Decode"]: every weight byte is read once per token, so
+ *   this is bound by HBM bandwidth.
+ *   blocks: W in fmt (Q4_0, Q8_0 or Q4_K), M rows of K.
+ *   x: fp32 [K]; y: fp32 [M], overwritten.
+ *   Accuracy: relative L2 error against the exact (fp64) product of the
+ *   dequantized weights with x is below 1e-3 for finite x; internally x is
+ *   rescaled per 32 elements by a power of two and rounded to fp16, and
+ *   products are accumulated in fp32.
+ */
+int qmat_gemv(int fmt, const void *blocks, const float *x, float *y,
+              int64_t M, int64_t K, void *stream);
+
+/*
+ * qmat_gemm — prefill matrix product over N tokens:
+ *   Y[n][m] = sum_k dequant(W)[m][k] * dequant(X_q8)[n][k].
+ *   [LC05 "算力决定 Prefill"]: one weight read serves many tokens, so this
+ *   is bound by the matrix cores (int8 MFMA over each 32-element block,
+ *   then the two fp16 block scales applied in fp32).
+ *   blocks: W in fmt (Q4_0, Q8_0 or Q4_K), M rows of K.
+ *   X_q8: Q8_0 blocks of the activations, N rows of K, exactly as
+ *         qmat_quantize(QMAT_Q8_0, X, X_q8, N, K, stream) writes them.
+ *   Y: fp32 [N][M] (token-major), overwritten.
+ *   Accuracy: relative L2 error against the exact (fp64) product of the
+ *   dequantized operands is below 2e-3; the per-block integer dot products
+ *   are exact.
+ */
+int qmat_gemm(int fmt, const void *blocks, const void *X_q8, float *Y,
+              int64_t M, int64_t K, int64_t N, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QMAT_H */
