@@ -1,0 +1,156 @@
+"""ctypes binding of libqmat.so (C ABI in include/qmat.h).
+
+Argument marshalling only: torch device tensors supply the memory and
+torch's current HIP stream orders the work; every step of the computation
+runs in the library's kernels. There is no CPU fallback: without the built
+library, or with a tensor that is not on a GPU, the calls raise.
+
+torch is imported before the library is loaded so that the library binds to
+the HIP runtime torch already loaded (both name it libamdhip64.so.7).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+Q4_0, Q8_0, Q4_K = 0, 1, 2
+FORMATS = {"q4_0": Q4_0, "q8_0": Q8_0, "q4_k": Q4_K}
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqmat.so")
+_lib = None
+
+
+class QmatError(RuntimeError):
+    """A non-zero status returned by the C ABI."""
+
+    def __init__(self, func: str, status: int, message: str):
+        super().__init__(f"{func}: {message} (status {status})")
+        self.status = status
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libqmat.so once (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is missing: build it with "
+                           "`python -m block_quantized_weight_qmat_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    i64, p, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+    lib.qmat_block_elems.argtypes = [i32]
+    lib.qmat_block_elems.restype = i64
+    lib.qmat_block_bytes.argtypes = [i32]
+    lib.qmat_block_bytes.restype = i64
+    lib.qmat_row_bytes.argtypes = [i32, i64]
+    lib.qmat_row_bytes.restype = i64
+    lib.qmat_strerror.argtypes = [i32]
+    lib.qmat_strerror.restype = ctypes.c_char_p
+    lib.qmat_quantize.argtypes = [i32, p, p, i64, i64, p]
+    lib.qmat_quantize.restype = i32
+    lib.qmat_gemv.argtypes = [i32, p, p, p, i64, i64, p]
+    lib.qmat_gemv.restype = i32
+    lib.qmat_gemm.argtypes = [i32, p, p, p, i64, i64, i64, p]
+    lib.qmat_gemm.restype = i32
+    _lib = lib
+    return lib
+
+
+def _fmt(fmt) -> int:
+    f = FORMATS[fmt.lower()] if isinstance(fmt, str) else int(fmt)
+    if f not in (Q4_0, Q8_0, Q4_K):
+        raise ValueError(f"unknown format {fmt!r}")
+    return f
+
+
+def _check(func: str, status: int):
+    if status != 0:
+        msg = load_library().qmat_strerror(status).decode()
+        raise QmatError(func, status, msg)
+
+
+def block_elems(fmt) -> int:
+    return int(load_library().qmat_block_elems(_fmt(fmt)))
+
+
+def block_bytes(fmt) -> int:
+    return int(load_library().qmat_block_bytes(_fmt(fmt)))
+
+
+def row_bytes(fmt, K: int) -> int:
+    rb = int(load_library().qmat_row_bytes(_fmt(fmt), int(K)))
+    if rb < 0:
+        raise ValueError(f"K={K} is not a multiple of the block size of format {fmt!r}")
+    return rb
+
+
+def _gpu(t: torch.Tensor, name: str, dtype: torch.dtype):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a GPU tensor (no CPU path exists)")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def quantize(fmt, W: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """fp32 [rows, K] -> uint8 [rows, row_bytes(fmt, K)] packed blocks."""
+    f = _fmt(fmt)
+    _gpu(W, "W", torch.float32)
+    if W.dim() != 2:
+        raise ValueError("W must be 2-D [rows, K]")
+    rows, K = W.shape
+    rb = row_bytes(f, K)
+    if out is None:
+        out = torch.empty((rows, rb), dtype=torch.uint8, device=W.device)
+    _gpu(out, "out", torch.uint8)
+    if out.numel() != rows * rb:
+        raise ValueError("out has the wrong size")
+    _check("qmat_quantize", load_library().qmat_quantize(
+        f, W.data_ptr(), out.data_ptr(), rows, K, _stream(W)))
+    return out
+
+
+def gemv(fmt, blocks: torch.Tensor, x: torch.Tensor, M: int, K: int,
+         out: torch.Tensor | None = None) -> torch.Tensor:
+    """y[M] = dequant(W) @ x, W given as packed blocks of M rows of K."""
+    f = _fmt(fmt)
+    _gpu(blocks, "blocks", torch.uint8)
+    _gpu(x, "x", torch.float32)
+    if blocks.numel() != M * row_bytes(f, K) or x.numel() != K:
+        raise ValueError("blocks or x does not match M, K")
+    if out is None:
+        out = torch.empty(M, dtype=torch.float32, device=x.device)
+    _gpu(out, "out", torch.float32)
+    if out.numel() != M:
+        raise ValueError("out must hold M values")
+    _check("qmat_gemv", load_library().qmat_gemv(
+        f, blocks.data_ptr(), x.data_ptr(), out.data_ptr(), M, K, _stream(x)))
+    return out
+
+
+def gemm(fmt, blocks: torch.Tensor, Xq: torch.Tensor, M: int, K: int, N: int,
+         out: torch.Tensor | None = None) -> torch.Tensor:
+    """Y[N, M] = dequant(Xq) @ dequant(W)^T; Xq are Q8_0 activation blocks."""
+    f = _fmt(fmt)
+    _gpu(blocks, "blocks", torch.uint8)
+    _gpu(Xq, "Xq", torch.uint8)
+    if blocks.numel() != M * row_bytes(f, K) or Xq.numel() != N * row_bytes(Q8_0, K):
+        raise ValueError("blocks or Xq does not match M, K, N")
+    if out is None:
+        out = torch.empty((N, M), dtype=torch.float32, device=Xq.device)
+    _gpu(out, "out", torch.float32)
+    if out.numel() != N * M:
+        raise ValueError("out must hold N*M values")
+    _check("qmat_gemm", load_library().qmat_gemm(
+        f, blocks.data_ptr(), Xq.data_ptr(), out.data_ptr(), M, K, N, _stream(Xq)))
+    return out

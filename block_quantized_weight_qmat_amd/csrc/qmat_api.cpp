@@ -1,0 +1,121 @@
+// qmat_api.cpp — the C ABI declared in include/qmat.h.
+//
+// Every argument is validated on the host before anything is enqueued; the
+// launchers in quantize.hip / gemv.hip / gemm.hip then enqueue the kernels on
+// the caller's stream. No device memory is allocated and no state is kept.
+#include "qmat.h"
+
+#include <hip/hip_runtime_api.h>
+
+#include "qmat_launch.hpp"
+
+namespace {
+
+constexpr int64_t kMaxDim = 0x7FFFFFFFLL;
+
+bool fmt_ok(int fmt) { return fmt == QMAT_Q4_0 || fmt == QMAT_Q8_0 || fmt == QMAT_Q4_K; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// A buffer that must exist (non-empty) must be non-NULL and 16-byte aligned.
+int check_buf(const void* p, bool nonempty) {
+  if (!nonempty) return QMAT_OK;
+  if (p == nullptr) return QMAT_E_NULL;
+  if (!aligned16(p)) return QMAT_E_ALIGN;
+  return QMAT_OK;
+}
+
+// rows x K matrix in fmt: sizes in range, K a multiple of the block, and the
+// packed byte size representable.
+int check_shape(int fmt, int64_t rows, int64_t K) {
+  if (rows < 0 || K < 0 || rows > kMaxDim || K > kMaxDim) return QMAT_E_SHAPE;
+  const int64_t be = qmat_block_elems(fmt);
+  if (K % be != 0) return QMAT_E_SHAPE;
+  const int64_t rb = qmat_row_bytes(fmt, K);
+  if (rb > 0 && rows > INT64_MAX / rb) return QMAT_E_SHAPE;
+  if (rows > 0 && K > INT64_MAX / 4 / rows) return QMAT_E_SHAPE;
+  return QMAT_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? QMAT_OK : QMAT_E_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int64_t qmat_block_elems(int fmt) {
+  switch (fmt) {
+    case QMAT_Q4_0: return 32;
+    case QMAT_Q8_0: return 32;
+    case QMAT_Q4_K: return 256;
+    default: return 0;
+  }
+}
+
+int64_t qmat_block_bytes(int fmt) {
+  switch (fmt) {
+    case QMAT_Q4_0: return 18;
+    case QMAT_Q8_0: return 34;
+    case QMAT_Q4_K: return 144;
+    default: return 0;
+  }
+}
+
+int64_t qmat_row_bytes(int fmt, int64_t K) {
+  if (!fmt_ok(fmt) || K < 0) return -1;
+  const int64_t be = qmat_block_elems(fmt);
+  if (K % be != 0) return -1;
+  return K / be * qmat_block_bytes(fmt);
+}
+
+const char* qmat_strerror(int status) {
+  switch (status) {
+    case QMAT_OK: return "success";
+    case QMAT_E_FMT: return "unknown or unsupported block format";
+    case QMAT_E_SHAPE: return "invalid shape (negative, out of range, or K not a multiple of the block)";
+    case QMAT_E_NULL: return "required pointer is NULL";
+    case QMAT_E_HIP: return "HIP kernel launch failed";
+    case QMAT_E_ALIGN: return "pointer is not 16-byte aligned";
+    default: return "unknown status";
+  }
+}
+
+int qmat_quantize(int fmt, const float* W, void* blocks, int64_t rows, int64_t K,
+                  void* stream) {
+  if (!fmt_ok(fmt)) return QMAT_E_FMT;
+  int rc = check_shape(fmt, rows, K);
+  if (rc != QMAT_OK) return rc;
+  if (rows == 0 || K == 0) return QMAT_OK;  // nothing to read or write
+  if ((rc = check_buf(W, true)) != QMAT_OK) return rc;
+  if ((rc = check_buf(blocks, true)) != QMAT_OK) return rc;
+  return hip_status(
+      qmat::launch_quantize(fmt, W, blocks, rows, K, static_cast<hipStream_t>(stream)));
+}
+
+int qmat_gemv(int fmt, const void* blocks, const float* x, float* y, int64_t M, int64_t K,
+              void* stream) {
+  if (!fmt_ok(fmt)) return QMAT_E_FMT;
+  int rc = check_shape(fmt, M, K);
+  if (rc != QMAT_OK) return rc;
+  if (M == 0) return QMAT_OK;  // nothing to read or write
+  if ((rc = check_buf(blocks, K > 0)) != QMAT_OK) return rc;
+  if ((rc = check_buf(x, K > 0)) != QMAT_OK) return rc;
+  if ((rc = check_buf(y, true)) != QMAT_OK) return rc;
+  return hip_status(qmat::launch_gemv(fmt, blocks, x, y, M, K, static_cast<hipStream_t>(stream)));
+}
+
+int qmat_gemm(int fmt, const void* blocks, const void* X_q8, float* Y, int64_t M, int64_t K,
+              int64_t N, void* stream) {
+  if (!fmt_ok(fmt)) return QMAT_E_FMT;
+  int rc = check_shape(fmt, M, K);
+  if (rc != QMAT_OK) return rc;
+  if ((rc = check_shape(QMAT_Q8_0, N, K)) != QMAT_OK) return rc;
+  if (M == 0 || N == 0) return QMAT_OK;  // nothing to read or write
+  if ((rc = check_buf(blocks, K > 0)) != QMAT_OK) return rc;
+  if ((rc = check_buf(X_q8, K > 0)) != QMAT_OK) return rc;
+  if ((rc = check_buf(Y, true)) != QMAT_OK) return rc;
+  return hip_status(
+      qmat::launch_gemm(fmt, blocks, X_q8, Y, M, K, N, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,23 @@
+// qmat_launch.hpp — internal launchers behind the C ABI (include/qmat.h).
+// Arguments are already validated by the caller (qmat_api.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qmat {
+
+constexpr int kFmtQ4_0 = 0;
+constexpr int kFmtQ8_0 = 1;
+constexpr int kFmtQ4_K = 2;
+
+hipError_t launch_quantize(int fmt, const float* W, void* blocks, int64_t rows, int64_t K,
+                           hipStream_t stream);
+
+hipError_t launch_gemv(int fmt, const void* blocks, const float* x, float* y, int64_t M,
+                       int64_t K, hipStream_t stream);
+
+hipError_t launch_gemm(int fmt, const void* blocks, const void* Xq8, float* Y, int64_t M,
+                       int64_t K, int64_t N, hipStream_t stream);
+
+}  // namespace qmat

@@ -60,7 +60,8 @@
  *     bit-identical outputs (no atomics, fixed reduction order).
  *   - Limits: 0 <= rows, M, N <= 2^31-1; 0 <= K <= 2^31-1; K a multiple of
  *     qmat_block_elems(fmt); rows*row_bytes must fit in int64. A zero M or
- *     N enqueues nothing. K == 0 is valid: quantize writes nothing, gemv
+ *     N (or rows, for quantize) enqueues nothing and dereferences no pointer.
+ *     K == 0 is valid: quantize writes nothing, gemv
  *     and gemm write zeros (the empty sum).
  *   - Thread safe; no global mutable state.
  */

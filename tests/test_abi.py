@@ -1,0 +1,126 @@
+"""The C-ABI library: loads, exports every symbol include/qmat.h declares, and
+rejects bad arguments on the host, before anything is enqueued (no GPU is
+needed for any of these: every case returns before the first HIP call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle
+from block_quantized_weight_qmat_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qmat.h")
+
+OK, E_FMT, E_SHAPE, E_NULL, E_HIP, E_ALIGN = 0, 1, 2, 3, 4, 5
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.library_path()):
+        pytest.skip("libqmat.so not built")
+    return binding.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qmat_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_three_entry_points():
+    names = declared_functions()
+    for n in ("qmat_quantize", "qmat_gemv", "qmat_gemm", "qmat_block_elems",
+              "qmat_block_bytes", "qmat_row_bytes", "qmat_strerror"):
+        assert n in names
+
+
+def test_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_enum_values_match_header():
+    text = open(HEADER).read()
+    vals = dict(re.findall(r"\b(QMAT_[A-Z0-9_]+)\s*=\s*(\d+)", text))
+    assert vals["QMAT_Q4_0"] == "0" and vals["QMAT_Q8_0"] == "1" and vals["QMAT_Q4_K"] == "2"
+    assert binding.Q4_0 == 0 and binding.Q8_0 == 1 and binding.Q4_K == 2
+    assert [vals[k] for k in ("QMAT_OK", "QMAT_E_FMT", "QMAT_E_SHAPE", "QMAT_E_NULL",
+                              "QMAT_E_HIP", "QMAT_E_ALIGN")] == ["0", "1", "2", "3", "4", "5"]
+
+
+def test_sizes_agree_with_oracle(lib):
+    for f in (0, 1, 2):
+        assert lib.qmat_block_elems(f) == oracle.block_elems(f)
+        assert lib.qmat_block_bytes(f) == oracle.block_bytes(f)
+        for K in (0, 256, 11008 if f != 2 else 4096, 2 ** 20):
+            assert lib.qmat_row_bytes(f, K) == oracle.row_bytes(f, K)
+    assert lib.qmat_block_elems(7) == 0 and lib.qmat_block_bytes(-1) == 0
+    assert lib.qmat_row_bytes(0, 33) == -1 and lib.qmat_row_bytes(2, 32) == -1
+    assert lib.qmat_row_bytes(0, -32) == -1 and lib.qmat_row_bytes(9, 32) == -1
+
+
+def test_strerror(lib):
+    for s in range(6):
+        assert len(lib.qmat_strerror(s)) > 3
+    assert lib.qmat_strerror(99) == b"unknown status"
+
+
+A = 0x10000  # a 16-byte aligned fake address: never dereferenced (rejected first)
+
+
+def test_bad_format(lib):
+    assert lib.qmat_quantize(3, A, A, 1, 32, None) == E_FMT
+    assert lib.qmat_gemv(-1, A, A, A, 1, 32, None) == E_FMT
+    assert lib.qmat_gemm(5, A, A, A, 1, 32, 1, None) == E_FMT
+
+
+def test_bad_shapes(lib):
+    assert lib.qmat_quantize(0, A, A, 1, 48, None) == E_SHAPE      # K % 32
+    assert lib.qmat_quantize(2, A, A, 1, 288, None) == E_SHAPE     # K % 256
+    assert lib.qmat_quantize(1, A, A, -1, 32, None) == E_SHAPE
+    assert lib.qmat_gemv(0, A, A, A, -5, 32, None) == E_SHAPE
+    assert lib.qmat_gemv(0, A, A, A, 1, -32, None) == E_SHAPE
+    assert lib.qmat_gemv(0, A, A, A, 2 ** 31, 32, None) == E_SHAPE  # M beyond 2^31-1
+    assert lib.qmat_gemv(0, A, A, A, 1, 2 ** 31 + 32, None) == E_SHAPE
+    assert lib.qmat_gemm(0, A, A, A, 1, 32, -1, None) == E_SHAPE
+    assert lib.qmat_gemm(2, A, A, A, 1, 32, 1, None) == E_SHAPE    # Q4_K needs K % 256
+
+
+def test_null_and_alignment(lib):
+    assert lib.qmat_quantize(0, None, A, 1, 32, None) == E_NULL
+    assert lib.qmat_quantize(0, A, None, 1, 32, None) == E_NULL
+    assert lib.qmat_gemv(0, A, None, A, 1, 32, None) == E_NULL
+    assert lib.qmat_gemv(0, A, A, None, 1, 32, None) == E_NULL
+    assert lib.qmat_gemm(0, A, A, None, 1, 32, 1, None) == E_NULL
+    assert lib.qmat_gemm(0, A, None, A, 1, 32, 1, None) == E_NULL
+    assert lib.qmat_quantize(0, A + 4, A, 1, 32, None) == E_ALIGN
+    assert lib.qmat_gemv(0, A + 2, A, A, 1, 32, None) == E_ALIGN
+    assert lib.qmat_gemm(1, A, A + 8, A, 1, 32, 1, None) == E_ALIGN
+
+
+def test_empty_work_is_ok_with_null_pointers(lib):
+    # nothing to read or write: nothing is enqueued, no pointer is needed
+    assert lib.qmat_quantize(0, None, None, 0, 32, None) == OK
+    assert lib.qmat_quantize(2, None, None, 5, 0, None) == OK
+    assert lib.qmat_gemv(1, None, None, None, 0, 64, None) == OK
+    assert lib.qmat_gemm(0, None, None, None, 0, 64, 3, None) == OK
+    assert lib.qmat_gemm(0, None, None, None, 3, 64, 0, None) == OK
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    W = torch.zeros(2, 32)
+    with pytest.raises(TypeError):
+        binding.quantize("q4_0", W)
+
+
+def test_product_path_does_not_use_the_oracle():
+    pkg = os.path.join(ROOT, "block_quantized_weight_qmat_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".hpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in text and "from oracle" not in text, f
+                assert "liboracle" not in text and "qmat_oracle" not in text, f
