@@ -17,17 +17,24 @@
 //     halves the live values at each exchange, then across waves in LDS in a
 //     fixed order (deterministic).
 //
-// Arithmetic
-//   * Activation prescale: the lane's 32 values are multiplied by 2^s with
-//     s = 15 - exponent(amax), so the largest is in [2^14, 2^15), then
-//     rounded to fp16. Relative rounding error <= 2^-11 per value.
-//   * Nibble unpack without conversions: a code c placed in the mantissa of
-//     the fp16 pattern 0x6400 is exactly 1024 + c; the high nibble of a byte,
-//     masked in place, gives 1024 + 16c. v_dot2_f32_f16 multiplies these by
-//     fp16 activation pairs exactly and accumulates in fp32; the 1024 offsets
-//     are removed once per slice with the slice's activation sums.
-//   * Q8_0 bytes are made unsigned by flipping the sign bit (q + 128) and go
-//     through the same 0x6400 pattern (1152 + q).
+// Arithmetic: exact integer products
+//   * Each lane turns its 32 activations into 16-bit fixed point with a
+//     power-of-two scale: X = rint(x * 2^s) with s = 15 - exponent(amax)
+//     (s one lower if the largest value would round to 2^15), so
+//     |X| <= 32767 and the step is at most 2^-14 of the slice's largest
+//     value. X is split into two int8 digits, X = 256 Xh + Xl (Xl in
+//     [0,255], Xh in [-128,127]).
+//   * The rounding needs no integer conversion: fma(x, 2^s, 1.5*2^23) is a
+//     float whose bit pattern is 0x4B400000 + X, so its bytes 0 and 1 are
+//     Xl and Xh directly; four lanes' bytes are gathered with v_perm.
+//   * Codes are multiplied by the digits with v_dot4 (four 8-bit products
+//     into an int32, exact): nibble codes c in [0,15] are valid as both u8
+//     and i8, so sum c Xl uses v_dot4_u32_u8 and sum c Xh v_dot4_i32_i8;
+//     Q8_0 bytes q use (q + 128) for the unsigned digit and subtract
+//     128 * sum Xl once per slice.
+//   * Per (row, slice) the exact integer sum_i (c_i - 8) X_i (Q4_0),
+//     sum_i q_i X_i (Q8_0) or S sum q X - O sum X (Q4_K) is converted to
+//     fp32, scaled by 2^-s and the block scale, and accumulated in fp32.
 #include "qmat_device.hpp"
 #include "qmat_launch.hpp"
 
@@ -35,20 +42,15 @@ namespace qmat {
 namespace {
 
 constexpr int kMaxWaves = 8;
+constexpr float kMagicF = 12582912.0f;  // 1.5 * 2^23
 
-// The fp16 pair (1024, 1024). Materialised in a VGPR so that
-// (w & mask) | magic is a single v_and_or_b32 (mask in an SGPR, magic in a
-// VGPR): a gfx9 VOP3 cannot take two literal or SGPR constants.
-__device__ __forceinline__ uint32_t magic_1024() {
-  uint32_t m;
-  asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(m));
-  return m;
-}
-
+// One lane's 32 activations in 16-bit fixed point, as int8 digit bytes:
+// xl[i] / xh[i] hold the low / high digits of elements 4i..4i+3.
 struct XPrep {
-  half2_t p[16];
-  float c0, c1, c2;  // per-format constants derived from the fp16 values
-  float inv;         // 2^-s
+  uint32_t xl[8], xh[8];
+  int32_t sx;   // sum of X
+  int32_t sxl;  // sum of the low digits (0..255 each)
+  int s;        // X = rint(x * 2^s)
 };
 
 __device__ __forceinline__ void load_x32(const float* __restrict__ x, float (&v)[32]) {
@@ -63,65 +65,62 @@ __device__ __forceinline__ void load_x32(const float* __restrict__ x, float (&v)
   }
 }
 
-// s such that amax * 2^s lies in [2^14, 2^15).
-__device__ __forceinline__ int prescale_exp(const float (&v)[32]) {
+__device__ __forceinline__ uint32_t udot4(uint32_t a, uint32_t b, uint32_t c) {
+  return __builtin_amdgcn_udot4(a, b, c, false);
+}
+
+__device__ __forceinline__ int32_t sdot4(uint32_t a, uint32_t b, int32_t c) {
+  return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);
+}
+
+__device__ __forceinline__ void prep_x(float (&v)[32], XPrep& xp) {
   float am = 0.0f;
 #pragma unroll
   for (int i = 0; i < 32; ++i) am = fmaxf(am, fabsf(v[i]));
   int e;
-  frexpf(am, &e);
-  return 15 - e;
+  frexpf(am, &e);  // am = m 2^e, m in [0.5, 1) (e = 0 for am = 0)
+  int s = 15 - e;  // am 2^s in [2^14, 2^15)
+  if (ldexpf(am, s) >= 32767.5f) s -= 1;  // would round to 2^15
+  xp.s = s;
+  int sa = s;
+  if (sa > 120) {  // tiny activations: pre-scale exactly so 2^sa stays finite
+#pragma unroll
+    for (int i = 0; i < 32; ++i) v[i] = ldexpf(v[i], 64);
+    sa -= 64;
+  }
+  const float scale = ldexpf(1.0f, sa);
+  uint32_t t[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) t[i] = __builtin_bit_cast(uint32_t, fmaf(v[i], scale, kMagicF));
+  int32_t sl = 0, sh = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t a = perm_b32(t[4 * i + 1], t[4 * i], 0x05010400u);
+    const uint32_t b = perm_b32(t[4 * i + 3], t[4 * i + 2], 0x05010400u);
+    xp.xl[i] = perm_b32(b, a, 0x05040100u);
+    xp.xh[i] = perm_b32(b, a, 0x07060302u);
+    sl = (int32_t)udot4(xp.xl[i], 0x01010101u, (uint32_t)sl);
+    sh = sdot4(xp.xh[i], 0x01010101u, sh);
+  }
+  xp.sxl = sl;
+  xp.sx = sh * 256 + sl;
 }
 
-__device__ __forceinline__ half2_t hpair(float a, float b, int s) {
-  half2_t r;
-  r.x = (_Float16)ldexpf(a, s);
-  r.y = (_Float16)ldexpf(b, s);
-  return r;
-}
-
-// Activation pairs for nibble formats. For code dword i (code bytes
-// 4i..4i+3; byte t = element t low nibble, element t+16 high nibble):
-//   p[4i+0] = (x[4i],    x[4i+2])          low nibbles of bytes 0, 2
-//   p[4i+1] = (x[4i+16], x[4i+18]) / 16    high nibbles of bytes 0, 2
-//   p[4i+2] = (x[4i+1],  x[4i+3])          low nibbles of bytes 1, 3
-//   p[4i+3] = (x[4i+17], x[4i+19]) / 16    high nibbles of bytes 1, 3
-// H = sum of the fp16 low-half values, G = sum of the fp16 high-half values
-// (the latter already divided by 16).
-__device__ __forceinline__ void prep_nibble(const float (&v)[32], XPrep& xp, float& H, float& G) {
-  const int s = prescale_exp(v);
-  const half2_t one = {(_Float16)1.0f, (_Float16)1.0f};
-  H = 0.0f;
-  G = 0.0f;
+// sum_e c_e X_e over the 32 nibble codes in c[0..3] (byte t: element t low
+// nibble, element t+16 high nibble), as the pair (sum c Xl, sum c Xh).
+__device__ __forceinline__ int32_t nib_dot(const uint32_t (&c)[4], const XPrep& xp) {
+  uint32_t accL = 0;
+  int32_t accH = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    xp.p[4 * i + 0] = hpair(v[4 * i], v[4 * i + 2], s);
-    xp.p[4 * i + 1] = hpair(v[4 * i + 16], v[4 * i + 18], s - 4);
-    xp.p[4 * i + 2] = hpair(v[4 * i + 1], v[4 * i + 3], s);
-    xp.p[4 * i + 3] = hpair(v[4 * i + 17], v[4 * i + 19], s - 4);
-    H = __builtin_amdgcn_fdot2(xp.p[4 * i + 0], one, H, false);
-    H = __builtin_amdgcn_fdot2(xp.p[4 * i + 2], one, H, false);
-    G = __builtin_amdgcn_fdot2(xp.p[4 * i + 1], one, G, false);
-    G = __builtin_amdgcn_fdot2(xp.p[4 * i + 3], one, G, false);
+    const uint32_t lo = c[i] & 0x0F0F0F0Fu;         // elements 4i..4i+3
+    const uint32_t hi = (c[i] >> 4) & 0x0F0F0F0Fu;  // elements 16+4i..16+4i+3
+    accL = udot4(lo, xp.xl[i], accL);
+    accH = sdot4(lo, xp.xh[i], accH);
+    accL = udot4(hi, xp.xl[4 + i], accL);
+    accH = sdot4(hi, xp.xh[4 + i], accH);
   }
-  xp.inv = ldexpf(1.0f, -s);
-}
-
-// Low-nibble and high-nibble sums over the 16 code bytes c[0..3]:
-//   lo = sum (1024 + c) x_lo,  hi = sum (1024 + 16c) (x_hi / 16).
-__device__ __forceinline__ void nib_dot(const uint32_t (&c)[4], const XPrep& xp, float& lo,
-                                        float& hi) {
-  lo = 0.0f;
-  hi = 0.0f;
-  const uint32_t kMagic = magic_1024();
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t w = c[i], t = w >> 8;
-    lo = dot2((w & 0x000F000Fu) | kMagic, xp.p[4 * i + 0], lo);
-    hi = dot2((w & 0x00F000F0u) | kMagic, xp.p[4 * i + 1], hi);
-    lo = dot2((t & 0x000F000Fu) | kMagic, xp.p[4 * i + 2], lo);
-    hi = dot2((t & 0x00F000F0u) | kMagic, xp.p[4 * i + 3], hi);
-  }
+  return accH * 256 + (int32_t)accL;
 }
 
 // ------------------------------------------------------------------ Q4_0 --
@@ -145,13 +144,6 @@ struct FmtQ4_0 {
     r.s = *reinterpret_cast<const uint16_t*>(b + (a ? 0 : 16));
     r.s |= a << 30;  // remember the alignment case in an unused bit
   }
-  __device__ static void prep(const float (&v)[32], XPrep& xp) {
-    float H, G;
-    prep_nibble(v, xp, H, G);
-    // sum (c-8) x = lo - 1032 H + hi - 1152 G   (hi pairs are x/16)
-    xp.c0 = 1032.0f * H;
-    xp.c1 = 1152.0f * G;
-  }
   __device__ static float apply(const Raw& r, const XPrep& xp, int /*sub*/) {
     const bool mis = (r.s >> 30) != 0;  // block at o = 2 mod 4
     const uint32_t s16 = r.s & 0xFFFFu;
@@ -162,9 +154,8 @@ struct FmtQ4_0 {
     c[2] = perm_b32(r.v.w, r.v.z, sel);
     c[3] = perm_b32(s16, r.v.w, sel);
     const float D = f16_bits_to_f32(mis ? s16 : r.v.x);
-    float lo, hi;
-    nib_dot(c, xp, lo, hi);
-    return (D * xp.inv) * ((lo - xp.c0) + (hi - xp.c1));
+    const int32_t S = nib_dot(c, xp) - 8 * xp.sx;  // sum (c - 8) X, exact
+    return D * ldexpf((float)S, -xp.s);
   }
 };
 
@@ -185,37 +176,22 @@ struct FmtQ8_0 {
     r.s = *reinterpret_cast<const uint16_t*>(b + (a ? 0 : 32));
     r.s |= a << 30;
   }
-  // pairs: for code dword i (elements 4i..4i+3): p[2i] = (x[4i], x[4i+2]),
-  // p[2i+1] = (x[4i+1], x[4i+3]).
-  __device__ static void prep(const float (&v)[32], XPrep& xp) {
-    const int s = prescale_exp(v);
-    const half2_t one = {(_Float16)1.0f, (_Float16)1.0f};
-    float H = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      xp.p[2 * i] = hpair(v[4 * i], v[4 * i + 2], s);
-      xp.p[2 * i + 1] = hpair(v[4 * i + 1], v[4 * i + 3], s);
-      H = __builtin_amdgcn_fdot2(xp.p[2 * i], one, H, false);
-      H = __builtin_amdgcn_fdot2(xp.p[2 * i + 1], one, H, false);
-    }
-    xp.inv = ldexpf(1.0f, -s);
-    xp.c0 = 1152.0f * H;  // sum q x = sum (1152 + q) x - 1152 H
-  }
   __device__ static float apply(const Raw& r, const XPrep& xp, int /*sub*/) {
     const bool mis = (r.s >> 30) != 0;
     const uint32_t s16 = r.s & 0xFFFFu;
     const uint32_t sel = mis ? 0x03020100u : 0x05040302u;
     const uint32_t w[9] = {r.v0.x, r.v0.y, r.v0.z, r.v0.w, r.v1.x, r.v1.y, r.v1.z, r.v1.w, s16};
-    const uint32_t kMagic = magic_1024();
-    float a0 = 0.0f, a1 = 0.0f;
+    uint32_t accL = 0;
+    int32_t accH = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const uint32_t u = perm_b32(w[i + 1], w[i], sel) ^ 0x80808080u;  // q + 128
-      a0 = dot2((u & 0x00FF00FFu) | kMagic, xp.p[2 * i], a0);
-      a1 = dot2(((u >> 8) & 0x00FF00FFu) | kMagic, xp.p[2 * i + 1], a1);
+      const uint32_t q = perm_b32(w[i + 1], w[i], sel);   // q[4i..4i+3], int8
+      accL = udot4(q ^ 0x80808080u, xp.xl[i], accL);      // sum (q + 128) Xl
+      accH = sdot4(q, xp.xh[i], accH);                    // sum q Xh
     }
+    const int32_t S = accH * 256 + ((int32_t)accL - 128 * xp.sxl);  // sum q X
     const float D = f16_bits_to_f32(mis ? s16 : r.v0.x);
-    return (D * xp.inv) * ((a0 + a1) - xp.c0);
+    return D * ldexpf((float)S, -xp.s);
   }
 };
 
@@ -234,14 +210,6 @@ struct FmtQ4_K {
     r.h = *reinterpret_cast<const u32x4*>(b);
     r.c = *reinterpret_cast<const u32x4*>(b + 16 + 16 * (j & 7));
   }
-  __device__ static void prep(const float (&v)[32], XPrep& xp) {
-    float H, G;
-    prep_nibble(v, xp, H, G);
-    // sum (S q - O) x = S (lo - 1024 H + hi - 1024 G) - O (H + 16 G)
-    xp.c0 = 1024.0f * H;
-    xp.c1 = 1024.0f * G;
-    xp.c2 = H + 16.0f * G;
-  }
   __device__ static float apply(const Raw& r, const XPrep& xp, int sub) {
     // 6-bit fields: sc at bit 6*sub, mn at bit 48 + 6*sub of {w, z, y}
     const int ps = 6 * sub, pm = 48 + 6 * sub;
@@ -252,9 +220,8 @@ struct FmtQ4_K {
     const float S = f16_bits_to_f32(r.h.x) * (float)sc;
     const float O = f16_bits_to_f32(r.h.x >> 16) * (float)mn;
     const uint32_t c[4] = {r.c.x, r.c.y, r.c.z, r.c.w};
-    float lo, hi;
-    nib_dot(c, xp, lo, hi);
-    return xp.inv * fmaf(S, (lo - xp.c0) + (hi - xp.c1), -O * xp.c2);
+    const int32_t Q = nib_dot(c, xp);  // sum q X, exact
+    return ldexpf(fmaf(S, (float)Q, -O * (float)xp.sx), -xp.s);
   }
 };
 
@@ -325,7 +292,7 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void gemv_kernel(const uint8_t* 
       // any of them is consumed
       __builtin_amdgcn_sched_barrier(0);
       XPrep xp;
-      F::prep(xv, xp);
+      prep_x(xv, xp);
 #pragma unroll
       for (int r = 0; r < R; ++r) part[r] += F::apply(raw[r], xp, lane & 7);
     }
