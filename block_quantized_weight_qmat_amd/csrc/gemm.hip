@@ -209,10 +209,11 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const uint8_t* __restric
             const i32x4 bv = *reinterpret_cast<const i32x4*>(&st.xq[bb][t * 32 + l32][16 * half]);
             const float dx = st.xd[bb][t * 32 + l32];
             const i32x16 d = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, bv, cmagic, 0, 0, 0);
+            const f32x16 df = __builtin_bit_cast(f32x16, d);
             const float c1 = -kMagicF * dx;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-              const float f = __builtin_bit_cast(float, d[i]);
+              const float f = df[i];
               const float s = fmaf(f, dx, c1);
               acc[t][i] = fmaf(s, dw[i], acc[t][i]);
             }

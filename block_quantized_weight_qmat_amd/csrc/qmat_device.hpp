@@ -17,6 +17,9 @@ typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef int32_t i32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+// Note: bit-cast whole vectors, never a subscripted element (vec[i]): clang
+// lowers __builtin_bit_cast of a vector subscript as a read of element 0.
 
 // Binary16 bits of an fp32 value: round to nearest even, subnormals kept
 // (v_cvt_f16_f32 in the default IEEE mode).
