@@ -136,9 +136,11 @@ int qmat_quantize(int fmt, const float *W, void *blocks, int64_t rows,
  *   blocks: W in fmt (Q4_0, Q8_0 or Q4_K), M rows of K.
  *   x: fp32 [K]; y: fp32 [M], overwritten.
  *   Accuracy: relative L2 error against the exact (fp64) product of the
- *   dequantized weights with x is below 1e-3 for finite x; internally x is
- *   rescaled per 32 elements by a power of two and rounded to fp16, and
- *   products are accumulated in fp32.
+ *   dequantized weights with x is below 1e-3 for finite x; internally each
+ *   32-element slice of x is scaled by a power of two and rounded to a
+ *   16-bit integer (|X| <= 32639, relative step <= 2^-14 of the slice's
+ *   largest element), the integer dot products with the codes are exact,
+ *   and the per-block results are accumulated in fp32.
  */
 int qmat_gemv(int fmt, const void *blocks, const float *x, float *y,
               int64_t M, int64_t K, void *stream);

@@ -199,10 +199,17 @@ def test_gemv_activation_range(q, fmt):
     rng = np.random.default_rng(400)
     M, K = 24, 4096
     W = rng.normal(0, 0.02, (M, K)).astype(np.float32)
-    for name, scale in (("tiny", 1e-30), ("huge", 1e30), ("subnormal", 1e-40), ("mixed", None)):
+    for name, scale in (("tiny", 1e-30), ("huge", 1e30), ("subnormal", 1e-40), ("mixed", None),
+                        ("binade-top", "top")):
         say(f"gemv x-range fmt={fmt} {name}")
         x = rng.normal(0, 1, K)
-        if scale is None:
+        if scale == "top":
+            # every slice's maximum is positive and just below a power of two
+            # (the top of the 16-bit fixed-point range after prescaling)
+            x = rng.uniform(-0.9, 0.9, K)
+            x[::32] = 1.0 - 2.0 ** -rng.integers(9, 24, K // 32)
+            x *= np.repeat(2.0 ** rng.integers(-8, 8, K // 32), 32)
+        elif scale is None:
             x *= np.repeat(10.0 ** rng.integers(-20, 20, K // 32), 32)
         else:
             x *= scale
