@@ -3,66 +3,77 @@
 // Source: "05. llama.cpp：从 GGUF 文件到本地推理服务", section "性能直觉：带宽
 // 决定 Decode，算力决定 Prefill": single-token decode reads every weight once,
 // so its speed limit is memory bandwidth divided by weight bytes. The kernel
-// is therefore built around the HBM stream of packed blocks.
+// is therefore built around the HBM stream of packed blocks, and its integer
+// work per block is kept small enough to hide under that stream.
 //
 // Work split
-//   * A workgroup owns R consecutive rows (R = 8) and all of K. Its waves
-//     split K into strips of 64 slices; lane l of a strip owns one 32-element
-//     slice (one Q4_0/Q8_0 block, or one sub-block of a Q4_K superblock) of
-//     each of the R rows, so neighbouring lanes read neighbouring blocks.
-//   * Each lane issues its activation loads, then all R rows' weight loads,
-//     before consuming anything; the activation slice is converted while the
-//     weights stream in, and reused from registers for all R rows. Two
-//     workgroups per CU (three waves per SIMD) keep enough loads in flight.
-//   * Row base addresses are wave-uniform (scalar registers); each lane
-//     keeps 32-bit offsets and its block-alignment case, fixed per pass (per
-//     row parity when the row stride is 2 mod 4).
-//   * Per-lane partial sums of the R rows are reduced with a butterfly that
-//     halves the live values at each exchange, then across the strips in LDS
-//     in a fixed order (deterministic).
+//   * A workgroup owns G groups of R consecutive rows and all of K. Its waves
+//     split K into strips of 64 slices; lane l of a strip owns one
+//     32-element slice (one Q4_0/Q8_0 block, or one sub-block of a Q4_K
+//     superblock) of every row, so neighbouring lanes read neighbouring
+//     blocks.
+//   * A wave first sends its strip of activations (64 x 128 bytes) from
+//     memory straight into LDS, then issues the R rows' weight loads: each
+//     lane reads its block with 4-byte-aligned 16- and 2-byte loads. Once
+//     the activation loads have landed (loads complete in issue order) the
+//     lane reads its slice back from LDS and converts it while the weights
+//     stream in; the converted slice serves all G x R rows from registers.
+//     Group g+1's loads are issued before group g is consumed.
+//     Activations loaded straight into registers, 128 bytes per lane, cost
+//     far more load bandwidth than the same bytes staged through LDS.
+//   * Row base addresses are wave-uniform (scalar registers), lane offsets
+//     32-bit. When the row stride is 2 mod 4, even and odd rows have
+//     different block alignments and get their own fixed load offsets.
+//   * Per-lane partial sums of the G x R rows are reduced across the wave
+//     with VALU lane exchanges that halve the live values at each step, then
+//     across the strips in LDS in a fixed order (deterministic).
 //
-// Arithmetic: exact integer products
-//   * Each lane turns its 32 activations into 16-bit fixed point with a
-//     power-of-two scale: X = rint(x * 2^s) with s = 15 - exponent(amax)
-//     (s one lower if the largest value would round above 32639), so
-//     |X| <= 32639 and the step is at most 2^-14 of the slice's largest
-//     value. X is split into two signed int8 digits, X = 256 Xh + Xl with
-//     Xl, Xh in [-128, 127] (balanced: Xh = (X + 128) >> 8).
-//   * The rounding needs no integer conversion: fma(x, 2^s, 1.5*2^23) is a
-//     float whose bit pattern is 0x4B400000 + X, so its low 16 bits are X;
-//     byte 0 is Xl and byte 1 of X + 128 (a packed 16-bit add) is Xh.
-//   * Codes are multiplied by the digits with v_dot4_i32_i8 (four 8-bit
-//     products into an int32, exact); nibble codes c in [0,15] are valid
-//     signed bytes once masked, Q8_0 bytes are signed already. The Q4_0
-//     offset -8 sum X is folded into the accumulator's initial value.
-//   * Per (row, slice) the exact integer sum_i (c_i - 8) X_i (Q4_0),
-//     sum_i q_i X_i (Q8_0) or S sum q X - O sum X (Q4_K) is converted to
-//     fp32, scaled by 2^-s and the block scale, and accumulated in fp32.
+// Arithmetic: exact integer dot products per block
+//   * Each lane turns its 32 activations into 20-bit fixed point with a
+//     power-of-two scale: X = rint(x * 2^s), s = 19 - exponent(amax), one
+//     lower if the largest value would round beyond the digit range. The
+//     step is then at most 2^-17.9 of the slice's largest value. (16 bits
+//     are not enough: a row of large weights with a small dot product turns
+//     a 2^-15 activation step into a relative error near 1e-3.)
+//   * The rounding needs no integer conversion: fma(x, 2^s, 1.5*2^23 + b)
+//     is a float whose low 20 bits are V = X + b, for a bias b that makes V
+//     non-negative.
+//   * 4-bit formats: b = 0x88888, so V's five nibbles minus 8 are signed
+//     digits with X = sum_i 16^i (nibble_i - 8). They are packed in the
+//     codes' own nibble order (byte t of a code word holds elements t and
+//     t+16) and multiplied with v_dot8_i32_i4. The codes become signed
+//     4-bit values c - 8 with one XOR (c ^ 8 read as a signed nibble is
+//     c - 8), so a Q4_0 block needs no offset term at all:
+//       sum (c - 8) X = sum_i 16^i dot8(c ^ 0x8..8, digit_i).
+//   * Q8_0: b = 0x88080, signed byte digits b0 - 128, b1 - 128, b2 - 8,
+//     multiplied with v_dot4_i32_i8 against the int8 codes.
+//   * Per (row, slice) the exact integer is converted to fp32, scaled by the
+//     block scale and 2^-s, and accumulated in fp32.
 #include "qmat_device.hpp"
 #include "qmat_launch.hpp"
 
 namespace qmat {
 namespace {
 
-constexpr int kMaxStrips = 8;  // waves per workgroup
-constexpr float kMagicF = 12582912.0f;  // 1.5 * 2^23
-
-// One lane's 32 activations in 16-bit fixed point, as signed int8 digit
-// bytes: xl[i] / xh[i] hold the low / high digits of elements 4i..4i+3.
-struct XPrep {
-  uint32_t xl[8], xh[8];
-  int32_t sx;   // sum of X
-  float inv;    // 2^-s, X = rint(x * 2^s)
-};
+// Waves per workgroup: 7 strips of activations (56 KB) plus the row sums
+// stay inside the default 64 KB of LDS a workgroup may allocate.
+constexpr int kMaxStrips = 7;
 
 __device__ __forceinline__ int32_t sdot4(uint32_t a, uint32_t b, int32_t c) {
   return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);
 }
 
-// Packed 16-bit add (two lanes of 16 bits, no carry between them).
-__device__ __forceinline__ uint32_t add_u16x2(uint32_t a, uint32_t b) {
-  typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
-  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, a) + __builtin_bit_cast(u16x2, b));
+__device__ __forceinline__ int32_t sdot8(uint32_t a, uint32_t b, int32_t c) {
+  return __builtin_amdgcn_sdot8((int)a, (int)b, c, false);
+}
+
+// (m & a) | (~m & b): v_bfi_b32
+__device__ __forceinline__ uint32_t bfi(uint32_t m, uint32_t a, uint32_t b) {
+  return (m & a) | (~m & b);
+}
+
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  return __builtin_fmaxf(__builtin_fmaxf(a, b), c);  // v_max3_f32
 }
 
 __device__ __forceinline__ void load_x32(const float* __restrict__ x, f32x4 (&v)[8]) {
@@ -71,11 +82,10 @@ __device__ __forceinline__ void load_x32(const float* __restrict__ x, f32x4 (&v)
   for (int i = 0; i < 8; ++i) v[i] = p[i];
 }
 
-__device__ __forceinline__ float max3f(float a, float b, float c) {
-  return __builtin_fmaxf(__builtin_fmaxf(a, b), c);  // v_max3_f32
-}
-
-__device__ __forceinline__ void prep_x(f32x4 (&v)[8], XPrep& xp) {
+// Scale the slice to 20-bit fixed point. Returns the multiplier 2^s (after
+// an exact 2^64 pre-scale of v when s is too large for one factor) and sets
+// inv = 2^-s. `lim` is the largest |X| the digit split accepts.
+__device__ __forceinline__ float slice_scale(f32x4 (&v)[8], float lim, float& inv) {
   float am = 0.0f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -84,13 +94,14 @@ __device__ __forceinline__ void prep_x(f32x4 (&v)[8], XPrep& xp) {
   }
   int e;
   frexpf(am, &e);  // am = m 2^e, m in [0.5, 1) (e = 0 for am = 0)
-  int s = 15 - e;  // am 2^s in [2^14, 2^15)
-  // balanced digits need X + 128 < 2^15, i.e. X <= 32639
-  if (ldexpf(am, s) >= 32639.5f) s -= 1;
-  xp.inv = ldexpf(1.0f, -s);
-  int sa = s;
+  int s = 19 - e;  // am 2^s in [2^18, 2^19)
+  if (ldexpf(am, s) >= lim + 0.5f) s -= 1;
+  // 2^-149 is the smallest float: subnormal x are integer multiples of it,
+  // so with s = 149 they scale to exact integers and 2^-s stays a float
+  s = min(s, 149);
+  inv = ldexpf(1.0f, -s);
   if (__builtin_expect(s > 120, 0)) {
-    // tiny activations: pre-scale exactly by 2^64 so that 2^sa stays finite
+    // tiny activations: pre-scale by 2^64 so that 2^s stays a finite float
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       v[i].x = ldexpf(v[i].x, 64);
@@ -98,50 +109,148 @@ __device__ __forceinline__ void prep_x(f32x4 (&v)[8], XPrep& xp) {
       v[i].z = ldexpf(v[i].z, 64);
       v[i].w = ldexpf(v[i].w, 64);
     }
-    sa -= 64;
+    s -= 64;
   }
-  const float scale = ldexpf(1.0f, sa);
-  int32_t sl = 0, sh = 0;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    uint32_t t[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-      t[k] = __builtin_bit_cast(uint32_t, fmaf(v[i][k], scale, kMagicF));
-    const uint32_t w01 = perm_b32(t[1], t[0], 0x05040100u);  // {X0, X1} as 16-bit
-    const uint32_t w23 = perm_b32(t[3], t[2], 0x05040100u);  // {X2, X3}
-    const uint32_t u01 = add_u16x2(w01, 0x00800080u);       // {X0+128, X1+128}
-    const uint32_t u23 = add_u16x2(w23, 0x00800080u);
-    xp.xl[i] = perm_b32(w23, w01, 0x06040200u);  // low bytes of X0..X3
-    xp.xh[i] = perm_b32(u23, u01, 0x07050301u);  // byte 1 of X0+128 .. X3+128
-    sl = sdot4(xp.xl[i], 0x01010101u, sl);
-    sh = sdot4(xp.xh[i], 0x01010101u, sh);
-  }
-  xp.sx = sh * 256 + sl;
+  return ldexpf(1.0f, s);
 }
 
-// sum_e c_e X_e over the 32 nibble codes in c[0..3] (byte t: element t low
-// nibble, element t+16 high nibble), starting from `init`.
-__device__ __forceinline__ int32_t nib_dot(const uint32_t (&c)[4], const XPrep& xp, int32_t init) {
-  int32_t accL = init, accH = 0;
+// Elements 4i..4i+3 scaled and biased: bytes 0, 1 and 2 of the four 20-bit
+// values V = rint(x 2^s) + bias, packed one per byte (lo, hi, top). The
+// float fma(x, 2^s, 1.5*2^23 + bias) is exact (it stays below 2^24) and its
+// bits are 0x4B400000 + bias + X, whose low 20 bits are V; byte 2 of the
+// float carries 0x40 above V's fifth nibble.
+__device__ __forceinline__ void bias20(const f32x4& v, float scale, float magic, uint32_t& lo,
+                                       uint32_t& hi, uint32_t& top) {
+  uint32_t t[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t lo = c[i] & 0x0F0F0F0Fu;         // elements 4i..4i+3
-    const uint32_t hi = (c[i] >> 4) & 0x0F0F0F0Fu;  // elements 16+4i..16+4i+3
-    accL = sdot4(lo, xp.xl[i], accL);
-    accH = sdot4(lo, xp.xh[i], accH);
-    accL = sdot4(hi, xp.xl[4 + i], accL);
-    accH = sdot4(hi, xp.xh[4 + i], accH);
+  for (int k = 0; k < 4; ++k) t[k] = __builtin_bit_cast(uint32_t, fmaf(v[k], scale, magic));
+  const uint32_t p = perm_b32(t[1], t[0], 0x05040100u);  // {V0, V1} low halves
+  const uint32_t q = perm_b32(t[3], t[2], 0x05040100u);  // {V2, V3}
+  lo = perm_b32(q, p, 0x06040200u);
+  hi = perm_b32(q, p, 0x07050301u);
+  // byte 2 of each (0x0c selects a zero byte)
+  top = perm_b32(t[1], t[0], 0x0c0c0602u) | perm_b32(t[3], t[2], 0x06020c0cu);
+}
+
+constexpr float kMagicF = 12582912.0f;  // 1.5 * 2^23
+
+// 4-bit digits: d[i][t] holds signed digit i of elements 4t+b (low nibble of
+// byte b) and 4t+b+16 (high nibble), the layout of code word t.
+struct XNib {
+  uint32_t d[5][4];
+  int32_t sx;  // sum of X (used by Q4_K only)
+  float inv;   // 2^-s
+};
+
+// X in [-0x88888, 0xFFFFF - 0x88888]: V = X + 0x88888 has five nibbles.
+constexpr uint32_t kNibBias = 0x88888u;
+constexpr float kNibLim = (float)(0xFFFFF - kNibBias);  // 489335
+
+__device__ __forceinline__ void nib_digits(uint32_t a, uint32_t b, uint32_t (&d)[2]) {
+  // low nibbles of a's bytes with b's low nibbles above them, then the high
+  // nibbles likewise; signed by flipping each nibble's top bit
+  constexpr uint32_t kHi = 0xF0F0F0F0u, kSign = 0x88888888u;
+  d[0] = bfi(kHi, b << 4, a) ^ kSign;
+  d[1] = bfi(kHi, b, a >> 4) ^ kSign;
+}
+
+__device__ __forceinline__ void prep_nib(f32x4 (&v)[8], XNib& xp, bool want_sum) {
+  const float scale = slice_scale(v, kNibLim, xp.inv);
+  const float magic = kMagicF + (float)kNibBias;  // exact: below 2^24
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    uint32_t aL, aH, aT, bL, bH, bT;
+    bias20(v[t], scale, magic, aL, aH, aT);      // elements 4t..4t+3
+    bias20(v[t + 4], scale, magic, bL, bH, bT);  // elements 16+4t..
+    uint32_t d[2];
+    nib_digits(aL, bL, d);
+    xp.d[0][t] = d[0];
+    xp.d[1][t] = d[1];
+    nib_digits(aH, bH, d);
+    xp.d[2][t] = d[0];
+    xp.d[3][t] = d[1];
+    nib_digits(aT, bT, d);  // byte 2 holds one nibble: d[1] would be all -8
+    xp.d[4][t] = d[0];
   }
-  return accH * 256 + accL;
+  xp.sx = 0;
+  if (want_sum) {
+    uint32_t a[5];
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+      int32_t acc = 0;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) acc = sdot8(xp.d[i][t], 0x11111111u, acc);
+      a[i] = (uint32_t)acc;
+    }
+    xp.sx = (int32_t)((((a[4] * 16u + a[3]) * 16u + a[2]) * 16u + a[1]) * 16u + a[0]);
+  }
+}
+
+// Digit accumulators carried from row to row: v_dot8/v_dot4 accumulate in
+// place, so instead of clearing them for every block (one move each) a row's
+// exact sum is the difference of the combined totals after and before it.
+// Differences are taken modulo 2^32, which is exact because every block's
+// sum fits in int32.
+struct NibAcc {
+  int32_t a[5];
+  uint32_t prev;  // combined total before the current block
+};
+
+// sum_e w_e X_e for 32 signed nibbles w (code word layout), exact.
+__device__ __forceinline__ int32_t nib_dot(const uint32_t (&w)[4], const XNib& xp, NibAcc& ac) {
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int i = 0; i < 5; ++i) ac.a[i] = sdot8(w[t], xp.d[i][t], ac.a[i]);
+  const uint32_t tot = (((((uint32_t)ac.a[4] * 16u + (uint32_t)ac.a[3]) * 16u +
+                          (uint32_t)ac.a[2]) * 16u + (uint32_t)ac.a[1]) * 16u) +
+                       (uint32_t)ac.a[0];
+  const int32_t r = (int32_t)(tot - ac.prev);
+  ac.prev = tot;
+  return r;
+}
+
+// 8-bit digits: xl[i] / xh[i] / xt[i] hold the low / middle / top signed
+// digit of elements 4i..4i+3, X = 65536 xt + 256 xh + xl.
+struct XByte {
+  uint32_t xl[8], xh[8], xt[8];
+  int32_t sx;
+  float inv;
+};
+
+struct ByteAcc {
+  int32_t l, h, t;
+  uint32_t prev;
+};
+
+// X in [-0x88080, 0xFFFFF - 0x88080]: V = X + 0x88080 has bytes b0, b1 in
+// [0, 255] and b2 in [0, 15], digits b0 - 128, b1 - 128, b2 - 8. The bound
+// also keeps |sum q X| over 32 int8 codes below 2^31.
+constexpr uint32_t kByteBias = 0x88080u;
+constexpr float kByteLim = (float)(0xFFFFF - kByteBias);  // 491391
+
+__device__ __forceinline__ void prep_byte(f32x4 (&v)[8], XByte& xp, bool /*want_sum*/) {
+  const float scale = slice_scale(v, kByteLim, xp.inv);
+  const float magic = kMagicF + (float)kByteBias;  // exact: below 2^24
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    uint32_t lo, hi, top;
+    bias20(v[i], scale, magic, lo, hi, top);
+    xp.xl[i] = lo ^ 0x80808080u;
+    xp.xh[i] = hi ^ 0x80808080u;
+    // byte 2 of the float is 0x40 | b2: keep b2, then b2 - 8 as a signed byte
+    xp.xt[i] = ((top & 0x0F0F0F0Fu) + 0x78787878u) ^ 0x80808080u;
+  }
+  xp.sx = 0;
 }
 
 // A lane's fixed load offsets and alignment case for one 18- or 34-byte
-// block at byte offset o of a row whose base has alignment parity p:
-// if (base + o) = 0 mod 4 the 16-byte load at o holds the scale and the first
-// code bytes and the 2-byte load at o+B-2 the last two code bytes; if it is
-// 2 mod 4 the 2-byte load at o is the scale and the 16-byte load(s) at o+2
-// hold the codes. Both cases read exactly the block.
+// block at byte offset o of a row whose base has alignment parity p (row
+// bases are 2-byte aligned): if (base + o) = 0 mod 4 the 16-byte load at o
+// holds the scale and the first code bytes and the 2-byte load at o+B-2 the
+// last two code bytes; if it is 2 mod 4 the 2-byte load at o is the scale
+// and the 16-byte load(s) at o+2 hold the codes. Both cases read exactly
+// the block with 4-byte-aligned 16-byte loads.
 struct BlockLane {
   uint32_t o16;  // offset of the (first) 16-byte load
   uint32_t o2;   // offset of the 2-byte load
@@ -162,25 +271,28 @@ __device__ __forceinline__ BlockLane block_lane(uint32_t o, uint32_t p, uint32_t
 // 18-byte blocks: fp16 scale, 16 code bytes; weight = d * (c - 8).
 struct FmtQ4_0 {
   static constexpr int kBytes = 18;
+  static constexpr int kLoads = 2;  // memory instructions per row
+  typedef XNib XP;
+  typedef NibAcc Acc;
   struct Raw {
     u32x4 v;
     uint32_t s;
   };
   __device__ static int64_t row_bytes(int K) { return (int64_t)(K >> 5) * 18; }
+  __device__ static void prep(f32x4 (&v)[8], XP& xp) { prep_nib(v, xp, false); }
   __device__ static void load(const uint8_t* __restrict__ row, const BlockLane& L, Raw& r) {
     r.v = *reinterpret_cast<const u32x4_a4*>(row + L.o16);
     r.s = *reinterpret_cast<const uint16_t*>(row + L.o2);
   }
-  // D * sum_i (c_i - 8) X_i (still to be scaled by 2^-s)
-  __device__ static float apply(const Raw& r, const BlockLane& L, const XPrep& xp, int /*sub*/) {
-    uint32_t c[4];
-    c[0] = perm_b32(r.v.y, r.v.x, L.sel);
-    c[1] = perm_b32(r.v.z, r.v.y, L.sel);
-    c[2] = perm_b32(r.v.w, r.v.z, L.sel);
-    c[3] = perm_b32(r.s, r.v.w, L.sel);
-    const float D = f16_bits_to_f32(L.mis ? r.s : r.v.x);
-    const int32_t S = nib_dot(c, xp, -8 * xp.sx);  // sum (c - 8) X, exact
-    return D * (float)S;
+  // D * sum (c - 8) X (still to be scaled by 2^-s)
+  __device__ static float apply(const Raw& r, const BlockLane& L, const XP& xp, int /*j*/,
+                               Acc& ac) {
+    uint32_t w[4];
+    w[0] = perm_b32(r.v.y, r.v.x, L.sel) ^ 0x88888888u;
+    w[1] = perm_b32(r.v.z, r.v.y, L.sel) ^ 0x88888888u;
+    w[2] = perm_b32(r.v.w, r.v.z, L.sel) ^ 0x88888888u;
+    w[3] = perm_b32(r.s, r.v.w, L.sel) ^ 0x88888888u;
+    return f16_bits_to_f32(L.mis ? r.s : r.v.x) * (float)nib_dot(w, xp, ac);
   }
 };
 
@@ -188,27 +300,35 @@ struct FmtQ4_0 {
 // 34-byte blocks: fp16 scale, 32 int8; weight = d * q.
 struct FmtQ8_0 {
   static constexpr int kBytes = 34;
+  static constexpr int kLoads = 3;
+  typedef XByte XP;
+  typedef ByteAcc Acc;
   struct Raw {
     u32x4 v0, v1;
     uint32_t s;
   };
   __device__ static int64_t row_bytes(int K) { return (int64_t)(K >> 5) * 34; }
+  __device__ static void prep(f32x4 (&v)[8], XP& xp) { prep_byte(v, xp, false); }
   __device__ static void load(const uint8_t* __restrict__ row, const BlockLane& L, Raw& r) {
     r.v0 = *reinterpret_cast<const u32x4_a4*>(row + L.o16);
     r.v1 = *reinterpret_cast<const u32x4_a4*>(row + L.o16 + 16);
     r.s = *reinterpret_cast<const uint16_t*>(row + L.o2);
   }
-  __device__ static float apply(const Raw& r, const BlockLane& L, const XPrep& xp, int /*sub*/) {
+  __device__ static float apply(const Raw& r, const BlockLane& L, const XP& xp, int /*j*/,
+                               Acc& ac) {
     const uint32_t w[9] = {r.v0.x, r.v0.y, r.v0.z, r.v0.w, r.v1.x, r.v1.y, r.v1.z, r.v1.w, r.s};
-    int32_t accL = 0, accH = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const uint32_t q = perm_b32(w[i + 1], w[i], L.sel);  // q[4i..4i+3], int8
-      accL = sdot4(q, xp.xl[i], accL);
-      accH = sdot4(q, xp.xh[i], accH);
+      ac.l = sdot4(q, xp.xl[i], ac.l);
+      ac.h = sdot4(q, xp.xh[i], ac.h);
+      ac.t = sdot4(q, xp.xt[i], ac.t);
     }
-    const float D = f16_bits_to_f32(L.mis ? r.s : r.v0.x);
-    return D * (float)(accH * 256 + accL);  // D * sum q X
+    // combined modulo 2^32 (sum q X itself fits in int32)
+    const uint32_t tot = ((uint32_t)ac.t * 256u + (uint32_t)ac.h) * 256u + (uint32_t)ac.l;
+    const int32_t S = (int32_t)(tot - ac.prev);
+    ac.prev = tot;
+    return f16_bits_to_f32(L.mis ? r.s : r.v0.x) * (float)S;  // D * sum q X
   }
 };
 
@@ -218,15 +338,21 @@ struct FmtQ8_0 {
 // j % 8 of superblock j / 8; weight = (d sc) q - (dmin mn).
 struct FmtQ4_K {
   static constexpr int kBytes = 144;
+  static constexpr int kLoads = 2;
+  typedef XNib XP;
+  typedef NibAcc Acc;
   struct Raw {
     u32x4 h, c;
   };
   __device__ static int64_t row_bytes(int K) { return (int64_t)(K >> 8) * 144; }
+  __device__ static void prep(f32x4 (&v)[8], XP& xp) { prep_nib(v, xp, true); }
   __device__ static void load(const uint8_t* __restrict__ row, const BlockLane& L, Raw& r) {
     r.h = *reinterpret_cast<const u32x4*>(row + L.o16);
     r.c = *reinterpret_cast<const u32x4*>(row + L.o2);
   }
-  __device__ static float apply(const Raw& r, const BlockLane& /*L*/, const XPrep& xp, int sub) {
+  __device__ static float apply(const Raw& r, const BlockLane& /*L*/, const XP& xp, int j,
+                               Acc& ac) {
+    const int sub = j & 7;
     // 6-bit fields: sc at bit 6*sub, mn at bit 48 + 6*sub of {w, z, y}
     const int ps = 6 * sub, pm = 48 + 6 * sub;
     const uint32_t slo = ps < 32 ? r.h.y : r.h.z, shi = ps < 32 ? r.h.z : r.h.w;
@@ -235,36 +361,78 @@ struct FmtQ4_K {
     const uint32_t mn = __builtin_amdgcn_alignbit(mhi, mlo, pm & 31) & 63u;
     const float S = f16_bits_to_f32(r.h.x) * (float)sc;
     const float O = f16_bits_to_f32(r.h.x >> 16) * (float)mn;
-    const uint32_t c[4] = {r.c.x, r.c.y, r.c.z, r.c.w};
-    const int32_t Q = nib_dot(c, xp, 0);  // sum q X, exact
-    return fmaf(S, (float)Q, -O * (float)xp.sx);
+    const uint32_t w[4] = {r.c.x ^ 0x88888888u, r.c.y ^ 0x88888888u, r.c.z ^ 0x88888888u,
+                           r.c.w ^ 0x88888888u};
+    // sum q X = sum (q - 8) X + 8 sum X
+    const int32_t Q8 = nib_dot(w, xp, ac);
+    return fmaf(S, (float)Q8, fmaf(8.0f, S, -O) * (float)xp.sx);
   }
 };
 
-// Butterfly reduction of R per-lane values: every exchange sends the half of
-// the live values that the partner keeps, so R values need
-// R/2 + R/4 + ... + 1 shuffles plus log2(64/R) full ones. On return lane l
-// holds the wave sum of row (l >> (6 - log2 R)) & (R - 1).
+// Cross-lane exchange at distance `mask` (32, 16, 8, 4, 2 or 1), all in
+// VALU: v_permlane32_swap / v_permlane16_swap swap the upper half of the
+// first operand with the lower half of the second (lanes 32-63 <-> 0-31, or
+// odd <-> even rows of 16), and DPP moves read a partner lane within a row
+// of 16 (row_ror:8 is lane ^ 8; row_half_mirror pairs lane i with 7 - i
+// inside each group of 8, which also crosses bit 2; quad_perm gives ^2, ^1).
+//
+// halve(mask, a, b): lanes whose `mask` bit is clear return a + partner's a,
+// the others b + partner's b.
+template <int kMask>
+__device__ __forceinline__ float dpp_other(float v) {
+  static_assert(kMask == 8 || kMask == 4 || kMask == 2 || kMask == 1, "DPP partner");
+  // row_ror:8, row_half_mirror, quad_perm [2,3,0,1], quad_perm [1,0,3,2]
+  constexpr int kCtrl = kMask == 8 ? 0x128 : kMask == 4 ? 0x141 : kMask == 2 ? 0x4E : 0xB1;
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl, 0xF, 0xF, false));
+}
+
+template <int kMask>
+__device__ __forceinline__ float halve(float a, float b, int lane) {
+  if constexpr (kMask == 32 || kMask == 16) {
+    // after the swap the first result holds a on the low side and the
+    // partner's b on the high side, the second the partner's a on the low
+    // side and b on the high side
+    const auto r = kMask == 32
+                       ? __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, a),
+                                                          __builtin_bit_cast(uint32_t, b), false,
+                                                          false)
+                       : __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, a),
+                                                          __builtin_bit_cast(uint32_t, b), false,
+                                                          false);
+    // bit-cast the whole pair: a bit-cast of one subscripted element would
+    // read element 0
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    const f32x2 f = __builtin_bit_cast(f32x2, r);
+    return f.x + f.y;
+  } else {
+    const bool up = (lane & kMask) != 0;
+    const float keep = up ? b : a, send = up ? a : b;
+    return keep + dpp_other<kMask>(send);
+  }
+}
+
+// Reduction of R per-lane values over the wave: every exchange sends the
+// half of the live values that the partner keeps (R/2 + R/4 + ... + 1
+// exchanges), then the groups left holding one row are summed. On return
+// lane l holds the wave sum of row (l >> (6 - log2 R)) & (R - 1).
+template <int kMask, int kHalf, int R>
+__device__ __forceinline__ void reduce_level(float (&v)[R], int lane) {
+  if constexpr (kMask >= 1) {
+    if constexpr (kHalf >= 1) {
+#pragma unroll
+      for (int i = 0; i < kHalf; ++i) v[i] = halve<kMask>(v[i], v[i + kHalf], lane);
+      reduce_level<kMask / 2, kHalf / 2, R>(v, lane);
+    } else {
+      v[0] = halve<kMask>(v[0], v[0], lane);
+      reduce_level<kMask / 2, 0, R>(v, lane);
+    }
+  }
+}
+
 template <int R>
 __device__ __forceinline__ float wave_reduce_rows(float (&v)[R], int lane) {
-  int mask = 32;
-#pragma unroll
-  for (int half = R / 2; half >= 1; half >>= 1) {
-    // all-ones in the upper lanes of this exchange; a bitwise select keeps
-    // the compiler from turning the choice into register-array indexing
-    const uint32_t up = (lane & mask) ? 0xFFFFFFFFu : 0u;
-#pragma unroll
-    for (int i = 0; i < half; ++i) {
-      const uint32_t a = __builtin_bit_cast(uint32_t, v[i]);
-      const uint32_t b = __builtin_bit_cast(uint32_t, v[i + half]);
-      const float keep = __builtin_bit_cast(float, (b & up) | (a & ~up));
-      const float send = __builtin_bit_cast(float, (a & up) | (b & ~up));
-      v[i] = keep + shfl_xor_f(send, mask);
-    }
-    mask >>= 1;
-  }
-#pragma unroll
-  for (int m = 32 / R; m >= 1; m >>= 1) v[0] += shfl_xor_f(v[0], m);
+  reduce_level<32, R / 2, R>(v, lane);
   return v[0];
 }
 
@@ -273,31 +441,71 @@ constexpr int log2i() {
   return R <= 1 ? 0 : 1 + log2i<R / 2>();
 }
 
-constexpr int kRows = 8;  // rows per workgroup
+// The activation slices of a strip go through LDS: 64 slices x 128 bytes
+// per wave, written by direct global->LDS loads (each instruction moves 1 KB,
+// 16 bytes per lane) so that no lane's registers wait on them, and read back
+// one slice per lane. Slice s keeps its 16-byte part k in column
+// (k + s) mod 8 of its 128-byte row, so the eight lanes of one LDS access
+// phase read eight different columns (no bank conflicts).
+constexpr int kXStripBytes = kWave * 128;
 
-// kOdd: the row stride is 2 mod 4 (K/32 odd for Q4_0/Q8_0), so even and odd
-// rows have different block alignments; row m0 + r has parity r & 1 since
-// m0 is a multiple of kRows (even).
-template <class F, bool kOdd>
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// s_waitcnt immediate (gfx9 encoding) that waits until at most N vector
+// memory operations are outstanding, leaving the other counters free.
+template <int N>
+constexpr int vmcnt_imm() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  return (N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8);
+}
+
+__device__ __forceinline__ void x_to_lds(const float* __restrict__ xs, int nsl, uint8_t* strip,
+                                         int lane) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int s = 8 * i + (lane >> 3);  // slice filled by this lane's column
+    const int k = (lane - s) & 7;       // its part stored in column lane & 7
+    if (s < nsl)
+      __builtin_amdgcn_global_load_lds(xs + 32 * s + 4 * k, (lds_ptr_t)(strip + 1024 * i), 16, 0,
+                                       0);
+  }
+}
+
+__device__ __forceinline__ void x_from_lds(const uint8_t* strip, int lane, f32x4 (&v)[8]) {
+  const uint8_t* row = strip + 128 * lane;
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+    v[k] = *reinterpret_cast<const f32x4*>(row + 16 * ((k + lane) & 7));
+}
+
+// A workgroup owns G groups of R rows. kOdd: the row stride is 2 mod 4
+// (K/32 odd for Q4_0/Q8_0), so even and odd rows have different block
+// alignments; row m0 + r has parity r & 1 since m0 and the group size are
+// even.
+template <class F, int R, int G, bool kOdd>
 __global__ __launch_bounds__(kMaxStrips * kWave) void gemv_kernel(const uint8_t* __restrict__ B,
                                                                   const float* __restrict__ x,
                                                                   float* __restrict__ y,
                                                                   int64_t M, int K) {
-  constexpr int R = kRows;
-  __shared__ float red[kMaxStrips][R];
+  constexpr int RG = R * G;
+  static_assert(RG <= kWave && (RG & (RG - 1)) == 0, "rows per workgroup");
+  extern __shared__ __attribute__((aligned(16))) uint8_t xlds[];
+  __shared__ float red[kMaxStrips][RG];
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
   const int nw = blockDim.x >> 6;
   const int ns = K >> 5;
   const int64_t rb = F::row_bytes(K);
-  const int64_t m0 = (int64_t)blockIdx.x * R;
+  const int64_t m0 = (int64_t)blockIdx.x * RG;
+  uint8_t* strip = xlds + wv * kXStripBytes;
 
-  float part[R];
+  float part[RG];
 #pragma unroll
-  for (int r = 0; r < R; ++r) part[r] = 0.0f;
+  for (int r = 0; r < RG; ++r) part[r] = 0.0f;
 
   for (int base = wv * kWave; base < ns; base += nw * kWave) {
     const int j = base + lane;
+    x_to_lds(x + (int64_t)base * 32, ns - base, strip, lane);
     if (j < ns) {
       BlockLane L[2];
       if (F::kBytes == 144) {  // Q4_K: header and the sub-block's 16 code bytes
@@ -312,57 +520,84 @@ __global__ __launch_bounds__(kMaxStrips * kWave) void gemv_kernel(const uint8_t*
         L[0] = block_lane(o, 0u, F::kBytes);
         L[1] = block_lane(o, kOdd ? 2u : 0u, F::kBytes);
       }
-      f32x4 xv[8];
-      load_x32(x + (int64_t)j * 32, xv);
-      typename F::Raw raw[R];
+      typename F::Raw raw[2][R];
+      auto load_group = [&](int g, typename F::Raw(&dst)[R]) {
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        // rows past M re-read the last row of the same parity (their sums
-        // are discarded); with an odd stride M >= 2 here
-        int64_t m = m0 + r;
-        if (m >= M) m = kOdd ? M - 1 - ((M - 1 - r) & 1) : M - 1;
-        F::load(B + m * rb, L[kOdd ? (r & 1) : 0], raw[r]);
-      }
-      // every load above is issued before any is consumed
+        for (int r = 0; r < R; ++r) {
+          // rows past M re-read the last row of the same parity (their
+          // sums are discarded); with an odd stride M >= 2 here
+          int64_t m = m0 + g * R + r;
+          if (m >= M) m = kOdd ? M - 1 - ((M - 1 - r) & 1) : M - 1;
+          F::load(B + m * rb, L[kOdd ? (r & 1) : 0], dst[r]);
+        }
+      };
+      load_group(0, raw[0]);
+      // Memory loads complete in issue order, so once no more than the
+      // first group's R * kLoads weight loads are outstanding, every
+      // activation load issued before them has landed in LDS. (The compiler
+      // does not track direct-to-LDS loads, hence the explicit wait.)
       __builtin_amdgcn_sched_barrier(0);
-      XPrep xp;
-      prep_x(xv, xp);
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm<R * F::kLoads>());
+      __builtin_amdgcn_sched_barrier(0);
+      f32x4 xv[8];
+      x_from_lds(strip, lane, xv);
+      typename F::XP xp;
+      F::prep(xv, xp);
+      typename F::Acc ac = {};
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const float t = F::apply(raw[r], L[kOdd ? (r & 1) : 0], xp, lane & 7);
-        part[r] = fmaf(t, xp.inv, part[r]);
+      for (int g = 0; g < G; ++g) {
+        // the next group's loads are in flight while this one is consumed
+        if (g + 1 < G) {
+          load_group(g + 1, raw[(g + 1) & 1]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+          part[g * R + r] = fmaf(F::apply(raw[g & 1][r], L[kOdd ? (r & 1) : 0], xp, j, ac),
+                                 xp.inv, part[g * R + r]);
       }
     }
   }
 
-  const float sum = wave_reduce_rows<R>(part, lane);
-  constexpr int kShift = 6 - log2i<R>();
-  const int row = (lane >> kShift) & (R - 1);
+  constexpr int kShift = 6 - log2i<RG>();
+  const int row = (lane >> kShift) & (RG - 1);
+  const float sum = wave_reduce_rows<RG>(part, lane);
   if ((lane & ((1 << kShift) - 1)) == 0) red[wv][row] = sum;
   __syncthreads();
-  if ((int)threadIdx.x < R) {
+  if ((int)threadIdx.x < RG) {
     float t = 0.0f;
     for (int w = 0; w < nw; ++w) t += red[w][threadIdx.x];
     if (m0 + threadIdx.x < M) y[m0 + threadIdx.x] = t;
   }
 }
 
-template <class F>
+#ifndef QMAT_GEMV_CFG
+// rows per group, groups per workgroup
+#define QMAT_GEMV_R_Q4_0 4
+#define QMAT_GEMV_G_Q4_0 4
+#define QMAT_GEMV_R_Q8_0 2
+#define QMAT_GEMV_G_Q8_0 8
+#define QMAT_GEMV_R_Q4_K 4
+#define QMAT_GEMV_G_Q4_K 4
+#endif
+
+template <class F, int R, int G>
 hipError_t launch_fmt(const void* blocks, const float* x, float* y, int64_t M, int64_t K,
                       hipStream_t stream) {
   const int64_t ns = K / 32;
   int waves = (int)((ns + kWave - 1) / kWave);
   if (waves < 1) waves = 1;
   if (waves > kMaxStrips) waves = kMaxStrips;
-  const int64_t grid = (M + kRows - 1) / kRows;
+  const int64_t grid = (M + R * G - 1) / (R * G);
+  const size_t lds = (size_t)waves * kXStripBytes;
   // a single row has only the even parity: the aligned variant covers it
   const bool odd = F::kBytes != 144 && (ns & 1) != 0 && M > 1;
   if (odd)
-    hipLaunchKernelGGL((gemv_kernel<F, true>), dim3((unsigned)grid), dim3(waves * kWave), 0,
-                       stream, static_cast<const uint8_t*>(blocks), x, y, M, (int)K);
+    hipLaunchKernelGGL((gemv_kernel<F, R, G, true>), dim3((unsigned)grid), dim3(waves * kWave),
+                       lds, stream, static_cast<const uint8_t*>(blocks), x, y, M, (int)K);
   else
-    hipLaunchKernelGGL((gemv_kernel<F, false>), dim3((unsigned)grid), dim3(waves * kWave), 0,
-                       stream, static_cast<const uint8_t*>(blocks), x, y, M, (int)K);
+    hipLaunchKernelGGL((gemv_kernel<F, R, G, false>), dim3((unsigned)grid), dim3(waves * kWave),
+                       lds, stream, static_cast<const uint8_t*>(blocks), x, y, M, (int)K);
   return hipGetLastError();
 }
 
@@ -372,9 +607,12 @@ hipError_t launch_gemv(int fmt, const void* blocks, const float* x, float* y, in
                        int64_t K, hipStream_t stream) {
   if (M == 0) return hipSuccess;
   switch (fmt) {
-    case kFmtQ4_0: return launch_fmt<FmtQ4_0>(blocks, x, y, M, K, stream);
-    case kFmtQ8_0: return launch_fmt<FmtQ8_0>(blocks, x, y, M, K, stream);
-    default: return launch_fmt<FmtQ4_K>(blocks, x, y, M, K, stream);
+    case kFmtQ4_0:
+      return launch_fmt<FmtQ4_0, QMAT_GEMV_R_Q4_0, QMAT_GEMV_G_Q4_0>(blocks, x, y, M, K, stream);
+    case kFmtQ8_0:
+      return launch_fmt<FmtQ8_0, QMAT_GEMV_R_Q8_0, QMAT_GEMV_G_Q8_0>(blocks, x, y, M, K, stream);
+    default:
+      return launch_fmt<FmtQ4_K, QMAT_GEMV_R_Q4_K, QMAT_GEMV_G_Q4_K>(blocks, x, y, M, K, stream);
   }
 }
 

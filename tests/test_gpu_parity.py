@@ -159,7 +159,7 @@ def gemv_case(q, fmt, W, x):
 def test_gemv_small_and_ragged(q, fmt):
     rng = np.random.default_rng(200 + fmt)
     shapes = [(1, 256), (3, 512), (17, 2048), (31, 11008 if fmt == 2 else 32 * 345), (70, 4096),
-              (129, 1024), (9, 256 * 40)]
+              (129, 1024), (9, 256 * 40), (6, 256 * 72)]
     if fmt != 2:
         shapes += [(1, 32), (5, 32 * 37), (2, 64), (40, 32 * 1001)]
     for M, K in shapes:
