@@ -5,25 +5,41 @@ Workload ("llama7b_layer"): one 7B-like FFN weight, W 4096 x 11008 fp32 drawn
 from N(0, 0.02^2), a decode activation x (11008, N(0,1)) and a prefill batch
 of 512 tokens X (512 x 11008, N(0,1)); synthetic, seeded.
 
-One step runs every part of the hot path once, each launch on the stream
-torch uses, bracketed by HIP events:
+One step runs every part of the hot path once, on the stream torch uses:
   quantize W -> Q4_0, Q8_0, Q4_K       (fp32 read once per format)
   GEMV  Q4_0, Q8_0, Q4_K               (decode, one token)
   quantize X -> Q8_0                   (activation quantizer)
   GEMM  Q4_0 x Q8_0 activations        (prefill, int8 MFMA)
 Inputs are resident in HBM before timing starts. The GEMVs read a different
-copy of the packed weights every step, the copies together exceeding the
+copy of the packed weights at every launch, the copies together exceeding the
 256 MB Infinity Cache, so they stream from HBM; the quantizers rotate fp32
 copies the same way.
 
+Timing, two passes:
+  * steps: the contract's K steps, bracketed by synchronisations, wall clock
+    (ms_per_step; includes the host's launch cost).
+  * kernels: each kernel launched K times back to back (at least 50), with a
+    HIP event before and after the batch on the launch stream. The stream is
+    first filled with a GPU sleep long enough for the host to enqueue the
+    whole batch behind it (checked, and lengthened if the sleep ended first),
+    so the events see the GPU's own time per launch, which agrees with
+    rocprofv3's kernel durations.
+
 Output: one JSON line. ``value`` is the Q4_0 GEMV's algorithmic bytes
-(packed weights + x + y) divided by its mean event-timed duration, the
-headline of the metric; the GEMM's int8 TOPS and every other kernel's rate
-and roofline fraction are reported beside it.
+(packed weights + x + y) divided by its mean time per launch, the headline of
+the metric; the GEMM's int8 TOPS and every other kernel's rate and roofline
+fraction are reported beside it.
+
+``--summarize-pmc FETCH.csv WRITE.csv`` (no GPU) turns the counter files of
+two ``rocprofv3 --pmc FETCH_SIZE`` / ``--pmc WRITE_SIZE`` runs of
+``bench.py --only gemv_q4_0,copy`` into the traffic summary that later runs
+report as ``roofline.traffic``.
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import hashlib
 import json
 import math
 import os
@@ -41,6 +57,11 @@ HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
 INT8_PEAK_TOPS = 5000.0     # MI355X dense int8 MFMA (5.0 POPS)
 M, K, N = 4096, 11008, 512
 COLD_BYTES = 1.5 * 2 ** 30  # > 256 MB Infinity Cache, several times over
+COPY_BYTES = 64 * 2 ** 20   # calibration copy for the byte counters
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_q4_0_llama7b_traffic.json")
+GEMV_SRC = os.path.join(ROOT, "block_quantized_weight_qmat_amd", "csrc", "gemv.hip")
+ALL_OPS = ["quantize_q4_0", "quantize_q8_0", "quantize_q4_k", "gemv_q4_0", "gemv_q8_0",
+           "gemv_q4_k", "quantize_act_q8_0", "gemm_q4_0"]
 
 
 def parse():
@@ -52,8 +73,10 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="approximate CPU time for the oracle baseline sample")
     p.add_argument("--only", default="all",
-                   help="comma list of kernels to run (for counter runs): "
-                        "quantize,gemv,actq,gemm or all")
+                   help="comma list of ops (" + ",".join(ALL_OPS) + ",copy) or all")
+    p.add_argument("--batch", type=int, default=0,
+                   help="launches per kernel-timing batch (default max(steps, 50))")
+    p.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     return p.parse_args()
 
 
@@ -63,11 +86,109 @@ def rel_l2(a, ref):
     return float(np.linalg.norm(a - ref) / np.linalg.norm(ref))
 
 
+def source_hash(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+# ------------------------------------------------------------------ counters
+def _counter_rows(path: str, counter: str) -> list:
+    with open(path) as f:
+        return [r for r in csv.DictReader(f) if r.get("Counter_Name") == counter]
+
+
+def summarize_pmc(fetch_csv: str, write_csv: str):
+    """The two runs execute the same command, so their dispatch ids match.
+    The calibration copies are the copy dispatches that write COPY_BYTES
+    (the same copy kernel also serves the other tensor copies)."""
+    fetch = _counter_rows(fetch_csv, "FETCH_SIZE")
+    write = _counter_rows(write_csv, "WRITE_SIZE")
+    is_gemv = lambda r: "gemv_kernel" in r["Kernel_Name"] and "FmtQ4_0" in r["Kernel_Name"]
+    is_copy = lambda r: "copy" in r["Kernel_Name"].lower()
+    kib = COPY_BYTES / 1024.0
+    copy_ids = {r["Dispatch_Id"] for r in write
+                if is_copy(r) and abs(float(r["Counter_Value"]) - kib) < 0.05 * kib}
+    if not copy_ids:
+        raise SystemExit("no calibration copy found in the WRITE_SIZE run")
+    mean = lambda rows: float(np.mean([float(r["Counter_Value"]) for r in rows]))
+    cfetch = mean([r for r in fetch if r["Dispatch_Id"] in copy_ids])
+    cwrite = mean([r for r in write if r["Dispatch_Id"] in copy_ids])
+    gf = [r for r in fetch if is_gemv(r)]
+    gw = [r for r in write if is_gemv(r)]
+    if not gf or not gw:
+        raise SystemExit("no Q4_0 GEMV dispatch in the counter files")
+    gfetch, gwrite = mean(gf), mean(gw)
+    # the counters are in KiB per dispatch; the plain copy reads and writes
+    # exactly COPY_BYTES, which calibrates each counter
+    f_scale = COPY_BYTES / (cfetch * 1024.0)
+    w_scale = COPY_BYTES / (cwrite * 1024.0)
+    out = {
+        "kernel": gf[0]["Kernel_Name"],
+        "gemv_src_sha256_16": source_hash(GEMV_SRC),
+        "gemv_dispatches": len(gf),
+        "fetch_kib_per_dispatch": gfetch,
+        "write_kib_per_dispatch": gwrite,
+        "copy_kernel": next(r["Kernel_Name"] for r in write if r["Dispatch_Id"] in copy_ids),
+        "copy_dispatches": len(copy_ids),
+        "copy_bytes": COPY_BYTES,
+        "copy_fetch_kib": cfetch,
+        "copy_write_kib": cwrite,
+        "fetch_scale": f_scale,
+        "write_scale": w_scale,
+        "traffic_bytes_per_launch": gfetch * 1024.0 * f_scale + gwrite * 1024.0 * w_scale,
+        "algorithmic_bytes_per_launch": M * 18 * (K // 32) + 4 * K + 4 * M,
+    }
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
+
+
+def traffic_for_current_kernel():
+    """HBM bytes per Q4_0 GEMV launch from the stored counter summary, or
+    None when there is none or the kernel source changed since."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("gemv_src_sha256_16") != source_hash(GEMV_SRC):
+        return None
+    return float(t["traffic_bytes_per_launch"])
+
+
+# ------------------------------------------------------------------ timing
+def timed_batch(torch, fn, n: int) -> float:
+    """Mean GPU time per launch (us) of n back-to-back launches of fn(i)."""
+    stream = torch.cuda.current_stream()
+    fill_us = 40.0 * n
+    for _ in range(5):
+        torch.cuda.synchronize()
+        torch.cuda._sleep(int(fill_us * 2000))  # ~2 GHz shader clock
+        mark = torch.cuda.Event()
+        mark.record(stream)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(n):
+            fn(i)
+        b.record(stream)
+        starved = mark.query()  # the sleep ended before the batch was queued
+        torch.cuda.synchronize()
+        if not starved:
+            return 1e3 * a.elapsed_time(b) / n
+        fill_us *= 3
+    return 1e3 * a.elapsed_time(b) / n
+
+
 def main():
     args = parse()
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: the block-quantized GEMV/GEMM is run on a single "
-              "MI355X (a multi-GPU row split would scale it per GPU; it is not built).",
+        print("bench.py measures one GPU: the block-quantized GEMV/GEMM runs on a single "
+              "MI355X here (a row split of W would scale it across GPUs; that is not built).",
               file=sys.stderr)
         sys.exit(2)
 
@@ -77,7 +198,7 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    only = set(args.only.split(",")) if args.only != "all" else {"quantize", "gemv", "actq", "gemm"}
+    only = ALL_OPS if args.only == "all" else args.only.split(",")
 
     # ------------------------------------------------------------ inputs
     W_np, x_np = inputs.llama7b_layer(0)
@@ -89,16 +210,19 @@ def main():
     torch.cuda.synchronize()
 
     def copies(t, total):
-        n = max(2, math.ceil(total / t.numel()))
+        n = max(2, math.ceil(total / (t.numel() * t.element_size())))
         return [t.clone() for _ in range(n)]
 
-    cold = {f: copies(packed[f], COLD_BYTES) for f in fmts}
-    W_rot = [Wf.clone() for _ in range(4)] if "quantize" in only else [Wf]
-    X_rot = [torch.from_numpy(X_np).to(dev) for _ in range(12 if "actq" in only else 1)]
+    need = lambda prefix: any(o.startswith(prefix) for o in only)
+    cold = {f: copies(packed[f], COLD_BYTES) if need("gemv_" + f) else [packed[f]] for f in fmts}
+    W_rot = [Wf] + ([Wf.clone()] if need("quantize_q") else [])
+    X_rot = [torch.from_numpy(X_np).to(dev) for _ in range(12 if need("quantize_act") else 1)]
     q_out = {f: torch.empty_like(packed[f]) for f in fmts}
     y = {f: torch.empty(M, dtype=torch.float32, device=dev) for f in fmts}
     Xq = binding.quantize(1, X_rot[0])
     Y = torch.empty((N, M), dtype=torch.float32, device=dev)
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
     torch.cuda.synchronize()
 
     rb = {f: binding.row_bytes(i, K) for f, i in fmts.items()}
@@ -107,60 +231,33 @@ def main():
     actq_bytes = 4 * N * K + N * binding.row_bytes(1, K)
     gemm_ops = 2 * M * N * K
 
-    ops = []
-    if "quantize" in only:
-        for f, i in fmts.items():
-            ops.append((f"quantize_{f}", lambda s, f=f, i=i: binding.quantize(
-                i, W_rot[s % len(W_rot)], out=q_out[f])))
-    if "gemv" in only:
-        for f, i in fmts.items():
-            ops.append((f"gemv_{f}", lambda s, f=f, i=i: binding.gemv(
-                i, cold[f][s % len(cold[f])], x, M, K, out=y[f])))
-    if "actq" in only:
-        ops.append(("quantize_act_q8_0", lambda s: binding.quantize(1, X_rot[s % len(X_rot)], out=Xq)))
-    if "gemm" in only:
-        ops.append(("gemm_q4_0", lambda s: binding.gemm(0, packed["q4_0"], Xq, M, K, N, out=Y)))
+    table = {}
+    for f, i in fmts.items():
+        table[f"quantize_{f}"] = lambda s, f=f, i=i: binding.quantize(
+            i, W_rot[s % len(W_rot)], out=q_out[f])
+        table[f"gemv_{f}"] = lambda s, f=f, i=i: binding.gemv(
+            i, cold[f][s % len(cold[f])], x, M, K, out=y[f])
+    table["quantize_act_q8_0"] = lambda s: binding.quantize(1, X_rot[s % len(X_rot)], out=Xq)
+    table["gemm_q4_0"] = lambda s: binding.gemm(0, packed["q4_0"], Xq, M, K, N, out=Y)
+    table["copy"] = lambda s: dst.copy_(src)
+    ops = [(name, table[name]) for name in only]
 
-    def run(steps, offset, timed):
-        evs = {name: [] for name, _ in ops}
-        for s in range(steps):
-            for name, fn in ops:
-                if timed:
-                    a = torch.cuda.Event(enable_timing=True)
-                    b = torch.cuda.Event(enable_timing=True)
-                    a.record()
-                    fn(s + offset)
-                    b.record()
-                    evs[name].append((a, b))
-                else:
-                    fn(s + offset)
-        return evs
-
-    run(args.warmup, 0, timed=False)
+    # ------------------------------------------------------------ steps
+    for s in range(args.warmup):
+        for _, fn in ops:
+            fn(s)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    evs = run(args.steps, args.warmup, timed=True)
+    for s in range(args.steps):
+        for _, fn in ops:
+            fn(args.warmup + s)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    mean_us = {name: 1e3 * float(np.mean([a.elapsed_time(b) for a, b in v])) for name, v in evs.items()}
+    # ------------------------------------------------------------ kernels
+    nb = args.batch if args.batch > 0 else max(args.steps, 50)
+    mean_us = {name: timed_batch(torch, fn, nb) for name, fn in ops if name != "copy"}
 
-    # back-to-back GEMV launches (no events between): average includes the
-    # dispatch gaps, i.e. what a decode loop of such GEMVs would see
-    b2b = {}
-    if "gemv" in only:
-        for f, i in fmts.items():
-            n = 4 * len(cold[f])
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
-            a.record()
-            for s in range(n):
-                binding.gemv(i, cold[f][s % len(cold[f])], x, M, K, out=y[f])
-            b.record()
-            torch.cuda.synchronize()
-            b2b[f] = 1e3 * a.elapsed_time(b) / n
-
-    # ------------------------------------------------------------ rates
     kernels = {}
     for name, us in mean_us.items():
         if name.startswith("gemv_"):
@@ -168,9 +265,6 @@ def main():
             gbs = gemv_bytes[f] / us / 1e3
             kernels[name] = {"us": us, "bytes": gemv_bytes[f], "GB/s": gbs, "bound": "hbm",
                              "frac": gbs / HBM_PEAK_GBS}
-            if f in b2b:
-                kernels[name]["us_back_to_back"] = b2b[f]
-                kernels[name]["GB/s_back_to_back"] = gemv_bytes[f] / b2b[f] / 1e3
         elif name.startswith("quantize_act"):
             gbs = actq_bytes / us / 1e3
             kernels[name] = {"us": us, "bytes": actq_bytes, "GB/s": gbs, "bound": "hbm",
@@ -187,22 +281,24 @@ def main():
 
     # ------------------------------------------------------------ parity
     parity = {}
-    import oracle
-    if "gemv" in only:
-        ref = oracle.gemv(0, packed["q4_0"].cpu().numpy(), x_np, M, K)
-        parity["gemv_q4_0_rel_l2"] = rel_l2(y["q4_0"].cpu().numpy(), ref)
-    if "gemm" in only:
-        rng = np.random.default_rng(1)
-        rows = np.sort(rng.choice(M, 32, replace=False))
-        toks = np.sort(rng.choice(N, 16, replace=False))
-        Bh = packed["q4_0"].cpu().numpy()
-        Xh = Xq.cpu().numpy()
-        refY = oracle.gemm(0, Bh[rows], Xh[toks], len(rows), K, len(toks))
-        parity["gemm_q4_0_sampled_rel_l2"] = rel_l2(Y.cpu().numpy()[np.ix_(toks, rows)], refY)
+    if "gemv_q4_0" in mean_us or "gemm_q4_0" in mean_us:
+        import oracle
+        if "gemv_q4_0" in mean_us:
+            ref = oracle.gemv(0, packed["q4_0"].cpu().numpy(), x_np, M, K)
+            parity["gemv_q4_0_rel_l2"] = rel_l2(y["q4_0"].cpu().numpy(), ref)
+        if "gemm_q4_0" in mean_us:
+            rng = np.random.default_rng(1)
+            rows = np.sort(rng.choice(M, 32, replace=False))
+            toks = np.sort(rng.choice(N, 16, replace=False))
+            Bh = packed["q4_0"].cpu().numpy()
+            Xh = Xq.cpu().numpy()
+            refY = oracle.gemm(0, Bh[rows], Xh[toks], len(rows), K, len(toks))
+            parity["gemm_q4_0_sampled_rel_l2"] = rel_l2(Y.cpu().numpy()[np.ix_(toks, rows)], refY)
 
     # ------------------------------------------------------------ CPU oracle
     cpu = None
-    if not args.no_cpu_baseline and "gemv" in only:
+    if not args.no_cpu_baseline and "gemv_q4_0" in mean_us:
+        import oracle
         Bh = packed["q4_0"].cpu().numpy()
         reps, t_cpu = 0, 0.0
         t1 = time.perf_counter()
@@ -210,13 +306,14 @@ def main():
             oracle.gemv(0, Bh, x_np, M, K)
             reps += 1
             t_cpu = time.perf_counter() - t1
-        cpu = {"value": gemv_bytes["q4_0"] * reps / t_cpu / 1e9, "unit": "GB/s",
+        cpu = {"value": round(gemv_bytes["q4_0"] * reps / t_cpu / 1e9, 3), "unit": "GB/s",
                "cores": oracle.num_threads(), "kind": "oracle",
-               "sample": f"{reps} full Q4_0 GEMVs 4096x11008 (dequantize to fp64, fp64 dot), "
-                         f"{t_cpu:.1f} s, same algorithmic bytes as the GPU figure"}
+               "sample": f"{reps} full Q4_0 GEMVs 4096x11008 (dequantize to fp64, fp64 dot, "
+                         f"OpenMP over rows) in {t_cpu:.1f} s; same algorithmic bytes as value"}
 
     headline = kernels.get("gemv_q4_0")
     gemm = kernels.get("gemm_q4_0")
+    traffic = traffic_for_current_kernel() if headline else None
     out = {
         "metric": METRIC,
         "value": round(headline["GB/s"], 1) if headline else None,
@@ -228,15 +325,17 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16",
+        "dtype": "i4*i20->i32, f32 acc",
         "data": "synthetic",
-        "config": {"workload": "llama7b_layer: Q4_0 W 4096x11008 decode GEMV; prefill GEMM "
-                               "over 512 tokens (Q8_0 activations, int8 MFMA)",
+        "config": {"workload": "llama7b_layer: Q4_0 GEMV W 4096x11008 (decode, one token); "
+                               "prefill GEMM over 512 tokens (Q8_0 activations, int8 MFMA)",
                    "M": M, "K": K, "prefill_tokens": N, "seed": 0},
         "roofline": None if not headline else {
             "bound": "hbm", "achieved": round(headline["GB/s"], 1), "peak": HBM_PEAK_GBS,
-            "unit": "GB/s", "frac": round(headline["frac"], 4), "traffic": None,
-            "kernel": "gemv_q4_0"},
+            "unit": "GB/s", "frac": round(headline["frac"], 4),
+            "traffic": None if traffic is None else round(traffic),
+            "kernel": "gemv_q4_0", "bytes_per_launch": gemv_bytes["q4_0"],
+            "us_per_launch": round(headline["us"], 3)},
         "gemm_int8_tops": None if not gemm else round(gemm["TOPS"], 1),
         "gemm_frac_of_int8_peak": None if not gemm else round(gemm["frac"], 4),
         "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
