@@ -41,12 +41,17 @@ namespace qmat {
 namespace {
 
 #ifndef QMAT_GEMM_DEPTH
-#define QMAT_GEMM_DEPTH 2
+#define QMAT_GEMM_DEPTH 1
 #endif
 constexpr int kBM = 128;
 constexpr int kBN = 64;
 constexpr int kKB = 8;  // K-blocks per stage
-constexpr int kThreads = 512;     // compute threads (8 waves)
+#ifndef QMAT_GEMM_NT
+#define QMAT_GEMM_NT 2
+#endif
+// each compute wave owns 32 rows x (32 * kNT) columns of the 128 x 64 tile
+constexpr int kNT = QMAT_GEMM_NT;  // 32-column MFMA tiles per compute wave
+constexpr int kThreads = 512 / kNT;  // compute threads
 constexpr int kLoadThreads = 256; // loader threads (4 waves)
 constexpr int kDepth = QMAT_GEMM_DEPTH;  // stages a loader thread holds in registers
 constexpr uint32_t kMagicI = 0x4B400000u;  // 1.5 * 2^23 as fp32 bits
@@ -146,9 +151,9 @@ __device__ __forceinline__ void mfma_block(const Stage& cur, int bb, int wm, int
 // acc += dw * dx * S for the 16 values per lane (lane l holds column l % 32
 // and rows 8q + 4(l / 32) + r of the tile); Q4_K-style also subtracts
 // O * dx * sum(xq).
-template <int FMT>
-__device__ __forceinline__ void epilogue(const Stage& cur, int bb, int wm, int wn, int l32,
-                                         int half, const i32x16& d, float (&acc)[16]) {
+template <int FMT, int NT>
+__device__ __forceinline__ void epilogue(const Stage& cur, int bb, int wm, int wn0, int l32,
+                                         int half, const i32x16 (&d)[NT], float (&acc)[NT][16]) {
   float dw[16], wo[16];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
@@ -165,18 +170,22 @@ __device__ __forceinline__ void epilogue(const Stage& cur, int bb, int wm, int w
       wo[4 * q + 3] = o.w;
     }
   }
-  const float dx = cur.xd[bb][wn * 32 + l32];
-  const f32x16 df = __builtin_bit_cast(f32x16, d);
-  const float c1 = -kMagicF * dx;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const float sdx = fmaf(df[i], dx, c1);
-    acc[i] = fmaf(sdx, dw[i], acc[i]);
-  }
-  if (FMT == kFmtQ4_K) {
-    const float xs = cur.xs[bb][wn * 32 + l32];
+  for (int t = 0; t < NT; ++t) {
+    const int col = (wn0 + t) * 32 + l32;
+    const float dx = cur.xd[bb][col];
+    const f32x16 df = __builtin_bit_cast(f32x16, d[t]);
+    const float c1 = -kMagicF * dx;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[i] = fmaf(-wo[i], xs, acc[i]);
+    for (int i = 0; i < 16; ++i) {
+      const float sdx = fmaf(df[i], dx, c1);
+      acc[t][i] = fmaf(sdx, dw[i], acc[t][i]);
+    }
+    if (FMT == kFmtQ4_K) {
+      const float xs = cur.xs[bb][col];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[t][i] = fmaf(-wo[i], xs, acc[t][i]);
+    }
   }
 }
 
@@ -343,50 +352,59 @@ __global__ __launch_bounds__(kThreads + kLoadThreads) void gemm_kernel(const uin
       i32x16 cmagic;
 #pragma unroll
       for (int i = 0; i < 16; ++i) cmagic[i] = (int)kMagicI;
-      const int wm = wv & 3, wn = wv >> 2;  // this wave's 32 x 32 tile
-      float acc[16];
+      const int wm = wv & 3, wn0 = (wv >> 2) * kNT;  // rows 32wm.., column tiles wn0..
+      float acc[kNT][16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
+      for (int t = 0; t < kNT; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[t][i] = 0.0f;
 
       __syncthreads();  // stage 0 is in LDS
       for (int s = 0; s < nstage; ++s) {
         const Stage& cur = st[s & 1];
         const int nbs = min(kKB, nb - s * kKB);
         if (nbs == kKB) {
-          // full stage: the MFMA of block bb+1 is issued before the scale
+          // full stage: the MFMAs of block bb+1 are issued before the scale
           // epilogue of block bb, so the matrix core and the VALU overlap
-          i32x16 d[2];
-          mfma_block(cur, 0, wm, wn, l32, half, cmagic, d[0]);
+          i32x16 d[2][kNT];
+#pragma unroll
+          for (int t = 0; t < kNT; ++t) mfma_block(cur, 0, wm, wn0 + t, l32, half, cmagic, d[0][t]);
 #pragma unroll
           for (int bb = 0; bb < kKB; ++bb) {
-            if (bb + 1 < kKB) mfma_block(cur, bb + 1, wm, wn, l32, half, cmagic, d[(bb + 1) & 1]);
-            epilogue<FMT>(cur, bb, wm, wn, l32, half, d[bb & 1], acc);
+            if (bb + 1 < kKB)
+#pragma unroll
+              for (int t = 0; t < kNT; ++t)
+                mfma_block(cur, bb + 1, wm, wn0 + t, l32, half, cmagic, d[(bb + 1) & 1][t]);
+            epilogue<FMT, kNT>(cur, bb, wm, wn0, l32, half, d[bb & 1], acc);
           }
         } else {
           for (int bb = 0; bb < nbs; ++bb) {
-            i32x16 d;
-            mfma_block(cur, bb, wm, wn, l32, half, cmagic, d);
-            epilogue<FMT>(cur, bb, wm, wn, l32, half, d, acc);
+            i32x16 d[kNT];
+#pragma unroll
+            for (int t = 0; t < kNT; ++t) mfma_block(cur, bb, wm, wn0 + t, l32, half, cmagic, d[t]);
+            epilogue<FMT, kNT>(cur, bb, wm, wn0, l32, half, d, acc);
           }
         }
         __syncthreads();
       }
 
-      // ---- store: lane holds column n = n0 + 32wn + l32, rows
+      // ---- store: lane holds column n = n0 + 32(wn0 + t) + l32, rows
       //      m = m0 + 32 wm + 8q + 4 half + r  (q, r in 0..3)
-      const int64_t n = n0 + 32 * wn + l32;
-      if (n < N) {
+#pragma unroll
+      for (int t = 0; t < kNT; ++t) {
+        const int64_t n = n0 + 32 * (wn0 + t) + l32;
+        if (n >= N) continue;
         float* yrow = Y + n * M;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int64_t mb = m0 + wm * 32 + 8 * q + 4 * half;
           if (mb + 3 < M && (M & 3) == 0) {
-            f32x4 v = {acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
+            f32x4 v = {acc[t][4 * q], acc[t][4 * q + 1], acc[t][4 * q + 2], acc[t][4 * q + 3]};
             *reinterpret_cast<f32x4*>(yrow + mb) = v;
           } else {
 #pragma unroll
             for (int r2 = 0; r2 < 4; ++r2)
-              if (mb + r2 < M) yrow[mb + r2] = acc[4 * q + r2];
+              if (mb + r2 < M) yrow[mb + r2] = acc[t][4 * q + r2];
           }
         }
       }

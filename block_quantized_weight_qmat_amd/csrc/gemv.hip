@@ -18,7 +18,8 @@
 //     the activation loads have landed (loads complete in issue order) the
 //     lane reads its slice back from LDS and converts it while the weights
 //     stream in; the converted slice serves all G x R rows from registers.
-//     Group g+1's loads are issued before group g is consumed.
+//     D row groups are requested before the conversion; group g+D is
+//     requested as soon as group g has been consumed.
 //     Activations loaded straight into registers, 128 bytes per lane, cost
 //     far more load bandwidth than the same bytes staged through LDS.
 //   * Row base addresses are wave-uniform (scalar registers), lane offsets
@@ -478,17 +479,19 @@ __device__ __forceinline__ void x_from_lds(const uint8_t* strip, int lane, f32x4
     v[k] = *reinterpret_cast<const f32x4*>(row + 16 * ((k + lane) & 7));
 }
 
-// A workgroup owns G groups of R rows. kOdd: the row stride is 2 mod 4
+// A workgroup owns G groups of R rows, D groups of loads in flight per
+// wave. kOdd: the row stride is 2 mod 4
 // (K/32 odd for Q4_0/Q8_0), so even and odd rows have different block
 // alignments; row m0 + r has parity r & 1 since m0 and the group size are
 // even.
-template <class F, int R, int G, bool kOdd>
+template <class F, int R, int G, int D, bool kOdd>
 __global__ __launch_bounds__(kMaxStrips * kWave) void gemv_kernel(const uint8_t* __restrict__ B,
                                                                   const float* __restrict__ x,
                                                                   float* __restrict__ y,
                                                                   int64_t M, int K) {
   constexpr int RG = R * G;
   static_assert(RG <= kWave && (RG & (RG - 1)) == 0, "rows per workgroup");
+  static_assert(D >= 1 && D <= G, "groups in flight");
   extern __shared__ __attribute__((aligned(16))) uint8_t xlds[];
   __shared__ float red[kMaxStrips][RG];
   const int lane = threadIdx.x & 63;
@@ -520,7 +523,7 @@ __global__ __launch_bounds__(kMaxStrips * kWave) void gemv_kernel(const uint8_t*
         L[0] = block_lane(o, 0u, F::kBytes);
         L[1] = block_lane(o, kOdd ? 2u : 0u, F::kBytes);
       }
-      typename F::Raw raw[2][R];
+      typename F::Raw raw[D][R];
       auto load_group = [&](int g, typename F::Raw(&dst)[R]) {
 #pragma unroll
         for (int r = 0; r < R; ++r) {
@@ -531,13 +534,17 @@ __global__ __launch_bounds__(kMaxStrips * kWave) void gemv_kernel(const uint8_t*
           F::load(B + m * rb, L[kOdd ? (r & 1) : 0], dst[r]);
         }
       };
-      load_group(0, raw[0]);
+      // D groups are in flight from the start, so the activation
+      // conversion below overlaps them; group g + D is requested as soon as
+      // group g has been consumed.
+#pragma unroll
+      for (int g = 0; g < D; ++g) load_group(g, raw[g]);
       // Memory loads complete in issue order, so once no more than the
-      // first group's R * kLoads weight loads are outstanding, every
-      // activation load issued before them has landed in LDS. (The compiler
-      // does not track direct-to-LDS loads, hence the explicit wait.)
+      // weight loads of those D groups are outstanding, every activation
+      // load issued before them has landed in LDS. (The compiler does not
+      // track direct-to-LDS loads, hence the explicit wait.)
       __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm<R * F::kLoads>());
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm<D * R * F::kLoads>());
       __builtin_amdgcn_sched_barrier(0);
       f32x4 xv[8];
       x_from_lds(strip, lane, xv);
@@ -546,15 +553,14 @@ __global__ __launch_bounds__(kMaxStrips * kWave) void gemv_kernel(const uint8_t*
       typename F::Acc ac = {};
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        // the next group's loads are in flight while this one is consumed
-        if (g + 1 < G) {
-          load_group(g + 1, raw[(g + 1) & 1]);
-          __builtin_amdgcn_sched_barrier(0);
-        }
 #pragma unroll
         for (int r = 0; r < R; ++r)
-          part[g * R + r] = fmaf(F::apply(raw[g & 1][r], L[kOdd ? (r & 1) : 0], xp, j, ac),
+          part[g * R + r] = fmaf(F::apply(raw[g % D][r], L[kOdd ? (r & 1) : 0], xp, j, ac),
                                  xp.inv, part[g * R + r]);
+        if (g + D < G) {
+          __builtin_amdgcn_sched_barrier(0);
+          load_group(g + D, raw[g % D]);
+        }
       }
     }
   }
@@ -572,16 +578,19 @@ __global__ __launch_bounds__(kMaxStrips * kWave) void gemv_kernel(const uint8_t*
 }
 
 #ifndef QMAT_GEMV_CFG
-// rows per group, groups per workgroup
-#define QMAT_GEMV_R_Q4_0 4
+// rows per group, groups per workgroup, groups in flight
+#define QMAT_GEMV_R_Q4_0 2
 #define QMAT_GEMV_G_Q4_0 4
+#define QMAT_GEMV_D_Q4_0 2
 #define QMAT_GEMV_R_Q8_0 2
-#define QMAT_GEMV_G_Q8_0 8
-#define QMAT_GEMV_R_Q4_K 4
-#define QMAT_GEMV_G_Q4_K 4
+#define QMAT_GEMV_G_Q8_0 4
+#define QMAT_GEMV_D_Q8_0 2
+#define QMAT_GEMV_R_Q4_K 2
+#define QMAT_GEMV_G_Q4_K 8
+#define QMAT_GEMV_D_Q4_K 3
 #endif
 
-template <class F, int R, int G>
+template <class F, int R, int G, int D>
 hipError_t launch_fmt(const void* blocks, const float* x, float* y, int64_t M, int64_t K,
                       hipStream_t stream) {
   const int64_t ns = K / 32;
@@ -593,11 +602,13 @@ hipError_t launch_fmt(const void* blocks, const float* x, float* y, int64_t M, i
   // a single row has only the even parity: the aligned variant covers it
   const bool odd = F::kBytes != 144 && (ns & 1) != 0 && M > 1;
   if (odd)
-    hipLaunchKernelGGL((gemv_kernel<F, R, G, true>), dim3((unsigned)grid), dim3(waves * kWave),
-                       lds, stream, static_cast<const uint8_t*>(blocks), x, y, M, (int)K);
+    hipLaunchKernelGGL((gemv_kernel<F, R, G, D, true>), dim3((unsigned)grid),
+                       dim3(waves * kWave), lds, stream, static_cast<const uint8_t*>(blocks), x,
+                       y, M, (int)K);
   else
-    hipLaunchKernelGGL((gemv_kernel<F, R, G, false>), dim3((unsigned)grid), dim3(waves * kWave),
-                       lds, stream, static_cast<const uint8_t*>(blocks), x, y, M, (int)K);
+    hipLaunchKernelGGL((gemv_kernel<F, R, G, D, false>), dim3((unsigned)grid),
+                       dim3(waves * kWave), lds, stream, static_cast<const uint8_t*>(blocks), x,
+                       y, M, (int)K);
   return hipGetLastError();
 }
 
@@ -608,11 +619,14 @@ hipError_t launch_gemv(int fmt, const void* blocks, const float* x, float* y, in
   if (M == 0) return hipSuccess;
   switch (fmt) {
     case kFmtQ4_0:
-      return launch_fmt<FmtQ4_0, QMAT_GEMV_R_Q4_0, QMAT_GEMV_G_Q4_0>(blocks, x, y, M, K, stream);
+      return launch_fmt<FmtQ4_0, QMAT_GEMV_R_Q4_0, QMAT_GEMV_G_Q4_0, QMAT_GEMV_D_Q4_0>(
+          blocks, x, y, M, K, stream);
     case kFmtQ8_0:
-      return launch_fmt<FmtQ8_0, QMAT_GEMV_R_Q8_0, QMAT_GEMV_G_Q8_0>(blocks, x, y, M, K, stream);
+      return launch_fmt<FmtQ8_0, QMAT_GEMV_R_Q8_0, QMAT_GEMV_G_Q8_0, QMAT_GEMV_D_Q8_0>(
+          blocks, x, y, M, K, stream);
     default:
-      return launch_fmt<FmtQ4_K, QMAT_GEMV_R_Q4_K, QMAT_GEMV_G_Q4_K>(blocks, x, y, M, K, stream);
+      return launch_fmt<FmtQ4_K, QMAT_GEMV_R_Q4_K, QMAT_GEMV_G_Q4_K, QMAT_GEMV_D_Q4_K>(
+          blocks, x, y, M, K, stream);
   }
 }
 

@@ -159,9 +159,10 @@ def gemv_case(q, fmt, W, x):
 def test_gemv_small_and_ragged(q, fmt):
     rng = np.random.default_rng(200 + fmt)
     shapes = [(1, 256), (3, 512), (17, 2048), (31, 11008 if fmt == 2 else 32 * 345), (70, 4096),
-              (129, 1024), (9, 256 * 40), (6, 256 * 72)]
+              (129, 1024), (9, 256 * 40), (6, 256 * 72), (64, 256 * 9), (200, 256 * 43)]
     if fmt != 2:
-        shapes += [(1, 32), (5, 32 * 37), (2, 64), (40, 32 * 1001)]
+        shapes += [(1, 32), (5, 32 * 37), (2, 64), (40, 32 * 1001), (100, 32 * 345),
+                   (65, 32 * 1001), (130, 32 * 65)]
     for M, K in shapes:
         say(f"gemv fmt={fmt} M={M} K={K}")
         W = mixed_matrix(rng, M, K) if M > 2 else rng.normal(0, 0.02, (M, K)).astype(np.float32)
@@ -173,13 +174,13 @@ def test_gemv_small_and_ragged(q, fmt):
 @pytest.mark.parametrize("fmt", [0, 1, 2])
 def test_gemv_one_hot_gives_the_column(q, fmt):
     rng = np.random.default_rng(300)
-    M, K = 40, 2048
-    W = rng.normal(0, 0.02, (M, K)).astype(np.float32)
-    B = oracle.quantize(fmt, W)
-    Wd = oracle.dequant(fmt, B, M, K)
-    dB = dev_tensor(B)
-    for k in (0, 15, 16, 31, 32, 1000, K - 1):
-        say(f"gemv one-hot fmt={fmt} k={k}")
+    for M, K, k in [(40, 2048, k) for k in (0, 15, 16, 31, 32, 1000, 2047)] + \
+                   [(70, 4096, k) for k in (0, 2047, 2048, 4095)]:
+        W = rng.normal(0, 0.02, (M, K)).astype(np.float32)
+        B = oracle.quantize(fmt, W)
+        Wd = oracle.dequant(fmt, B, M, K)
+        dB = dev_tensor(B)
+        say(f"gemv one-hot fmt={fmt} M={M} K={K} k={k}")
         x = np.zeros(K, np.float32)
         x[k] = 1.0
         y = host(q.gemv(fmt, dB, dev_tensor(x), M, K)).astype(np.float64)
@@ -197,11 +198,13 @@ def test_gemv_one_hot_gives_the_column(q, fmt):
 def test_gemv_activation_range(q, fmt):
     """Per-32 power-of-two prescaling keeps any finite x in fp16 range."""
     rng = np.random.default_rng(400)
-    M, K = 24, 4096
-    W = rng.normal(0, 0.02, (M, K)).astype(np.float32)
-    for name, scale in (("tiny", 1e-30), ("huge", 1e30), ("subnormal", 1e-40), ("mixed", None),
-                        ("binade-top", "top")):
-        say(f"gemv x-range fmt={fmt} {name}")
+    K = 4096
+    cases = [(M, name, scale) for M in (24, 70)
+             for name, scale in (("tiny", 1e-30), ("huge", 1e30), ("subnormal", 1e-40),
+                                 ("mixed", None), ("binade-top", "top"))]
+    for M, name, scale in cases:
+        say(f"gemv x-range fmt={fmt} M={M} {name}")
+        W = rng.normal(0, 0.02, (M, K)).astype(np.float32)
         x = rng.normal(0, 1, K)
         if scale == "top":
             # every slice's maximum is positive and just below a power of two
@@ -273,6 +276,31 @@ def test_gemv_deterministic(q):
     a = host(q.gemv(0, B, dx, 4096, 11008))
     b = host(q.gemv(0, B, dx, 4096, 11008))
     assert np.array_equal(a, b)
+
+
+def test_gemv_two_streams(q):
+    """Calls in flight on two streams at once."""
+    import torch
+    rng = np.random.default_rng(6)
+    cases = []
+    for M, K in ((4096, 11008), (300, 32 * 345)):
+        W = rng.normal(0, 0.02, (M, K)).astype(np.float32)
+        x = rng.normal(0, 1, K).astype(np.float32)
+        B = oracle.quantize(0, W)
+        cases.append((dev_tensor(B), dev_tensor(x), M, K, oracle.gemv(0, B, x, M, K)))
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    torch.cuda.synchronize()
+    outs = []
+    for rep in range(4):
+        say(f"gemv two streams rep {rep}")
+        for (dB, dx, M, K, _), st in zip(cases, streams):
+            with torch.cuda.stream(st):
+                outs.append((q.gemv(0, dB, dx, M, K), M, K))
+    torch.cuda.synchronize()
+    for i, (y, M, K) in enumerate(outs):
+        ref = cases[i % 2][4]
+        assert rel_l2(host(y), ref) <= GEMV_TOL, (i, M, K)
+        assert np.array_equal(host(y), host(outs[i % 2][0]))
 
 
 # ------------------------------------------------------------------ GEMM --
