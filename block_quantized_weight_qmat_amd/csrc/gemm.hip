@@ -111,32 +111,58 @@ struct StageRegs {
   uint32_t xs[kXItems];
 };
 
-// Byte address parity: blocks of 18 or 34 bytes start at 0 or 2 mod 4.
-__device__ __forceinline__ void load_blk(const uint8_t* b, int bytes, u32x4& va, u32x4& vb,
-                                         uint32_t& s2) {
-  const uint32_t a = (uint32_t)(reinterpret_cast<uintptr_t>(b) & 2u);
-  va = *reinterpret_cast<const u32x4_a4*>(b + a);
-  if (bytes == 34) vb = *reinterpret_cast<const u32x4_a4*>(b + a + 16);
-  s2 = *reinterpret_cast<const uint16_t*>(b + (a ? 0 : bytes - 2));
+// One loader item's fixed offsets from the stage base: an 18- or 34-byte
+// block at byte offset o starts at 0 or 2 mod 4. If 0, the 16-byte load(s)
+// at o hold the scale and the first code bytes and the 2-byte load at
+// o + bytes - 2 the last two code bytes; if 2, the 2-byte load at o is the
+// scale and the 16-byte load(s) at o + 2 hold the codes. sel realigns the
+// code words with v_perm; hsel picks the scale's two bytes.
+struct BlkLane {
+  uint32_t o16, o2, sel, hsel;
+};
+
+__device__ __forceinline__ BlkLane blk_lane(uint32_t o, uint32_t par, int bytes) {
+  const bool mis = ((o + par) & 2u) != 0;
+  BlkLane l;
+  l.o16 = o + (mis ? 2u : 0u);
+  l.o2 = o + (mis ? 0u : (uint32_t)bytes - 2u);
+  l.sel = mis ? 0x03020100u : 0x05040302u;
+  l.hsel = mis ? 0x0c0c0504u : 0x0c0c0100u;  // s2's or the first word's low half
+  return l;
 }
 
-// Realign the code words of a block loaded by load_blk; h = fp16 scale bits.
-__device__ __forceinline__ void realign(const uint8_t* b, int bytes, const u32x4& va,
-                                        const u32x4& vb, uint32_t s2, uint32_t& h,
-                                        uint32_t (&c)[8]) {
-  const uint32_t a = (uint32_t)(reinterpret_cast<uintptr_t>(b) & 2u);
-  const uint32_t sel = a ? 0x03020100u : 0x05040302u;
+// Buffer resource over [base, base + bytes) for raw buffer loads (gfx9
+// descriptor: stride 0, 32-bit dword data format); lane offsets are 32-bit
+// and the per-stage offset is a scalar register.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const uint8_t* base, int64_t bytes) {
+  const uint32_t n = bytes < (int64_t)0xFFFFFFFF ? (uint32_t)bytes : 0xFFFFFFFFu;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, (int)n,
+                                           0x00020000);
+}
+
+__device__ __forceinline__ void load_lane(__amdgpu_buffer_rsrc_t rs, uint32_t soff,
+                                          const BlkLane& l, int bytes, u32x4& va, u32x4& vb,
+                                          uint32_t& s2) {
+  va = __builtin_amdgcn_raw_buffer_load_b128(rs, l.o16, soff, 0);
+  if (bytes == 34) vb = __builtin_amdgcn_raw_buffer_load_b128(rs, l.o16 + 16u, soff, 0);
+  s2 = __builtin_amdgcn_raw_buffer_load_b16(rs, l.o2, soff, 0);
+}
+
+// Realign the code words of a block loaded by load_lane; h = fp16 scale bits.
+__device__ __forceinline__ void realign_lane(const BlkLane& l, int bytes, const u32x4& va,
+                                             const u32x4& vb, uint32_t s2, uint32_t& h,
+                                             uint32_t (&c)[8]) {
   if (bytes == 18) {
-    c[0] = perm_b32(va.y, va.x, sel);
-    c[1] = perm_b32(va.z, va.y, sel);
-    c[2] = perm_b32(va.w, va.z, sel);
-    c[3] = perm_b32(s2, va.w, sel);
+    c[0] = perm_b32(va.y, va.x, l.sel);
+    c[1] = perm_b32(va.z, va.y, l.sel);
+    c[2] = perm_b32(va.w, va.z, l.sel);
+    c[3] = perm_b32(s2, va.w, l.sel);
   } else {
     const uint32_t w[9] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w, s2};
 #pragma unroll
-    for (int i = 0; i < 8; ++i) c[i] = perm_b32(w[i + 1], w[i], sel);
+    for (int i = 0; i < 8; ++i) c[i] = perm_b32(w[i + 1], w[i], l.sel);
   }
-  h = a ? s2 : (va.x & 0xFFFFu);
+  h = perm_b32(s2, va.x, l.hsel);
 }
 
 // The MFMA tile of one K-block: rows 32wm..32wm+31 against columns
@@ -148,44 +174,73 @@ __device__ __forceinline__ void mfma_block(const Stage& cur, int bb, int wm, int
   d = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, bv, cmagic, 0, 0, 0);
 }
 
-// acc += dw * dx * S for the 16 values per lane (lane l holds column l % 32
-// and rows 8q + 4(l / 32) + r of the tile); Q4_K-style also subtracts
-// O * dx * sum(xq).
-template <int FMT, int NT>
-__device__ __forceinline__ void epilogue(const Stage& cur, int bb, int wm, int wn0, int l32,
-                                         int half, const i32x16 (&d)[NT], float (&acc)[NT][16]) {
-  float dw[16], wo[16];
+// Per-block scales a lane needs: dw of its 16 rows and dx of its column in
+// each of the NT tiles.
+template <int NT>
+struct Scales {
+  float dw[16];
+  float dx[NT];
+};
+
+template <int NT>
+__device__ __forceinline__ void load_scales(const Stage& cur, int bb, int wm, int wn0, int l32,
+                                            int half, Scales<NT>& sc) {
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const f32x4 t = *reinterpret_cast<const f32x4*>(&cur.wd[bb][wm * 32 + 8 * q + 4 * half]);
-    dw[4 * q + 0] = t.x;
-    dw[4 * q + 1] = t.y;
-    dw[4 * q + 2] = t.z;
-    dw[4 * q + 3] = t.w;
-    if (FMT == kFmtQ4_K) {
-      const f32x4 o = *reinterpret_cast<const f32x4*>(&cur.wo[bb][wm * 32 + 8 * q + 4 * half]);
-      wo[4 * q + 0] = o.x;
-      wo[4 * q + 1] = o.y;
-      wo[4 * q + 2] = o.z;
-      wo[4 * q + 3] = o.w;
-    }
+    sc.dw[4 * q + 0] = t.x;
+    sc.dw[4 * q + 1] = t.y;
+    sc.dw[4 * q + 2] = t.z;
+    sc.dw[4 * q + 3] = t.w;
   }
 #pragma unroll
+  for (int t = 0; t < NT; ++t) sc.dx[t] = cur.xd[bb][(wn0 + t) * 32 + l32];
+}
+
+// acc += dw * dx * S for the 16 values per lane (lane l holds column l % 32
+// and rows 8q + 4(l / 32) + r of the tile). The MFMA accumulated S onto
+// 1.5 * 2^23, so its result read as a float is 1.5 * 2^23 + S and
+// S * dx = fma(F, dx, -1.5 * 2^23 * dx) exactly (dx is an fp16 value).
+template <int NT>
+__device__ __forceinline__ void apply_scales(const Scales<NT>& sc, const i32x16 (&d)[NT],
+                                             float (&acc)[NT][16]) {
+  // Two passes of independent instructions: first every S * dx (in place of
+  // the MFMA results), then every accumulation, so that no instruction waits
+  // on the one just before it.
+  f32x16 df[NT];
+#pragma unroll
   for (int t = 0; t < NT; ++t) {
-    const int col = (wn0 + t) * 32 + l32;
-    const float dx = cur.xd[bb][col];
-    const f32x16 df = __builtin_bit_cast(f32x16, d[t]);
-    const float c1 = -kMagicF * dx;
+    const float c1 = -kMagicF * sc.dx[t];
+    df[t] = __builtin_bit_cast(f32x16, d[t]);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float sdx = fmaf(df[i], dx, c1);
-      acc[t][i] = fmaf(sdx, dw[i], acc[t][i]);
-    }
-    if (FMT == kFmtQ4_K) {
-      const float xs = cur.xs[bb][col];
+    for (int i = 0; i < 16; ++i) df[t][i] = fmaf(df[t][i], sc.dx[t], c1);
+  }
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc[t][i] = fmaf(-wo[i], xs, acc[t][i]);
-    }
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[t][i] = fmaf(df[t][i], sc.dw[i], acc[t][i]);
+}
+
+// Q4_K-style min term of blocks b0 and b0 + 1 (b0 + 1 < nbs, else only b0):
+// acc -= O[m, b] * xs[n, b] summed over the two blocks, as one fp32 MFMA
+// (32 x 32 x 2) whose output layout is that of the int8 MFMA. Lane l gives
+// A[row l % 32][block l / 32] = -O and B[block l / 32][column l % 32] = xs.
+template <int NT>
+__device__ __forceinline__ void min_term(const Stage& cur, int b0, int nbs, int wm, int wn0,
+                                         int l32, int half, float (&acc)[NT][16]) {
+  const int b = b0 + half;
+  const bool ok = b < nbs;
+  const float a = ok ? cur.wo[b][wm * 32 + l32] : 0.0f;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const float x = ok ? cur.xs[b][(wn0 + t) * 32 + l32] : 0.0f;
+    f32x16 c;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) c[i] = acc[t][i];
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(a, x, c, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[t][i] = c[i];
   }
 }
 
@@ -221,54 +276,74 @@ __global__ __launch_bounds__(kThreads + kLoadThreads) void gemm_kernel(const uin
     const int64_t m0 = tm * kBM, n0 = tn * kBN;
 
     if (loader) {
-      // item -> (row, block): 8 consecutive threads cover one row's 8 blocks.
-      // Rows are addressed from the tile's first row (a wave-uniform base)
-      // with 32-bit offsets; rows past M re-read the last row.
+      // item -> (row, block): 8 consecutive threads cover one row's 8
+      // blocks of a stage. A stage is the same 8 blocks of every row, so an
+      // item keeps its byte offsets from the stage's (wave-uniform) base,
+      // and its alignment case, for the whole tile. Rows past M re-read the
+      // last row.
+      constexpr int stage_wbytes = FMT == kFmtQ4_K ? 144 : kKB * wbytes;
       const uint8_t* wtile = Wb + m0 * wrb;
       const uint8_t* xtile = Xb + n0 * xrb;
       const uint32_t wlast = (uint32_t)min<int64_t>(kBM - 1, M - 1 - m0);
       const uint32_t xlast = (uint32_t)min<int64_t>(kBN - 1, N - 1 - n0);
-      auto w_row = [&](int it) -> const uint8_t* {
-        const uint32_t r = min((uint32_t)((tid + it * kLoadThreads) >> 3), wlast);
-        return wtile + r * (uint32_t)wrb;
-      };
-      auto x_row = [&](int it) -> const uint8_t* {
-        const uint32_t r = min((uint32_t)((tid + it * kLoadThreads) >> 3), xlast);
-        return xtile + r * (uint32_t)xrb;
-      };
+      // tile bases mod 4 (the buffers are 16-byte aligned, stage strides are
+      // multiples of 4)
+      const uint32_t wpar = (uint32_t)(m0 * wrb) & 3u, xpar = (uint32_t)(n0 * xrb) & 3u;
+      BlkLane wl[R::kWItems], xl[R::kXItems];
+#pragma unroll
+      for (int it = 0; it < R::kWItems; ++it) {
+        const int item = tid + it * kLoadThreads;
+        const uint32_t ro = min((uint32_t)(item >> 3), wlast) * (uint32_t)wrb;
+        if (FMT == kFmtQ4_K) {
+          wl[it].o16 = ro;  // superblock header
+          wl[it].o2 = ro + 16u + 16u * (uint32_t)(item & 7);  // sub-block codes
+          wl[it].sel = 0u;
+          wl[it].hsel = 0u;
+        } else {
+          wl[it] = blk_lane(ro + (uint32_t)(item & 7) * (uint32_t)wbytes, wpar, wbytes);
+        }
+      }
+#pragma unroll
+      for (int it = 0; it < R::kXItems; ++it) {
+        const int item = tid + it * kLoadThreads;
+        const uint32_t ro = min((uint32_t)(item >> 3), xlast) * (uint32_t)xrb;
+        xl[it] = blk_lane(ro + (uint32_t)(item & 7) * 34u, xpar, 34);
+      }
       // global -> registers for stage s (blocks past nb are not loaded)
+      // the bytes from each tile base to the end of its matrix
+      const __amdgpu_buffer_rsrc_t wrs = make_rsrc(wtile, (M - m0) * wrb);
+      const __amdgpu_buffer_rsrc_t xrs = make_rsrc(xtile, (N - n0) * xrb);
       auto load_stage = [&](int s, R& r) {
+        const uint32_t wso = (uint32_t)s * (uint32_t)stage_wbytes;
+        const uint32_t xso = (uint32_t)s * (uint32_t)(kKB * 34);
+        const int left = nb - s * kKB;  // blocks of this stage that exist
 #pragma unroll
         for (int it = 0; it < R::kWItems; ++it) {
-          const int b = s * kKB + ((tid + it * kLoadThreads) & 7);
-          if (b < nb) {
-            const uint8_t* row = w_row(it);
+          if (((tid + it * kLoadThreads) & 7) < left) {
             if (FMT == kFmtQ4_K) {
-              const uint8_t* sb = row + (int64_t)(b >> 3) * 144;
-              r.wa[it] = *reinterpret_cast<const u32x4*>(sb);
-              r.wb[it] = *reinterpret_cast<const u32x4*>(sb + 16 + 16 * (b & 7));
+              r.wa[it] = __builtin_amdgcn_raw_buffer_load_b128(wrs, wl[it].o16, wso, 0);
+              r.wb[it] = __builtin_amdgcn_raw_buffer_load_b128(wrs, wl[it].o2, wso, 0);
             } else {
-              load_blk(row + (int64_t)b * wbytes, wbytes, r.wa[it], r.wb[it], r.ws[it]);
+              load_lane(wrs, wso, wl[it], wbytes, r.wa[it], r.wb[it], r.ws[it]);
             }
           }
         }
 #pragma unroll
-        for (int it = 0; it < R::kXItems; ++it) {
-          const int b = s * kKB + ((tid + it * kLoadThreads) & 7);
-          if (b < nb) load_blk(x_row(it) + (int64_t)b * 34, 34, r.xa[it], r.xb[it], r.xs[it]);
-        }
+        for (int it = 0; it < R::kXItems; ++it)
+          if (((tid + it * kLoadThreads) & 7) < left)
+            load_lane(xrs, xso, xl[it], 34, r.xa[it], r.xb[it], r.xs[it]);
       };
       // registers -> LDS buffer for stage s
       auto write_stage = [&](int s, const R& r, Stage& dst) {
+        const int left = nb - s * kKB;
 #pragma unroll
         for (int it = 0; it < R::kWItems; ++it) {
           const int item = tid + it * kLoadThreads;
           const int rr = item >> 3, bb = item & 7;
-          const int b = s * kKB + bb;
-          if (b < nb) {
+          if (bb < left) {
             if (FMT == kFmtQ4_0) {
               uint32_t h, c[8];
-              realign(w_row(it) + (int64_t)b * 18, 18, r.wa[it], r.wb[it], r.ws[it], h, c);
+              realign_lane(wl[it], 18, r.wa[it], r.wb[it], r.ws[it], h, c);
               store16(dst.w(bb, 0, rr), nib_signed(c[0], 0), nib_signed(c[1], 0),
                       nib_signed(c[2], 0), nib_signed(c[3], 0));
               store16(dst.w(bb, 1, rr), nib_signed(c[0], 4), nib_signed(c[1], 4),
@@ -276,13 +351,13 @@ __global__ __launch_bounds__(kThreads + kLoadThreads) void gemm_kernel(const uin
               dst.wd[bb][rr] = f16_bits_to_f32(h);
             } else if (FMT == kFmtQ8_0) {
               uint32_t h, c[8];
-              realign(w_row(it) + (int64_t)b * 34, 34, r.wa[it], r.wb[it], r.ws[it], h, c);
+              realign_lane(wl[it], 34, r.wa[it], r.wb[it], r.ws[it], h, c);
               store16(dst.w(bb, 0, rr), c[0], c[1], c[2], c[3]);
               store16(dst.w(bb, 1, rr), c[4], c[5], c[6], c[7]);
               dst.wd[bb][rr] = f16_bits_to_f32(h);
             } else {
               const u32x4 hd = r.wa[it], cv = r.wb[it];
-              const int sub = b & 7;
+              const int sub = bb;  // a stage is one superblock
               const int ps = 6 * sub, pm = 48 + 6 * sub;
               const uint32_t slo = ps < 32 ? hd.y : hd.z, shi = ps < 32 ? hd.z : hd.w;
               const uint32_t mlo = pm < 64 ? hd.z : hd.w, mhi = pm < 64 ? hd.w : 0u;
@@ -293,7 +368,7 @@ __global__ __launch_bounds__(kThreads + kLoadThreads) void gemm_kernel(const uin
               store16(dst.w(bb, 1, rr), nib_unsigned(cv.x, 4), nib_unsigned(cv.y, 4),
                       nib_unsigned(cv.z, 4), nib_unsigned(cv.w, 4));
               dst.wd[bb][rr] = f16_bits_to_f32(hd.x) * (float)sc;
-              dst.wo[bb][rr] = f16_bits_to_f32(hd.x >> 16) * (float)mn;
+              dst.wo[bb][rr] = -(f16_bits_to_f32(hd.x >> 16) * (float)mn);  // -O
             }
           }
         }
@@ -301,10 +376,9 @@ __global__ __launch_bounds__(kThreads + kLoadThreads) void gemm_kernel(const uin
         for (int it = 0; it < R::kXItems; ++it) {
           const int item = tid + it * kLoadThreads;
           const int cc = item >> 3, bb = item & 7;
-          const int b = s * kKB + bb;
-          if (b < nb) {
+          if (bb < left) {
             uint32_t h, c[8];
-            realign(x_row(it) + (int64_t)b * 34, 34, r.xa[it], r.xb[it], r.xs[it], h, c);
+            realign_lane(xl[it], 34, r.xa[it], r.xb[it], r.xs[it], h, c);
             store16(dst.x(bb, 0, cc), c[0], c[1], c[2], c[3]);
             store16(dst.x(bb, 1, cc), c[4], c[5], c[6], c[7]);
             const float dx = f16_bits_to_f32(h);
@@ -364,25 +438,36 @@ __global__ __launch_bounds__(kThreads + kLoadThreads) void gemm_kernel(const uin
         const Stage& cur = st[s & 1];
         const int nbs = min(kKB, nb - s * kKB);
         if (nbs == kKB) {
-          // full stage: the MFMAs of block bb+1 are issued before the scale
-          // epilogue of block bb, so the matrix core and the VALU overlap
+          // full stage: the MFMAs and scale reads of block bb+1 are issued
+          // before the epilogue of block bb, so the matrix core, the LDS and
+          // the VALU overlap
           i32x16 d[2][kNT];
+          Scales<kNT> sc[2];
 #pragma unroll
           for (int t = 0; t < kNT; ++t) mfma_block(cur, 0, wm, wn0 + t, l32, half, cmagic, d[0][t]);
+          load_scales(cur, 0, wm, wn0, l32, half, sc[0]);
 #pragma unroll
           for (int bb = 0; bb < kKB; ++bb) {
-            if (bb + 1 < kKB)
+            if (bb + 1 < kKB) {
 #pragma unroll
               for (int t = 0; t < kNT; ++t)
                 mfma_block(cur, bb + 1, wm, wn0 + t, l32, half, cmagic, d[(bb + 1) & 1][t]);
-            epilogue<FMT, kNT>(cur, bb, wm, wn0, l32, half, d[bb & 1], acc);
+              load_scales(cur, bb + 1, wm, wn0, l32, half, sc[(bb + 1) & 1]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            apply_scales(sc[bb & 1], d[bb & 1], acc);
+            if (FMT == kFmtQ4_K && (bb & 1)) min_term(cur, bb - 1, kKB, wm, wn0, l32, half, acc);
           }
         } else {
           for (int bb = 0; bb < nbs; ++bb) {
             i32x16 d[kNT];
+            Scales<kNT> sc;
 #pragma unroll
             for (int t = 0; t < kNT; ++t) mfma_block(cur, bb, wm, wn0 + t, l32, half, cmagic, d[t]);
-            epilogue<FMT, kNT>(cur, bb, wm, wn0, l32, half, d, acc);
+            load_scales(cur, bb, wm, wn0, l32, half, sc);
+            apply_scales(sc, d, acc);
+            if (FMT == kFmtQ4_K && ((bb & 1) || bb + 1 == nbs))
+              min_term(cur, bb & ~1, nbs, wm, wn0, l32, half, acc);
           }
         }
         __syncthreads();

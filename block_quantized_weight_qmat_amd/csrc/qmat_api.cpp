@@ -12,6 +12,9 @@
 namespace {
 
 constexpr int64_t kMaxDim = 0x7FFFFFFFLL;
+// The GEMM addresses a 128-row tile of W (and a 64-row tile of X_q8) with
+// 32-bit byte offsets: 129 Q8_0 rows of K = 2^24 take 2.3e9 bytes.
+constexpr int64_t kMaxGemmK = 1LL << 24;
 
 bool fmt_ok(int fmt) { return fmt == QMAT_Q4_0 || fmt == QMAT_Q8_0 || fmt == QMAT_Q4_K; }
 
@@ -110,6 +113,7 @@ int qmat_gemm(int fmt, const void* blocks, const void* X_q8, float* Y, int64_t M
   int rc = check_shape(fmt, M, K);
   if (rc != QMAT_OK) return rc;
   if ((rc = check_shape(QMAT_Q8_0, N, K)) != QMAT_OK) return rc;
+  if (K > kMaxGemmK) return QMAT_E_SHAPE;
   if (M == 0 || N == 0) return QMAT_OK;  // nothing to read or write
   if ((rc = check_buf(blocks, K > 0)) != QMAT_OK) return rc;
   if ((rc = check_buf(X_q8, K > 0)) != QMAT_OK) return rc;

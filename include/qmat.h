@@ -138,7 +138,7 @@ int qmat_quantize(int fmt, const float *W, void *blocks, int64_t rows,
  *   Accuracy: relative L2 error against the exact (fp64) product of the
  *   dequantized weights with x is below 1e-3 for finite x; internally each
  *   32-element slice of x is scaled by a power of two and rounded to a
- *   16-bit integer (|X| <= 32639, relative step <= 2^-14 of the slice's
+ *   20-bit integer (|X| < 2^19, relative step <= 2^-17.9 of the slice's
  *   largest element), the integer dot products with the codes are exact,
  *   and the per-block results are accumulated in fp32.
  */
@@ -155,9 +155,12 @@ int qmat_gemv(int fmt, const void *blocks, const float *x, float *y,
  *   X_q8: Q8_0 blocks of the activations, N rows of K, exactly as
  *         qmat_quantize(QMAT_Q8_0, X, X_q8, N, K, stream) writes them.
  *   Y: fp32 [N][M] (token-major), overwritten.
+ *   K is at most 2^24 here (QMAT_E_SHAPE above that): the kernel addresses
+ *   a 128-row tile with 32-bit byte offsets.
  *   Accuracy: relative L2 error against the exact (fp64) product of the
  *   dequantized operands is below 2e-3; the per-block integer dot products
- *   are exact.
+ *   are exact. Q4_K's min term (dmin*mn_j times the block sums of X_q8) is
+ *   accumulated in fp32.
  */
 int qmat_gemm(int fmt, const void *blocks, const void *X_q8, float *Y,
               int64_t M, int64_t K, int64_t N, void *stream);

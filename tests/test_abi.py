@@ -86,6 +86,7 @@ def test_bad_shapes(lib):
     assert lib.qmat_gemv(0, A, A, A, 1, 2 ** 31 + 32, None) == E_SHAPE
     assert lib.qmat_gemm(0, A, A, A, 1, 32, -1, None) == E_SHAPE
     assert lib.qmat_gemm(2, A, A, A, 1, 32, 1, None) == E_SHAPE    # Q4_K needs K % 256
+    assert lib.qmat_gemm(0, A, A, A, 1, 2 ** 24 + 32, 1, None) == E_SHAPE  # GEMM K limit
 
 
 def test_null_and_alignment(lib):
