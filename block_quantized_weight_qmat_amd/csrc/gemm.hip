@@ -43,16 +43,24 @@ namespace {
 #ifndef QMAT_GEMM_DEPTH
 #define QMAT_GEMM_DEPTH 1
 #endif
-constexpr int kBM = 128;
-constexpr int kBN = 64;
+#ifndef QMAT_GEMM_BM
+#define QMAT_GEMM_BM 128
+#define QMAT_GEMM_BN 64
+#endif
+constexpr int kBM = QMAT_GEMM_BM;  // tile rows (weights)
+constexpr int kBN = QMAT_GEMM_BN;  // tile columns (tokens)
+constexpr int kRT = kBM / 32, kCT = kBN / 32;  // 32 x 32 MFMA tiles per tile
 constexpr int kKB = 8;  // K-blocks per stage
 #ifndef QMAT_GEMM_NT
 #define QMAT_GEMM_NT 2
 #endif
-// each compute wave owns 32 rows x (32 * kNT) columns of the 128 x 64 tile
+// each compute wave owns 32 rows x (32 * kNT) columns of the tile
 constexpr int kNT = QMAT_GEMM_NT;  // 32-column MFMA tiles per compute wave
-constexpr int kThreads = 512 / kNT;  // compute threads
-constexpr int kLoadThreads = 256; // loader threads (4 waves)
+constexpr int kThreads = kWave * kRT * kCT / kNT;  // compute threads
+#ifndef QMAT_GEMM_LOADERS
+#define QMAT_GEMM_LOADERS 4
+#endif
+constexpr int kLoadThreads = kWave * QMAT_GEMM_LOADERS;  // loader threads
 constexpr int kDepth = QMAT_GEMM_DEPTH;  // stages a loader thread holds in registers
 constexpr uint32_t kMagicI = 0x4B400000u;  // 1.5 * 2^23 as fp32 bits
 constexpr float kMagicF = 12582912.0f;
@@ -252,8 +260,10 @@ __global__ __launch_bounds__(kThreads + kLoadThreads) void gemm_kernel(const uin
                                                             int64_t ntiles) {
   __shared__ __attribute__((aligned(16))) Stage st[2];
   typedef StageRegs<FMT> R;
-  const bool loader = threadIdx.x >= kThreads;
-  const int tid = loader ? threadIdx.x - kThreads : threadIdx.x;  // index within its group
+  // role per wave, in a scalar register so that the branch is uniform
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const bool loader = wave >= kThreads / kWave;
+  const int tid = (int)threadIdx.x - (loader ? kThreads : 0);  // index within its group
   const int lane = tid & 63;
   const int wv = tid >> 6;
   const int half = lane >> 5;
@@ -271,11 +281,13 @@ __global__ __launch_bounds__(kThreads + kLoadThreads) void gemm_kernel(const uin
     lin = (int64_t)(blockIdx.x & 7) * per + (blockIdx.x >> 3);
   }
 
-  for (int64_t tile = lin; tile < ntiles; tile += gridDim.x) {
-    const int64_t tm = tile / tiles_n, tn = tile - tm * tiles_n;
-    const int64_t m0 = tm * kBM, n0 = tn * kBN;
-
-    if (loader) {
+  // Each role runs its own tile loop (so that neither keeps the other's
+  // tile-invariant values live); both pass the same barriers per tile: one
+  // before the first stage, one per stage and one after the last.
+  if (loader) {
+    for (int64_t tile = lin; tile < ntiles; tile += gridDim.x) {
+      const int64_t tm = tile / tiles_n, tn = tile - tm * tiles_n;
+      const int64_t m0 = tm * kBM, n0 = tn * kBN;
       // item -> (row, block): 8 consecutive threads cover one row's 8
       // blocks of a stage. A stage is the same 8 blocks of every row, so an
       // item keeps its byte offsets from the stage's (wave-uniform) base,
@@ -422,11 +434,17 @@ __global__ __launch_bounds__(kThreads + kLoadThreads) void gemm_kernel(const uin
 #pragma unroll
       for (int k = 0; k + 1 < kDepth; ++k)
         if (s + k < nstage) step(s + k, regs[(k + 1) % kDepth]);
-    } else {
+      // the next tile reuses both LDS stages
+      __syncthreads();
+    }
+  } else {
+    for (int64_t tile = lin; tile < ntiles; tile += gridDim.x) {
+      const int64_t tm = tile / tiles_n, tn = tile - tm * tiles_n;
+      const int64_t m0 = tm * kBM, n0 = tn * kBN;
       i32x16 cmagic;
 #pragma unroll
       for (int i = 0; i < 16; ++i) cmagic[i] = (int)kMagicI;
-      const int wm = wv & 3, wn0 = (wv >> 2) * kNT;  // rows 32wm.., column tiles wn0..
+      const int wm = wv % kRT, wn0 = (wv / kRT) * kNT;  // rows 32wm.., column tiles wn0..
       float acc[kNT][16];
 #pragma unroll
       for (int t = 0; t < kNT; ++t)
@@ -493,9 +511,8 @@ __global__ __launch_bounds__(kThreads + kLoadThreads) void gemm_kernel(const uin
           }
         }
       }
+      __syncthreads();
     }
-    // the next tile reuses both LDS stages
-    __syncthreads();
   }
 }
 
