@@ -182,6 +182,56 @@ __device__ __forceinline__ void mfma_block(const Stage& cur, int bb, int wm, int
   d = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, bv, cmagic, 0, 0, 0);
 }
 
+// MFMA operands of one K-block for a wave's NT tiles: its 32 weight rows
+// and the NT x 32 token columns (16 bytes per lane each).
+template <int NT>
+struct Ops {
+  i32x4 a;
+  i32x4 b[NT];
+};
+
+template <int NT>
+__device__ __forceinline__ void load_ops(const Stage& cur, int bb, int wm, int wn0, int l32,
+                                         int half, Ops<NT>& op) {
+  op.a = *reinterpret_cast<const i32x4*>(cur.w(bb, half, wm * 32 + l32));
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+    op.b[t] = *reinterpret_cast<const i32x4*>(cur.x(bb, half, (wn0 + t) * 32 + l32));
+}
+
+template <int NT>
+__device__ __forceinline__ void load_dw(const Stage& cur, int bb, int wm, int half,
+                                        float (&dw)[16]) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const f32x4 t = *reinterpret_cast<const f32x4*>(&cur.wd[bb][wm * 32 + 8 * q + 4 * half]);
+    dw[4 * q + 0] = t.x;
+    dw[4 * q + 1] = t.y;
+    dw[4 * q + 2] = t.z;
+    dw[4 * q + 3] = t.w;
+  }
+}
+
+// acc += dw * (S * dx): S * dx = fma(F, dx, c1) with c1 = -1.5 * 2^23 * dx
+// (see apply_scales); two passes of independent instructions.
+template <int NT>
+__device__ __forceinline__ void apply_block(const float (&dw)[16], const float (&dx)[NT],
+                                            const float (&c1)[NT], const i32x16 (&d)[NT],
+                                            float (&acc)[NT][16]) {
+  f32x16 df[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    df[t] = __builtin_bit_cast(f32x16, d[t]);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) df[t][i] = fmaf(df[t][i], dx[t], c1[t]);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[t][i] = fmaf(df[t][i], dw[i], acc[t][i]);
+}
+
 // Per-block scales a lane needs: dw of its 16 rows and dx of its column in
 // each of the NT tiles.
 template <int NT>
@@ -456,24 +506,43 @@ __global__ __launch_bounds__(kThreads + kLoadThreads) void gemm_kernel(const uin
         const Stage& cur = st[s & 1];
         const int nbs = min(kKB, nb - s * kKB);
         if (nbs == kKB) {
-          // full stage: the MFMAs and scale reads of block bb+1 are issued
-          // before the epilogue of block bb, so the matrix core, the LDS and
-          // the VALU overlap
-          i32x16 d[2][kNT];
-          Scales<kNT> sc[2];
+          // Full stage, software-pipelined: the column scales of all 8
+          // blocks are read up front; in step bb the MFMAs of block bb+1 are
+          // issued (operands read one step earlier), the operands of block
+          // bb+2 and the row scales of block bb+1 are requested, and block bb
+          // is scaled into the accumulators, so that the LDS, the matrix
+          // core and the VALU overlap.
+          float dxs[kKB][kNT], c1s[kKB][kNT];
 #pragma unroll
-          for (int t = 0; t < kNT; ++t) mfma_block(cur, 0, wm, wn0 + t, l32, half, cmagic, d[0][t]);
-          load_scales(cur, 0, wm, wn0, l32, half, sc[0]);
+          for (int bb = 0; bb < kKB; ++bb)
+#pragma unroll
+            for (int t = 0; t < kNT; ++t) dxs[bb][t] = cur.xd[bb][(wn0 + t) * 32 + l32];
+          Ops<kNT> op[2];
+          float dw[2][16];
+          i32x16 d[2][kNT];
+          load_ops(cur, 0, wm, wn0, l32, half, op[0]);
+          load_ops(cur, 1, wm, wn0, l32, half, op[1]);
+          load_dw<kNT>(cur, 0, wm, half, dw[0]);
+#pragma unroll
+          for (int bb = 0; bb < kKB; ++bb)
+#pragma unroll
+            for (int t = 0; t < kNT; ++t) c1s[bb][t] = -kMagicF * dxs[bb][t];
+#pragma unroll
+          for (int t = 0; t < kNT; ++t)
+            d[0][t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(op[0].a, op[0].b[t], cmagic, 0, 0, 0);
 #pragma unroll
           for (int bb = 0; bb < kKB; ++bb) {
+            __builtin_amdgcn_sched_barrier(0);
             if (bb + 1 < kKB) {
 #pragma unroll
               for (int t = 0; t < kNT; ++t)
-                mfma_block(cur, bb + 1, wm, wn0 + t, l32, half, cmagic, d[(bb + 1) & 1][t]);
-              load_scales(cur, bb + 1, wm, wn0, l32, half, sc[(bb + 1) & 1]);
+                d[(bb + 1) & 1][t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
+                    op[(bb + 1) & 1].a, op[(bb + 1) & 1].b[t], cmagic, 0, 0, 0);
             }
+            if (bb + 2 < kKB) load_ops(cur, bb + 2, wm, wn0, l32, half, op[bb & 1]);
+            if (bb + 1 < kKB) load_dw<kNT>(cur, bb + 1, wm, half, dw[(bb + 1) & 1]);
             __builtin_amdgcn_sched_barrier(0);
-            apply_scales(sc[bb & 1], d[bb & 1], acc);
+            apply_block(dw[bb & 1], dxs[bb], c1s[bb], d[bb & 1], acc);
             if (FMT == kFmtQ4_K && (bb & 1)) min_term(cur, bb - 1, kKB, wm, wn0, l32, half, acc);
           }
         } else {
