@@ -12,10 +12,8 @@
 // from zero (roundf), and fp16 rounding to nearest even by v_cvt_f16_f32, so
 // the bytes are identical to any other implementation of the same rules.
 //
-// Work split: 8 lanes own one 32-element block (4 consecutive floats each,
-// one 16-byte load per lane, so a wave reads 1 KiB contiguously). The packed
-// blocks of a workgroup are assembled in LDS and written out as 16-byte
-// stores. Q4_K uses one wave per 256-element superblock.
+// Work split: one lane per 32-element block (Q4_K-style: per sub-block), so
+// the per-block steps run once; a wave's 64 blocks are staged through LDS.
 #include "qmat_device.hpp"
 #include "qmat_launch.hpp"
 
@@ -23,134 +21,213 @@ namespace qmat {
 namespace {
 
 constexpr int kQThreads = 256;
-constexpr int kBlocksPerWG = kQThreads / 8;  // 32 blocks of 32 elements
 
 __device__ __forceinline__ float clampf(float v, float lo, float hi) {
   return fminf(fmaxf(v, lo), hi);
 }
 
-// Copy `nbytes` (even) of LDS staging to global memory starting at a
-// 16-byte aligned address: 16-byte stores, then 2-byte stores for the tail.
-__device__ __forceinline__ void copy_out(const uint8_t* lds, uint8_t* dst, int nbytes) {
-  const int n16 = nbytes >> 4;
-  for (int i = threadIdx.x; i < n16; i += blockDim.x)
-    reinterpret_cast<u32x4*>(dst)[i] = reinterpret_cast<const u32x4*>(lds)[i];
-  const int tail = nbytes - (n16 << 4);
-  for (int i = threadIdx.x; i < (tail >> 1); i += blockDim.x) {
-    const int o = (n16 << 4) + 2 * i;
-    *reinterpret_cast<uint16_t*>(dst + o) = *reinterpret_cast<const uint16_t*>(lds + o);
+// Staging of 64 consecutive 32-element blocks (8 KB) of one wave, copied
+// from memory straight into LDS (1 KB per instruction, 16 bytes per lane).
+// Part k (elements 4k..4k+3) of block b sits in column (k + b / 2) mod 8 of
+// row b, so the 16 lanes of an LDS access phase hit 16 different 16-byte bank
+// groups when lane b reads its block back.
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+__device__ __forceinline__ void stage_blocks(const float* __restrict__ src, int nblk, float* lds,
+                                             int lane) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int b = 8 * i + (lane >> 3);  // block filled by this lane's slot
+    const int k = ((lane & 7) - (b >> 1)) & 7;
+    if (8 * i < nblk && b < nblk)
+      __builtin_amdgcn_global_load_lds(src + 32 * b + 4 * k, (lds_ptr_t)(lds + 256 * i), 16, 0,
+                                       0);
+  }
+  // the compiler does not track direct-to-LDS loads: wait for all of them
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), other counters free
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+__device__ __forceinline__ void read_block(const float* lds, int lane, bool valid,
+                                           float (&v)[32]) {
+  const float* row = lds + 32 * lane;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const f32x4 t = *reinterpret_cast<const f32x4*>(row + 4 * ((k + (lane >> 1)) & 7));
+    v[4 * k + 0] = valid ? t.x : 0.0f;
+    v[4 * k + 1] = valid ? t.y : 0.0f;
+    v[4 * k + 2] = valid ? t.z : 0.0f;
+    v[4 * k + 3] = valid ? t.w : 0.0f;
   }
 }
 
-// Q4_0 (kQ4 = true) or Q8_0 (false): one 32-element block per 8 lanes.
+// a / b correctly rounded, for a divisor shared by many quotients: with
+// y = 1/b correctly rounded (one IEEE division per block), q0 = a * y and
+// the residual a - q0 * b exact in one fma, q0 + residual * y rounded once
+// is the correctly rounded quotient whenever it can round to a code. Checked
+// against IEEE division on the CPU for every fp16 divisor range, quotients
+// within +-130 (half-integer neighbourhoods included) and random operands:
+// only subnormal numerators differ, and those round to code 0 either way.
+__device__ __forceinline__ float div_shared(float a, float b, float y) {
+  const float q0 = a * y;
+  return fmaf(fmaf(-q0, b, a), y, q0);
+}
+
+// Q4_0 (kQ4 = true) or Q8_0 (false): one lane per 32-element block, 64
+// blocks per wave. The packed blocks of a wave are assembled in LDS and
+// written out with 16-byte stores.
 template <bool kQ4>
 __global__ __launch_bounds__(kQThreads) void quantize_b32_kernel(
     const float* __restrict__ W, uint8_t* __restrict__ out, int64_t nblocks) {
   constexpr int kBB = kQ4 ? 18 : 34;
   constexpr float kQmax = kQ4 ? 7.0f : 127.0f;
-  __shared__ __attribute__((aligned(16))) uint8_t stage[kBlocksPerWG * kBB];
-  uint16_t* stage16 = reinterpret_cast<uint16_t*>(stage);
+  constexpr int kWaves = kQThreads / kWave;
+  __shared__ __attribute__((aligned(16))) float xs[kWaves][kWave * 32];
+  __shared__ __attribute__((aligned(16))) uint8_t ob[kWaves][kWave * kBB];
 
-  const int tid = threadIdx.x;
-  const int lb = tid >> 3;  // block within the workgroup
-  const int j = tid & 7;    // this lane holds elements 4j..4j+3
-  const int64_t nchunks = (nblocks + kBlocksPerWG - 1) / kBlocksPerWG;
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  constexpr int kPerWG = kWaves * kWave;
+  const int64_t nchunks = (nblocks + kPerWG - 1) / kPerWG;
 
   for (int64_t chunk = blockIdx.x; chunk < nchunks; chunk += gridDim.x) {
-    const int64_t g = chunk * kBlocksPerWG + lb;
-    const bool valid = g < nblocks;
-    f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
-    if (valid) v = *reinterpret_cast<const f32x4*>(W + g * 32 + 4 * j);
+    const int64_t g0 = chunk * kPerWG + (int64_t)wv * kWave;  // first block of this wave
+    const int64_t left = nblocks - g0;
+    const int nblk = left <= 0 ? 0 : (left < kWave ? (int)left : kWave);
+    stage_blocks(W + g0 * 32, nblk, xs[wv], lane);
+    const bool valid = lane < nblk;
+    float v[32];
+    read_block(xs[wv], lane, valid, v);
 
-    // amax over the block (|x| >= +0, so max order does not matter)
-    float a = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-    a = fmaxf(a, shfl_xor_f(a, 1));
-    a = fmaxf(a, shfl_xor_f(a, 2));
-    a = fmaxf(a, shfl_xor_f(a, 4));
-
+    // amax over the block (|x| >= +0, so the max order does not matter)
+    float a = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) a = fmaxf(a, fabsf(v[e]));
     const float d = a / kQmax;
     const uint32_t h = f32_to_f16_bits(d);
     const float D = f16_bits_to_f32(h);
 
-    uint32_t packed = 0;
+    // codes q = clamp(round(x / D)); Q4_0 stores q + 8, element t in the low
+    // nibble of code byte t and element t + 16 in its high nibble
+    uint32_t w[kQ4 ? 4 : 8];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const float t = v[k];
-      int q = 0;
-      if (D != 0.0f) q = (int)clampf(roundf(t / D), kQ4 ? -8.0f : -127.0f, kQ4 ? 7.0f : 127.0f);
-      const uint32_t c = kQ4 ? (uint32_t)(q + 8) : ((uint32_t)q & 0xFFu);
-      packed |= c << (8 * k);
-    }
-
-    uint8_t* blk = stage + lb * kBB;
-    (void)blk;
-    if (kQ4) {
-      // byte t of the code area: element t (low nibble) | element t+16 (high)
-      const uint32_t partner = shfl_xor_u(packed, 4);
-      if (j < 4) {
-        const uint32_t w = packed | (partner << 4);
-        stage16[(lb * kBB) / 2 + 1 + 2 * j] = (uint16_t)(w & 0xFFFFu);
-        stage16[(lb * kBB) / 2 + 2 + 2 * j] = (uint16_t)(w >> 16);
+    for (int i = 0; i < (kQ4 ? 4 : 8); ++i) w[i] = kQ4 ? 0x88888888u : 0u;
+    if (D != 0.0f) {
+      const float y = 1.0f / D;
+#pragma unroll
+      for (int i = 0; i < (kQ4 ? 4 : 8); ++i) w[i] = 0u;
+#pragma unroll
+      for (int e = 0; e < 32; ++e) {
+        const int q =
+            (int)clampf(roundf(div_shared(v[e], D, y)), kQ4 ? -8.0f : -127.0f, kQ4 ? 7.0f : 127.0f);
+        if (kQ4)
+          w[(e & 15) >> 2] |= (uint32_t)(q + 8) << (8 * (e & 3) + (e >= 16 ? 4 : 0));
+        else
+          w[e >> 2] |= ((uint32_t)q & 0xFFu) << (8 * (e & 3));
       }
-    } else {
-      stage16[(lb * kBB) / 2 + 1 + 2 * j] = (uint16_t)(packed & 0xFFFFu);
-      stage16[(lb * kBB) / 2 + 2 + 2 * j] = (uint16_t)(packed >> 16);
     }
-    if (j == 0) stage16[(lb * kBB) / 2] = (uint16_t)h;
-    __syncthreads();
 
-    const int64_t remaining = nblocks - chunk * kBlocksPerWG;
-    const int nb = remaining < kBlocksPerWG ? (int)remaining : kBlocksPerWG;
-    copy_out(stage, out + chunk * kBlocksPerWG * kBB, nb * kBB);
-    __syncthreads();
+    // the block at byte 18 * lane (34 * lane) of the wave's output: written
+    // as 4-byte words where aligned, 2-byte pieces at the ends
+    uint8_t* o = ob[wv] + kBB * lane;
+    if (((kBB * lane) & 2) == 0) {
+      // scale and the first two code bytes share a word
+      reinterpret_cast<uint32_t*>(o)[0] = h | (w[0] << 16);
+#pragma unroll
+      for (int i = 1; i < (kQ4 ? 4 : 8); ++i)
+        reinterpret_cast<uint32_t*>(o)[i] = __builtin_amdgcn_alignbyte(w[i], w[i - 1], 2);
+      reinterpret_cast<uint16_t*>(o)[(kBB - 2) / 2] = (uint16_t)(w[(kQ4 ? 4 : 8) - 1] >> 16);
+    } else {
+      reinterpret_cast<uint16_t*>(o)[0] = (uint16_t)h;
+#pragma unroll
+      for (int i = 0; i < (kQ4 ? 4 : 8); ++i) reinterpret_cast<uint32_t*>(o + 2)[i] = w[i];
+    }
+    // the wave's blocks are contiguous in memory and start 16-byte aligned
+    // (64 * 18 and 64 * 34 are multiples of 16)
+    const int nbytes = nblk * kBB;
+    uint8_t* dst = out + g0 * kBB;
+    for (int i = lane; i < (nbytes >> 4); i += kWave)
+      reinterpret_cast<u32x4*>(dst)[i] = reinterpret_cast<const u32x4*>(ob[wv])[i];
+    const int t0 = nbytes & ~15;
+    for (int i = t0 + 2 * lane; i < nbytes; i += 2 * kWave)
+      *reinterpret_cast<uint16_t*>(dst + i) = *reinterpret_cast<const uint16_t*>(ob[wv] + i);
   }
 }
 
-// Q4_K-style: one wave per 256-element superblock, 4 superblocks per
-// workgroup. Lane l holds elements 4l..4l+3; sub-block j = lanes 8j..8j+7.
+// Q4_K-style: one lane per 32-element sub-block, so a wave quantizes 8
+// superblocks and the per-sub-block work (range, scale, 6-bit codes) is done
+// once. A wave copies its 8 superblocks (8 KB) from memory straight into its
+// own LDS area (1 KB per instruction, 16 bytes per lane), then each lane reads
+// its sub-block back. Part k (elements 4k..4k+3) of sub-block b sits in
+// column (k + b / 2) mod 8 of row b, so the 16 lanes of an LDS access phase
+// hit 16 different 16-byte bank groups.
+constexpr int kQkWaves = kQThreads / kWave;
+constexpr int kQkSuperPerWave = 8;
+
+// max / or over the 8 lanes of a superblock (xor 1, 2, 4 within 32 lanes)
+template <int kXor>
+__device__ __forceinline__ uint32_t swz_xor(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x1F | (kXor << 10));
+}
+
+__device__ __forceinline__ float max8_from0(float v) {
+  // the superblock maxima start from +0 and only see values >= +0
+  float o = __builtin_bit_cast(float, swz_xor<1>(__builtin_bit_cast(uint32_t, v)));
+  v = o > v ? o : v;
+  o = __builtin_bit_cast(float, swz_xor<2>(__builtin_bit_cast(uint32_t, v)));
+  v = o > v ? o : v;
+  o = __builtin_bit_cast(float, swz_xor<4>(__builtin_bit_cast(uint32_t, v)));
+  return o > v ? o : v;
+}
+
+__device__ __forceinline__ uint32_t or8(uint32_t v) {
+  v |= swz_xor<1>(v);
+  v |= swz_xor<2>(v);
+  return v | swz_xor<4>(v);
+}
+
 __global__ __launch_bounds__(kQThreads) void quantize_q4k_kernel(
     const float* __restrict__ W, uint8_t* __restrict__ out, int64_t nsuper) {
   constexpr int kSB = 144;
-  constexpr int kSuperPerWG = kQThreads / kWave;
-  __shared__ __attribute__((aligned(16))) uint8_t stage[kSuperPerWG * kSB];
-  uint32_t* stage32 = reinterpret_cast<uint32_t*>(stage);
+  __shared__ __attribute__((aligned(16))) float xs[kQkWaves][kQkSuperPerWave * 256];
 
-  const int tid = threadIdx.x;
-  const int wv = tid >> 6;
-  const int lane = tid & 63;
-  const int sub = lane >> 3;  // sub-block
-  const int jl = lane & 7;
-  const int64_t nchunks = (nsuper + kSuperPerWG - 1) / kSuperPerWG;
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int sub = lane & 7;  // sub-block within the superblock
+  constexpr int kPerWG = kQkWaves * kQkSuperPerWave;
+  const int64_t nchunks = (nsuper + kPerWG - 1) / kPerWG;
+  float* mine = xs[wv];
 
   for (int64_t chunk = blockIdx.x; chunk < nchunks; chunk += gridDim.x) {
-    const int64_t s = chunk * kSuperPerWG + wv;
-    const bool valid = s < nsuper;
-    f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
-    if (valid) v = *reinterpret_cast<const f32x4*>(W + s * 256 + 4 * lane);
+    const int64_t s0 = chunk * kPerWG + (int64_t)wv * kQkSuperPerWave;
+    const int64_t left = nsuper - s0;
+    const int nsb = left <= 0 ? 0 : (left < kQkSuperPerWave ? (int)left : kQkSuperPerWave);
 
-    // 1. sub-block min and max (comparison order is irrelevant: the values
-    //    and the derived bytes do not depend on which zero sign wins)
-    float mn = fminf(fminf(v.x, v.y), fminf(v.z, v.w));
-    float mx = fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w));
+    // 8 superblocks = 64 sub-blocks, staged like 64 blocks
+    stage_blocks(W + s0 * 256, 8 * nsb, mine, lane);
+
+    const bool valid = (lane >> 3) < nsb;
+    float v[32];
+    read_block(mine, lane, valid, v);
+
+    // 1. sub-block min and max (the derived bytes do not depend on which
+    //    zero sign a comparison keeps)
+    float mn = v[0], mx = v[0];
 #pragma unroll
-    for (int m = 1; m < 8; m <<= 1) {
-      mn = fminf(mn, shfl_xor_f(mn, m));
-      mx = fmaxf(mx, shfl_xor_f(mx, m));
+    for (int e = 1; e < 32; ++e) {
+      mn = fminf(mn, v[e]);
+      mx = fmaxf(mx, v[e]);
     }
     const float lo = mn < 0.0f ? mn : 0.0f;
     const float hi = mx;
     // 2. sub-block scale and offset
     const float scale = (hi - lo) / 15.0f;
     const float off = -lo;
-    // 3. super-scale and super-min: max over sub-blocks, starting from +0
-    float smax = scale > 0.0f ? scale : 0.0f;
-    float omax = off > 0.0f ? off : 0.0f;
-#pragma unroll
-    for (int m = 8; m < 64; m <<= 1) {
-      const float so = shfl_xor_f(smax, m), oo = shfl_xor_f(omax, m);
-      smax = so > smax ? so : smax;
-      omax = oo > omax ? oo : omax;
-    }
+    // 3. super-scale and super-min: max over the superblock's sub-blocks,
+    //    starting from +0
+    const float smax = max8_from0(scale > 0.0f ? scale : 0.0f);
+    const float omax = max8_from0(off > 0.0f ? off : 0.0f);
     const float d = smax / 63.0f, dmin = omax / 63.0f;
     const uint32_t hd = f32_to_f16_bits(d), hm = f32_to_f16_bits(dmin);
     const float D = f16_bits_to_f32(hd), Dm = f16_bits_to_f32(hm);
@@ -160,51 +237,33 @@ __global__ __launch_bounds__(kQThreads) void quantize_q4k_kernel(
     // 5. exact effective scale and offset
     const float S = D * (float)sc;
     const float O = Dm * (float)mq;
-    // 6. 4-bit codes
-    uint32_t packed = 0;
+    // 6. 4-bit codes q = clamp(round((v + O) / S), 0, 15), the 32
+    //    quotients sharing the divisor (div_shared)
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+    if (S != 0.0f) {
+      const float y = 1.0f / S;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      int q = 0;
-      if (S != 0.0f) q = (int)clampf(roundf((v[k] + O) / S), 0.0f, 15.0f);
-      packed |= (uint32_t)q << (8 * k);
+      for (int e = 0; e < 32; ++e) {
+        const uint32_t c = (uint32_t)(int)clampf(roundf(div_shared(v[e] + O, S, y)), 0.0f, 15.0f);
+        // byte t of the code area: element t (low nibble) | t + 16 (high)
+        w[(e & 15) >> 2] |= c << (8 * (e & 3) + (e >= 16 ? 4 : 0));
+      }
     }
-    const uint32_t partner = shfl_xor_u(packed, 4);
-    uint8_t* blk = stage + wv * kSB;
-    if (jl < 4)
-      reinterpret_cast<uint32_t*>(blk + 16 + 16 * sub)[jl] = packed | (partner << 4);
-
-    // 96-bit field word: sc at bit 6*sub, min at bit 48 + 6*sub
-    uint32_t f0 = 0, f1 = 0, f2 = 0;
-    if (jl == 0) {
+    // 96-bit field word: sc at bit 6 * sub, min at bit 48 + 6 * sub
+    uint32_t fw[3] = {0u, 0u, 0u};
+    {
       const int ps = 6 * sub, pm = 48 + 6 * sub;
-      uint32_t fw[3] = {0, 0, 0};
       fw[ps >> 5] |= (uint32_t)sc << (ps & 31);
       if ((ps & 31) > 26) fw[(ps >> 5) + 1] |= (uint32_t)sc >> (32 - (ps & 31));
       fw[pm >> 5] |= (uint32_t)mq << (pm & 31);
-      if ((pm & 31) > 26) fw[(pm >> 5) + 1] |= (uint32_t)mq >> (32 - (pm & 31));
-      f0 = fw[0];
-      f1 = fw[1];
-      f2 = fw[2];
+      if ((pm & 31) > 26 && (pm >> 5) + 1 < 3) fw[(pm >> 5) + 1] |= (uint32_t)mq >> (32 - (pm & 31));
     }
-#pragma unroll
-    for (int m = 8; m < 64; m <<= 1) {
-      f0 |= shfl_xor_u(f0, m);
-      f1 |= shfl_xor_u(f1, m);
-      f2 |= shfl_xor_u(f2, m);
+    const uint32_t f0 = or8(fw[0]), f1 = or8(fw[1]), f2 = or8(fw[2]);
+    if (valid) {
+      uint8_t* blk = out + (s0 + (lane >> 3)) * kSB;
+      reinterpret_cast<u32x4*>(blk + 16 + 16 * sub)[0] = u32x4{w[0], w[1], w[2], w[3]};
+      if (sub == 0) reinterpret_cast<u32x4*>(blk)[0] = u32x4{hd | (hm << 16), f0, f1, f2};
     }
-    if (lane == 0) {
-      uint32_t* h32 = reinterpret_cast<uint32_t*>(blk);
-      h32[0] = hd | (hm << 16);
-      h32[1] = f0;
-      h32[2] = f1;
-      h32[3] = f2;
-    }
-    (void)stage32;
-    __syncthreads();
-    const int64_t remaining = nsuper - chunk * kSuperPerWG;
-    const int ns = remaining < kSuperPerWG ? (int)remaining : kSuperPerWG;
-    copy_out(stage, out + chunk * kSuperPerWG * kSB, ns * kSB);
-    __syncthreads();
   }
 }
 
@@ -219,13 +278,13 @@ hipError_t launch_quantize(int fmt, const float* W, void* blocks, int64_t rows, 
   uint8_t* out = static_cast<uint8_t*>(blocks);
   if (fmt == kFmtQ4_K) {
     const int64_t nsuper = rows * (K / 256);
-    const int64_t chunks = (nsuper + 3) / 4;
+    const int64_t chunks = (nsuper + kQkWaves * kQkSuperPerWave - 1) / (kQkWaves * kQkSuperPerWave);
     if (chunks == 0) return hipSuccess;
     hipLaunchKernelGGL(quantize_q4k_kernel, dim3((unsigned)grid_for(chunks)), dim3(kQThreads), 0,
                        stream, W, out, nsuper);
   } else {
     const int64_t nb = rows * (K / 32);
-    const int64_t chunks = (nb + kBlocksPerWG - 1) / kBlocksPerWG;
+    const int64_t chunks = (nb + kQThreads - 1) / kQThreads;  // one block per thread
     if (chunks == 0) return hipSuccess;
     if (fmt == kFmtQ4_0)
       hipLaunchKernelGGL(quantize_b32_kernel<true>, dim3((unsigned)grid_for(chunks)),
