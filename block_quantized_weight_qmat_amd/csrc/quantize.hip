@@ -66,9 +66,10 @@ __device__ __forceinline__ void read_block(const float* lds, int lane, bool vali
 // y = 1/b correctly rounded (one IEEE division per block), q0 = a * y and
 // the residual a - q0 * b exact in one fma, q0 + residual * y rounded once
 // is the correctly rounded quotient whenever it can round to a code. Checked
-// against IEEE division on the CPU for every fp16 divisor range, quotients
-// within +-130 (half-integer neighbourhoods included) and random operands:
-// only subnormal numerators differ, and those round to code 0 either way.
+// against IEEE division on the CPU (tests/shared_divisor_check.c) over the
+// fp16 divisor range, quotients within +-135 (half-integer neighbourhoods
+// included) and random operands: only subnormal numerators differ, and
+// those round to code 0 either way.
 __device__ __forceinline__ float div_shared(float a, float b, float y) {
   const float q0 = a * y;
   return fmaf(fmaf(-q0, b, a), y, q0);
