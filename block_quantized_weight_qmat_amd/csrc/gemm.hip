@@ -107,18 +107,6 @@ __device__ __forceinline__ void store16(int8_t* dst, uint32_t a, uint32_t b, uin
   *reinterpret_cast<u32x4*>(dst) = v;
 }
 
-// Global data of one stage held in registers between its load and its LDS
-// write: four W items (row, block) and two X items per thread.
-template <int FMT>
-struct StageRegs {
-  static constexpr int kWItems = kBM * kKB / kLoadThreads;  // 4
-  static constexpr int kXItems = kBN * kKB / kLoadThreads;  // 2
-  u32x4 wa[kWItems], wb[kWItems];  // Q8_0: 2 x 16 B; Q4_0: 16 B; Q4_K: header, codes
-  uint32_t ws[kWItems];            // 2-byte piece (Q4_0/Q8_0)
-  u32x4 xa[kXItems], xb[kXItems];
-  uint32_t xs[kXItems];
-};
-
 // One loader item's fixed offsets from the stage base: an 18- or 34-byte
 // block at byte offset o starts at 0 or 2 mod 4. If 0, the 16-byte load(s)
 // at o hold the scale and the first code bytes and the 2-byte load at
@@ -302,14 +290,252 @@ __device__ __forceinline__ void min_term(const Stage& cur, int b0, int nbs, int 
   }
 }
 
+// Loader side of a tile: kLT threads move the 128 x 8 W items and 64 x 8
+// X items (row, block) of each stage from memory into registers and then,
+// unpacked, into an LDS stage. 8 consecutive threads cover one row's 8
+// blocks of a stage. A stage is the same 8 blocks of every row, so an item
+// keeps its byte offsets from the stage's (wave-uniform) base, and its
+// alignment case, for the whole tile. Rows past M (N) re-read the last row.
+template <int FMT, int kLT>
+struct TileLoader {
+  static constexpr int kWItems = kBM * kKB / kLT;
+  static constexpr int kXItems = kBN * kKB / kLT;
+  static constexpr int wbytes = FMT == kFmtQ4_0 ? 18 : FMT == kFmtQ8_0 ? 34 : 144;
+  static constexpr int stage_wbytes = FMT == kFmtQ4_K ? 144 : kKB * wbytes;
+  struct Regs {
+    u32x4 wa[kWItems], wb[kWItems];  // Q8_0: 2 x 16 B; Q4_0: 16 B; Q4_K: header, codes
+    uint32_t ws[kWItems];            // 2-byte piece (Q4_0/Q8_0)
+    u32x4 xa[kXItems], xb[kXItems];
+    uint32_t xs[kXItems];
+  };
+  BlkLane wl[kWItems], xl[kXItems];
+  int tid, nb;
+
+  __device__ __forceinline__ void setup(int64_t M, int64_t N, int64_t m0, int64_t n0,
+                                        int64_t wrb, int64_t xrb, int tid_, int nb_) {
+    tid = tid_;
+    nb = nb_;
+    const uint32_t wlast = (uint32_t)min<int64_t>(kBM - 1, M - 1 - m0);
+    const uint32_t xlast = (uint32_t)min<int64_t>(kBN - 1, N - 1 - n0);
+    // tile bases mod 4 (the buffers are 16-byte aligned, stage strides are
+    // multiples of 4)
+    const uint32_t wpar = (uint32_t)(m0 * wrb) & 3u, xpar = (uint32_t)(n0 * xrb) & 3u;
+#pragma unroll
+    for (int it = 0; it < kWItems; ++it) {
+      const int item = tid + it * kLT;
+      const uint32_t ro = min((uint32_t)(item >> 3), wlast) * (uint32_t)wrb;
+      if (FMT == kFmtQ4_K) {
+        wl[it].o16 = ro;                                    // superblock header
+        wl[it].o2 = ro + 16u + 16u * (uint32_t)(item & 7);  // sub-block codes
+        wl[it].sel = 0u;
+        wl[it].hsel = 0u;
+      } else {
+        wl[it] = blk_lane(ro + (uint32_t)(item & 7) * (uint32_t)wbytes, wpar, wbytes);
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < kXItems; ++it) {
+      const int item = tid + it * kLT;
+      const uint32_t ro = min((uint32_t)(item >> 3), xlast) * (uint32_t)xrb;
+      xl[it] = blk_lane(ro + (uint32_t)(item & 7) * 34u, xpar, 34);
+    }
+  }
+
+  // global -> registers for stage s (blocks past nb are not loaded); wrs and
+  // xrs cover the W and X bytes from the tile's first rows to the end
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t wrs, __amdgpu_buffer_rsrc_t xrs,
+                                       int s, Regs& r) const {
+    const uint32_t wso = (uint32_t)s * (uint32_t)stage_wbytes;
+    const uint32_t xso = (uint32_t)s * (uint32_t)(kKB * 34);
+    const int left = nb - s * kKB;  // blocks of this stage that exist
+#pragma unroll
+    for (int it = 0; it < kWItems; ++it) {
+      if (((tid + it * kLT) & 7) < left) {
+        if (FMT == kFmtQ4_K) {
+          r.wa[it] = __builtin_amdgcn_raw_buffer_load_b128(wrs, wl[it].o16, wso, 0);
+          r.wb[it] = __builtin_amdgcn_raw_buffer_load_b128(wrs, wl[it].o2, wso, 0);
+        } else {
+          load_lane(wrs, wso, wl[it], wbytes, r.wa[it], r.wb[it], r.ws[it]);
+        }
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < kXItems; ++it)
+      if (((tid + it * kLT) & 7) < left) load_lane(xrs, xso, xl[it], 34, r.xa[it], r.xb[it], r.xs[it]);
+  }
+
+  // registers -> LDS buffer for stage s
+  __device__ __forceinline__ void write(int s, const Regs& r, Stage& dst) const {
+    const int left = nb - s * kKB;
+#pragma unroll
+    for (int it = 0; it < kWItems; ++it) {
+      const int item = tid + it * kLT;
+      const int rr = item >> 3, bb = item & 7;
+      if (bb < left) {
+        if (FMT == kFmtQ4_0) {
+          uint32_t h, c[8];
+          realign_lane(wl[it], 18, r.wa[it], r.wb[it], r.ws[it], h, c);
+          store16(dst.w(bb, 0, rr), nib_signed(c[0], 0), nib_signed(c[1], 0),
+                  nib_signed(c[2], 0), nib_signed(c[3], 0));
+          store16(dst.w(bb, 1, rr), nib_signed(c[0], 4), nib_signed(c[1], 4),
+                  nib_signed(c[2], 4), nib_signed(c[3], 4));
+          dst.wd[bb][rr] = f16_bits_to_f32(h);
+        } else if (FMT == kFmtQ8_0) {
+          uint32_t h, c[8];
+          realign_lane(wl[it], 34, r.wa[it], r.wb[it], r.ws[it], h, c);
+          store16(dst.w(bb, 0, rr), c[0], c[1], c[2], c[3]);
+          store16(dst.w(bb, 1, rr), c[4], c[5], c[6], c[7]);
+          dst.wd[bb][rr] = f16_bits_to_f32(h);
+        } else {
+          const u32x4 hd = r.wa[it], cv = r.wb[it];
+          const int sub = bb;  // a stage is one superblock
+          const int ps = 6 * sub, pm = 48 + 6 * sub;
+          const uint32_t slo = ps < 32 ? hd.y : hd.z, shi = ps < 32 ? hd.z : hd.w;
+          const uint32_t mlo = pm < 64 ? hd.z : hd.w, mhi = pm < 64 ? hd.w : 0u;
+          const uint32_t sc = __builtin_amdgcn_alignbit(shi, slo, ps & 31) & 63u;
+          const uint32_t mn = __builtin_amdgcn_alignbit(mhi, mlo, pm & 31) & 63u;
+          store16(dst.w(bb, 0, rr), nib_unsigned(cv.x, 0), nib_unsigned(cv.y, 0),
+                  nib_unsigned(cv.z, 0), nib_unsigned(cv.w, 0));
+          store16(dst.w(bb, 1, rr), nib_unsigned(cv.x, 4), nib_unsigned(cv.y, 4),
+                  nib_unsigned(cv.z, 4), nib_unsigned(cv.w, 4));
+          dst.wd[bb][rr] = f16_bits_to_f32(hd.x) * (float)sc;
+          dst.wo[bb][rr] = -(f16_bits_to_f32(hd.x >> 16) * (float)mn);  // -O
+        }
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < kXItems; ++it) {
+      const int item = tid + it * kLT;
+      const int cc = item >> 3, bb = item & 7;
+      if (bb < left) {
+        uint32_t h, c[8];
+        realign_lane(xl[it], 34, r.xa[it], r.xb[it], r.xs[it], h, c);
+        store16(dst.x(bb, 0, cc), c[0], c[1], c[2], c[3]);
+        store16(dst.x(bb, 1, cc), c[4], c[5], c[6], c[7]);
+        const float dx = f16_bits_to_f32(h);
+        dst.xd[bb][cc] = dx;
+        if (FMT == kFmtQ4_K) {
+          int qs = 0;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) qs = __builtin_amdgcn_sdot4((int)c[i], 0x01010101, qs, false);
+          dst.xs[bb][cc] = dx * (float)qs;
+        }
+      }
+    }
+  }
+};
+
+// One K-stage of a wave's NT 32 x 32 tiles (rows 32 wm.., column tiles
+// wn0..) from LDS into the fp32 accumulators; nbs blocks of the stage exist.
+template <int FMT, int NT>
+__device__ __forceinline__ void compute_stage(const Stage& cur, int nbs, int wm, int wn0,
+                                              int l32, int half, const i32x16& cmagic,
+                                              float (&acc)[NT][16]) {
+  if (nbs == kKB) {
+    // Full stage, software-pipelined: the column scales of all 8 blocks are
+    // read up front; in step bb the MFMAs of block bb+1 are issued
+    // (operands read one step earlier), the operands of block bb+2 and the
+    // row scales of block bb+1 are requested, and block bb is scaled into
+    // the accumulators, so that the LDS, the matrix core and the VALU
+    // overlap.
+    float dxs[kKB][NT], c1s[kKB][NT];
+#pragma unroll
+    for (int bb = 0; bb < kKB; ++bb)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) dxs[bb][t] = cur.xd[bb][(wn0 + t) * 32 + l32];
+    Ops<NT> op[2];
+    float dw[2][16];
+    i32x16 d[2][NT];
+    load_ops(cur, 0, wm, wn0, l32, half, op[0]);
+    load_ops(cur, 1, wm, wn0, l32, half, op[1]);
+    load_dw<NT>(cur, 0, wm, half, dw[0]);
+#pragma unroll
+    for (int bb = 0; bb < kKB; ++bb)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) c1s[bb][t] = -kMagicF * dxs[bb][t];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+      d[0][t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(op[0].a, op[0].b[t], cmagic, 0, 0, 0);
+#pragma unroll
+    for (int bb = 0; bb < kKB; ++bb) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (bb + 1 < kKB) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+          d[(bb + 1) & 1][t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
+              op[(bb + 1) & 1].a, op[(bb + 1) & 1].b[t], cmagic, 0, 0, 0);
+      }
+      if (bb + 2 < kKB) load_ops(cur, bb + 2, wm, wn0, l32, half, op[bb & 1]);
+      if (bb + 1 < kKB) load_dw<NT>(cur, bb + 1, wm, half, dw[(bb + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+      apply_block(dw[bb & 1], dxs[bb], c1s[bb], d[bb & 1], acc);
+      if (FMT == kFmtQ4_K && (bb & 1)) min_term(cur, bb - 1, kKB, wm, wn0, l32, half, acc);
+    }
+  } else {
+    for (int bb = 0; bb < nbs; ++bb) {
+      i32x16 d[NT];
+      Scales<NT> sc;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) mfma_block(cur, bb, wm, wn0 + t, l32, half, cmagic, d[t]);
+      load_scales(cur, bb, wm, wn0, l32, half, sc);
+      apply_scales(sc, d, acc);
+      if (FMT == kFmtQ4_K && ((bb & 1) || bb + 1 == nbs))
+        min_term(cur, bb & ~1, nbs, wm, wn0, l32, half, acc);
+    }
+  }
+}
+
+// Store: lane holds column n = n0 + 32(wn0 + t) + l32, rows
+// m = m0 + 32 wm + 8q + 4 half + r (q, r in 0..3).
+template <int NT>
+__device__ __forceinline__ void store_tile(float* __restrict__ Y, int64_t M, int64_t N,
+                                           int64_t m0, int64_t n0, int wm, int wn0, int l32,
+                                           int half, const float (&acc)[NT][16]) {
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int64_t n = n0 + 32 * (wn0 + t) + l32;
+    if (n >= N) continue;
+    float* yrow = Y + n * M;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t mb = m0 + wm * 32 + 8 * q + 4 * half;
+      if (mb + 3 < M && (M & 3) == 0) {
+        f32x4 v = {acc[t][4 * q], acc[t][4 * q + 1], acc[t][4 * q + 2], acc[t][4 * q + 3]};
+        *reinterpret_cast<f32x4*>(yrow + mb) = v;
+      } else {
+#pragma unroll
+        for (int r2 = 0; r2 < 4; ++r2)
+          if (mb + r2 < M) yrow[mb + r2] = acc[t][4 * q + r2];
+      }
+    }
+  }
+}
+
+// XCD-aware order: XCD x = id % 8 takes linear tiles [x * per, (x+1) * per)
+__device__ __forceinline__ int64_t first_tile(int64_t ntiles) {
+  int64_t lin = blockIdx.x;
+  if ((ntiles & 7) == 0 && (int64_t)gridDim.x == ntiles) {
+    const int64_t per = ntiles >> 3;
+    lin = (int64_t)(blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  }
+  return lin;
+}
+
+__device__ __forceinline__ i32x16 magic_vec() {
+  i32x16 c;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) c[i] = (int)kMagicI;
+  return c;
+}
+
+// Warp-specialized kernel: kLoadThreads loader threads fill the LDS stages,
+// kThreads compute threads own 32 x (32 kNT) tiles each.
 template <int FMT>
-__global__ __launch_bounds__(kThreads + kLoadThreads) void gemm_kernel(const uint8_t* __restrict__ Wb,
-                                                            const uint8_t* __restrict__ Xb,
-                                                            float* __restrict__ Y, int64_t M,
-                                                            int K, int64_t N, int64_t tiles_n,
-                                                            int64_t ntiles) {
+__global__ __launch_bounds__(kThreads + kLoadThreads) void gemm_kernel(
+    const uint8_t* __restrict__ Wb, const uint8_t* __restrict__ Xb, float* __restrict__ Y,
+    int64_t M, int K, int64_t N, int64_t tiles_n, int64_t ntiles) {
   __shared__ __attribute__((aligned(16))) Stage st[2];
-  typedef StageRegs<FMT> R;
+  typedef TileLoader<FMT, kLoadThreads> TL;
   // role per wave, in a scalar register so that the branch is uniform
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const bool loader = wave >= kThreads / kWave;
@@ -320,16 +546,9 @@ __global__ __launch_bounds__(kThreads + kLoadThreads) void gemm_kernel(const uin
   const int l32 = lane & 31;
   const int nb = K >> 5;  // 32-element blocks along K
   const int nstage = (nb + kKB - 1) / kKB;
-  constexpr int wbytes = FMT == kFmtQ4_0 ? 18 : FMT == kFmtQ8_0 ? 34 : 144;
-  const int64_t wrb = FMT == kFmtQ4_K ? (int64_t)(K >> 8) * 144 : (int64_t)nb * wbytes;
+  const int64_t wrb = FMT == kFmtQ4_K ? (int64_t)(K >> 8) * 144 : (int64_t)nb * TL::wbytes;
   const int64_t xrb = (int64_t)nb * 34;
-
-  // XCD-aware order: XCD x = id % 8 takes linear tiles [x * per, (x+1) * per)
-  int64_t lin = blockIdx.x;
-  if ((ntiles & 7) == 0 && (int64_t)gridDim.x == ntiles) {
-    const int64_t per = ntiles >> 3;
-    lin = (int64_t)(blockIdx.x & 7) * per + (blockIdx.x >> 3);
-  }
+  const int64_t lin = first_tile(ntiles);
 
   // Each role runs its own tile loop (so that neither keeps the other's
   // tile-invariant values live); both pass the same barriers per tile: one
@@ -338,141 +557,27 @@ __global__ __launch_bounds__(kThreads + kLoadThreads) void gemm_kernel(const uin
     for (int64_t tile = lin; tile < ntiles; tile += gridDim.x) {
       const int64_t tm = tile / tiles_n, tn = tile - tm * tiles_n;
       const int64_t m0 = tm * kBM, n0 = tn * kBN;
-      // item -> (row, block): 8 consecutive threads cover one row's 8
-      // blocks of a stage. A stage is the same 8 blocks of every row, so an
-      // item keeps its byte offsets from the stage's (wave-uniform) base,
-      // and its alignment case, for the whole tile. Rows past M re-read the
-      // last row.
-      constexpr int stage_wbytes = FMT == kFmtQ4_K ? 144 : kKB * wbytes;
-      const uint8_t* wtile = Wb + m0 * wrb;
-      const uint8_t* xtile = Xb + n0 * xrb;
-      const uint32_t wlast = (uint32_t)min<int64_t>(kBM - 1, M - 1 - m0);
-      const uint32_t xlast = (uint32_t)min<int64_t>(kBN - 1, N - 1 - n0);
-      // tile bases mod 4 (the buffers are 16-byte aligned, stage strides are
-      // multiples of 4)
-      const uint32_t wpar = (uint32_t)(m0 * wrb) & 3u, xpar = (uint32_t)(n0 * xrb) & 3u;
-      BlkLane wl[R::kWItems], xl[R::kXItems];
-#pragma unroll
-      for (int it = 0; it < R::kWItems; ++it) {
-        const int item = tid + it * kLoadThreads;
-        const uint32_t ro = min((uint32_t)(item >> 3), wlast) * (uint32_t)wrb;
-        if (FMT == kFmtQ4_K) {
-          wl[it].o16 = ro;  // superblock header
-          wl[it].o2 = ro + 16u + 16u * (uint32_t)(item & 7);  // sub-block codes
-          wl[it].sel = 0u;
-          wl[it].hsel = 0u;
-        } else {
-          wl[it] = blk_lane(ro + (uint32_t)(item & 7) * (uint32_t)wbytes, wpar, wbytes);
-        }
-      }
-#pragma unroll
-      for (int it = 0; it < R::kXItems; ++it) {
-        const int item = tid + it * kLoadThreads;
-        const uint32_t ro = min((uint32_t)(item >> 3), xlast) * (uint32_t)xrb;
-        xl[it] = blk_lane(ro + (uint32_t)(item & 7) * 34u, xpar, 34);
-      }
-      // global -> registers for stage s (blocks past nb are not loaded)
-      // the bytes from each tile base to the end of its matrix
-      const __amdgpu_buffer_rsrc_t wrs = make_rsrc(wtile, (M - m0) * wrb);
-      const __amdgpu_buffer_rsrc_t xrs = make_rsrc(xtile, (N - n0) * xrb);
-      auto load_stage = [&](int s, R& r) {
-        const uint32_t wso = (uint32_t)s * (uint32_t)stage_wbytes;
-        const uint32_t xso = (uint32_t)s * (uint32_t)(kKB * 34);
-        const int left = nb - s * kKB;  // blocks of this stage that exist
-#pragma unroll
-        for (int it = 0; it < R::kWItems; ++it) {
-          if (((tid + it * kLoadThreads) & 7) < left) {
-            if (FMT == kFmtQ4_K) {
-              r.wa[it] = __builtin_amdgcn_raw_buffer_load_b128(wrs, wl[it].o16, wso, 0);
-              r.wb[it] = __builtin_amdgcn_raw_buffer_load_b128(wrs, wl[it].o2, wso, 0);
-            } else {
-              load_lane(wrs, wso, wl[it], wbytes, r.wa[it], r.wb[it], r.ws[it]);
-            }
-          }
-        }
-#pragma unroll
-        for (int it = 0; it < R::kXItems; ++it)
-          if (((tid + it * kLoadThreads) & 7) < left)
-            load_lane(xrs, xso, xl[it], 34, r.xa[it], r.xb[it], r.xs[it]);
-      };
-      // registers -> LDS buffer for stage s
-      auto write_stage = [&](int s, const R& r, Stage& dst) {
-        const int left = nb - s * kKB;
-#pragma unroll
-        for (int it = 0; it < R::kWItems; ++it) {
-          const int item = tid + it * kLoadThreads;
-          const int rr = item >> 3, bb = item & 7;
-          if (bb < left) {
-            if (FMT == kFmtQ4_0) {
-              uint32_t h, c[8];
-              realign_lane(wl[it], 18, r.wa[it], r.wb[it], r.ws[it], h, c);
-              store16(dst.w(bb, 0, rr), nib_signed(c[0], 0), nib_signed(c[1], 0),
-                      nib_signed(c[2], 0), nib_signed(c[3], 0));
-              store16(dst.w(bb, 1, rr), nib_signed(c[0], 4), nib_signed(c[1], 4),
-                      nib_signed(c[2], 4), nib_signed(c[3], 4));
-              dst.wd[bb][rr] = f16_bits_to_f32(h);
-            } else if (FMT == kFmtQ8_0) {
-              uint32_t h, c[8];
-              realign_lane(wl[it], 34, r.wa[it], r.wb[it], r.ws[it], h, c);
-              store16(dst.w(bb, 0, rr), c[0], c[1], c[2], c[3]);
-              store16(dst.w(bb, 1, rr), c[4], c[5], c[6], c[7]);
-              dst.wd[bb][rr] = f16_bits_to_f32(h);
-            } else {
-              const u32x4 hd = r.wa[it], cv = r.wb[it];
-              const int sub = bb;  // a stage is one superblock
-              const int ps = 6 * sub, pm = 48 + 6 * sub;
-              const uint32_t slo = ps < 32 ? hd.y : hd.z, shi = ps < 32 ? hd.z : hd.w;
-              const uint32_t mlo = pm < 64 ? hd.z : hd.w, mhi = pm < 64 ? hd.w : 0u;
-              const uint32_t sc = __builtin_amdgcn_alignbit(shi, slo, ps & 31) & 63u;
-              const uint32_t mn = __builtin_amdgcn_alignbit(mhi, mlo, pm & 31) & 63u;
-              store16(dst.w(bb, 0, rr), nib_unsigned(cv.x, 0), nib_unsigned(cv.y, 0),
-                      nib_unsigned(cv.z, 0), nib_unsigned(cv.w, 0));
-              store16(dst.w(bb, 1, rr), nib_unsigned(cv.x, 4), nib_unsigned(cv.y, 4),
-                      nib_unsigned(cv.z, 4), nib_unsigned(cv.w, 4));
-              dst.wd[bb][rr] = f16_bits_to_f32(hd.x) * (float)sc;
-              dst.wo[bb][rr] = -(f16_bits_to_f32(hd.x >> 16) * (float)mn);  // -O
-            }
-          }
-        }
-#pragma unroll
-        for (int it = 0; it < R::kXItems; ++it) {
-          const int item = tid + it * kLoadThreads;
-          const int cc = item >> 3, bb = item & 7;
-          if (bb < left) {
-            uint32_t h, c[8];
-            realign_lane(xl[it], 34, r.xa[it], r.xb[it], r.xs[it], h, c);
-            store16(dst.x(bb, 0, cc), c[0], c[1], c[2], c[3]);
-            store16(dst.x(bb, 1, cc), c[4], c[5], c[6], c[7]);
-            const float dx = f16_bits_to_f32(h);
-            dst.xd[bb][cc] = dx;
-            if (FMT == kFmtQ4_K) {
-              int qs = 0;
-#pragma unroll
-              for (int i = 0; i < 8; ++i)
-                qs = __builtin_amdgcn_sdot4((int)c[i], 0x01010101, qs, false);
-              dst.xs[bb][cc] = dx * (float)qs;
-            }
-          }
-        }
-      };
-
+      TL ld;
+      ld.setup(M, N, m0, n0, wrb, xrb, tid, nb);
+      const __amdgpu_buffer_rsrc_t wrs = make_rsrc(Wb + m0 * wrb, (M - m0) * wrb);
+      const __amdgpu_buffer_rsrc_t xrs = make_rsrc(Xb + n0 * xrb, (N - n0) * xrb);
       // Register set k holds stages k, k + kDepth, ...: set indices stay
       // compile-time constants by stepping kDepth stages per iteration.
-      R regs[kDepth];
+      typename TL::Regs regs[kDepth];
 #pragma unroll
       for (int k = 0; k < kDepth; ++k)
-        if (k < nstage) load_stage(k, regs[k]);
+        if (k < nstage) ld.load(wrs, xrs, k, regs[k]);
       if (nstage > 0) {
-        write_stage(0, regs[0], st[0]);
-        if (kDepth < nstage) load_stage(kDepth, regs[0]);
+        ld.write(0, regs[0], st[0]);
+        if (kDepth < nstage) ld.load(wrs, xrs, kDepth, regs[0]);
       }
       __syncthreads();
       // step s: write stage s+1 (set (s+1) % kDepth), refill it with stage
       // s+1+kDepth
-      auto step = [&](int s, R& r) {
+      auto step = [&](int s, typename TL::Regs& r) {
         if (s + 1 < nstage) {
-          write_stage(s + 1, r, st[(s + 1) & 1]);
-          if (s + 1 + kDepth < nstage) load_stage(s + 1 + kDepth, r);
+          ld.write(s + 1, r, st[(s + 1) & 1]);
+          if (s + 1 + kDepth < nstage) ld.load(wrs, xrs, s + 1 + kDepth, r);
         }
         __syncthreads();
       };
@@ -488,98 +593,23 @@ __global__ __launch_bounds__(kThreads + kLoadThreads) void gemm_kernel(const uin
       __syncthreads();
     }
   } else {
+    const i32x16 cmagic = magic_vec();
+    const int wm = wv % kRT, wn0 = (wv / kRT) * kNT;  // rows 32wm.., column tiles wn0..
     for (int64_t tile = lin; tile < ntiles; tile += gridDim.x) {
       const int64_t tm = tile / tiles_n, tn = tile - tm * tiles_n;
       const int64_t m0 = tm * kBM, n0 = tn * kBN;
-      i32x16 cmagic;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) cmagic[i] = (int)kMagicI;
-      const int wm = wv % kRT, wn0 = (wv / kRT) * kNT;  // rows 32wm.., column tiles wn0..
       float acc[kNT][16];
 #pragma unroll
       for (int t = 0; t < kNT; ++t)
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[t][i] = 0.0f;
-
       __syncthreads();  // stage 0 is in LDS
       for (int s = 0; s < nstage; ++s) {
-        const Stage& cur = st[s & 1];
-        const int nbs = min(kKB, nb - s * kKB);
-        if (nbs == kKB) {
-          // Full stage, software-pipelined: the column scales of all 8
-          // blocks are read up front; in step bb the MFMAs of block bb+1 are
-          // issued (operands read one step earlier), the operands of block
-          // bb+2 and the row scales of block bb+1 are requested, and block bb
-          // is scaled into the accumulators, so that the LDS, the matrix
-          // core and the VALU overlap.
-          float dxs[kKB][kNT], c1s[kKB][kNT];
-#pragma unroll
-          for (int bb = 0; bb < kKB; ++bb)
-#pragma unroll
-            for (int t = 0; t < kNT; ++t) dxs[bb][t] = cur.xd[bb][(wn0 + t) * 32 + l32];
-          Ops<kNT> op[2];
-          float dw[2][16];
-          i32x16 d[2][kNT];
-          load_ops(cur, 0, wm, wn0, l32, half, op[0]);
-          load_ops(cur, 1, wm, wn0, l32, half, op[1]);
-          load_dw<kNT>(cur, 0, wm, half, dw[0]);
-#pragma unroll
-          for (int bb = 0; bb < kKB; ++bb)
-#pragma unroll
-            for (int t = 0; t < kNT; ++t) c1s[bb][t] = -kMagicF * dxs[bb][t];
-#pragma unroll
-          for (int t = 0; t < kNT; ++t)
-            d[0][t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(op[0].a, op[0].b[t], cmagic, 0, 0, 0);
-#pragma unroll
-          for (int bb = 0; bb < kKB; ++bb) {
-            __builtin_amdgcn_sched_barrier(0);
-            if (bb + 1 < kKB) {
-#pragma unroll
-              for (int t = 0; t < kNT; ++t)
-                d[(bb + 1) & 1][t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
-                    op[(bb + 1) & 1].a, op[(bb + 1) & 1].b[t], cmagic, 0, 0, 0);
-            }
-            if (bb + 2 < kKB) load_ops(cur, bb + 2, wm, wn0, l32, half, op[bb & 1]);
-            if (bb + 1 < kKB) load_dw<kNT>(cur, bb + 1, wm, half, dw[(bb + 1) & 1]);
-            __builtin_amdgcn_sched_barrier(0);
-            apply_block(dw[bb & 1], dxs[bb], c1s[bb], d[bb & 1], acc);
-            if (FMT == kFmtQ4_K && (bb & 1)) min_term(cur, bb - 1, kKB, wm, wn0, l32, half, acc);
-          }
-        } else {
-          for (int bb = 0; bb < nbs; ++bb) {
-            i32x16 d[kNT];
-            Scales<kNT> sc;
-#pragma unroll
-            for (int t = 0; t < kNT; ++t) mfma_block(cur, bb, wm, wn0 + t, l32, half, cmagic, d[t]);
-            load_scales(cur, bb, wm, wn0, l32, half, sc);
-            apply_scales(sc, d, acc);
-            if (FMT == kFmtQ4_K && ((bb & 1) || bb + 1 == nbs))
-              min_term(cur, bb & ~1, nbs, wm, wn0, l32, half, acc);
-          }
-        }
+        compute_stage<FMT, kNT>(st[s & 1], min(kKB, nb - s * kKB), wm, wn0, l32, half, cmagic,
+                                acc);
         __syncthreads();
       }
-
-      // ---- store: lane holds column n = n0 + 32(wn0 + t) + l32, rows
-      //      m = m0 + 32 wm + 8q + 4 half + r  (q, r in 0..3)
-#pragma unroll
-      for (int t = 0; t < kNT; ++t) {
-        const int64_t n = n0 + 32 * (wn0 + t) + l32;
-        if (n >= N) continue;
-        float* yrow = Y + n * M;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int64_t mb = m0 + wm * 32 + 8 * q + 4 * half;
-          if (mb + 3 < M && (M & 3) == 0) {
-            f32x4 v = {acc[t][4 * q], acc[t][4 * q + 1], acc[t][4 * q + 2], acc[t][4 * q + 3]};
-            *reinterpret_cast<f32x4*>(yrow + mb) = v;
-          } else {
-#pragma unroll
-            for (int r2 = 0; r2 < 4; ++r2)
-              if (mb + r2 < M) yrow[mb + r2] = acc[t][4 * q + r2];
-          }
-        }
-      }
+      store_tile<kNT>(Y, M, N, m0, n0, wm, wn0, l32, half, acc);
       __syncthreads();
     }
   }
@@ -597,20 +627,21 @@ hipError_t launch_gemm(int fmt, const void* blocks, const void* Xq8, float* Y, i
   const unsigned grid = (unsigned)(ntiles < kMaxGrid ? ntiles : kMaxGrid);
   const uint8_t* W = static_cast<const uint8_t*>(blocks);
   const uint8_t* X = static_cast<const uint8_t*>(Xq8);
+#define QMAT_GEMM_LAUNCH(F)                                                                \
+  hipLaunchKernelGGL(gemm_kernel<F>, dim3(grid), dim3(kThreads + kLoadThreads), 0, stream, W, \
+                     X, Y, M, (int)K, N, tiles_n, ntiles)
   switch (fmt) {
     case kFmtQ4_0:
-      hipLaunchKernelGGL(gemm_kernel<kFmtQ4_0>, dim3(grid), dim3(kThreads + kLoadThreads), 0, stream, W, X, Y,
-                         M, (int)K, N, tiles_n, ntiles);
+      QMAT_GEMM_LAUNCH(kFmtQ4_0);
       break;
     case kFmtQ8_0:
-      hipLaunchKernelGGL(gemm_kernel<kFmtQ8_0>, dim3(grid), dim3(kThreads + kLoadThreads), 0, stream, W, X, Y,
-                         M, (int)K, N, tiles_n, ntiles);
+      QMAT_GEMM_LAUNCH(kFmtQ8_0);
       break;
     default:
-      hipLaunchKernelGGL(gemm_kernel<kFmtQ4_K>, dim3(grid), dim3(kThreads + kLoadThreads), 0, stream, W, X, Y,
-                         M, (int)K, N, tiles_n, ntiles);
+      QMAT_GEMM_LAUNCH(kFmtQ4_K);
       break;
   }
+#undef QMAT_GEMM_LAUNCH
   return hipGetLastError();
 }
 
