@@ -62,6 +62,10 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_q4_0_llama7b_traffic.json")
 GEMV_SRC = os.path.join(ROOT, "block_quantized_weight_qmat_amd", "csrc", "gemv.hip")
 ALL_OPS = ["quantize_q4_0", "quantize_q8_0", "quantize_q4_k", "gemv_q4_0", "gemv_q8_0",
            "gemv_q4_k", "quantize_act_q8_0", "gemm_q4_0"]
+# the few-token decode batch (qmat_gemm with N <= 48): timed per kernel,
+# not part of the step
+DECODE_NS = (4, 16)
+EXTRA_OPS = [f"decode_q4_0_n{n}" for n in DECODE_NS]
 
 
 def parse():
@@ -73,7 +77,7 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="approximate CPU time for the oracle baseline sample")
     p.add_argument("--only", default="all",
-                   help="comma list of ops (" + ",".join(ALL_OPS) + ",copy) or all")
+                   help="comma list of ops (" + ",".join(ALL_OPS + EXTRA_OPS) + ",copy) or all")
     p.add_argument("--batch", type=int, default=0,
                    help="launches per kernel-timing batch (default max(steps, 50))")
     p.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
@@ -198,7 +202,7 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    only = ALL_OPS if args.only == "all" else args.only.split(",")
+    only = ALL_OPS + EXTRA_OPS if args.only == "all" else args.only.split(",")
 
     # ------------------------------------------------------------ inputs
     W_np, x_np = inputs.llama7b_layer(0)
@@ -214,13 +218,16 @@ def main():
         return [t.clone() for _ in range(n)]
 
     need = lambda prefix: any(o.startswith(prefix) for o in only)
-    cold = {f: copies(packed[f], COLD_BYTES) if need("gemv_" + f) else [packed[f]] for f in fmts}
+    cold = {f: copies(packed[f], COLD_BYTES) if need("gemv_" + f) or need("decode_" + f)
+            else [packed[f]] for f in fmts}
     W_rot = [Wf] + ([Wf.clone()] if need("quantize_q") else [])
     X_rot = [torch.from_numpy(X_np).to(dev) for _ in range(12 if need("quantize_act") else 1)]
     q_out = {f: torch.empty_like(packed[f]) for f in fmts}
     y = {f: torch.empty(M, dtype=torch.float32, device=dev) for f in fmts}
     Xq = binding.quantize(1, X_rot[0])
     Y = torch.empty((N, M), dtype=torch.float32, device=dev)
+    Xq_dec = {n: binding.quantize(1, X_rot[0][:n].contiguous()) for n in DECODE_NS}
+    Y_dec = {n: torch.empty((n, M), dtype=torch.float32, device=dev) for n in DECODE_NS}
     src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
@@ -230,6 +237,7 @@ def main():
     quant_bytes = {f: 4 * M * K + M * rb[f] for f in fmts}
     actq_bytes = 4 * N * K + N * binding.row_bytes(1, K)
     gemm_ops = 2 * M * N * K
+    dec_bytes = {n: M * rb["q4_0"] + n * binding.row_bytes(1, K) + 4 * n * M for n in DECODE_NS}
 
     table = {}
     for f, i in fmts.items():
@@ -239,8 +247,12 @@ def main():
             i, cold[f][s % len(cold[f])], x, M, K, out=y[f])
     table["quantize_act_q8_0"] = lambda s: binding.quantize(1, X_rot[s % len(X_rot)], out=Xq)
     table["gemm_q4_0"] = lambda s: binding.gemm(0, packed["q4_0"], Xq, M, K, N, out=Y)
+    for n in DECODE_NS:
+        table[f"decode_q4_0_n{n}"] = lambda s, n=n: binding.gemm(
+            0, cold["q4_0"][s % len(cold["q4_0"])], Xq_dec[n], M, K, n, out=Y_dec[n])
     table["copy"] = lambda s: dst.copy_(src)
-    ops = [(name, table[name]) for name in only]
+    ops = [(name, table[name]) for name in only if name not in EXTRA_OPS]
+    extra = [(name, table[name]) for name in only if name in EXTRA_OPS]
 
     # ------------------------------------------------------------ steps
     for s in range(args.warmup):
@@ -256,7 +268,7 @@ def main():
 
     # ------------------------------------------------------------ kernels
     nb = args.batch if args.batch > 0 else max(args.steps, 50)
-    mean_us = {name: timed_batch(torch, fn, nb) for name, fn in ops if name != "copy"}
+    mean_us = {name: timed_batch(torch, fn, nb) for name, fn in ops + extra if name != "copy"}
 
     kernels = {}
     for name, us in mean_us.items():
@@ -274,6 +286,11 @@ def main():
             gbs = quant_bytes[f] / us / 1e3
             kernels[name] = {"us": us, "bytes": quant_bytes[f], "GB/s": gbs, "bound": "hbm",
                              "frac": gbs / HBM_PEAK_GBS}
+        elif name.startswith("decode_"):
+            n = int(name.rsplit("_n", 1)[1])
+            gbs = dec_bytes[n] / us / 1e3
+            kernels[name] = {"us": us, "bytes": dec_bytes[n], "GB/s": gbs, "bound": "hbm",
+                             "frac": gbs / HBM_PEAK_GBS, "tokens_per_s": n / us * 1e6}
         elif name.startswith("gemm_"):
             tops = gemm_ops / us / 1e6
             kernels[name] = {"us": us, "int8_ops": gemm_ops, "TOPS": tops, "bound": "mfma",

@@ -616,12 +616,19 @@ __global__ __launch_bounds__(kThreads + kLoadThreads) void gemm_kernel(
 }
 
 constexpr int64_t kMaxGrid = 1 << 24;
+#ifndef QMAT_GEMM_SMALL_N
+#define QMAT_GEMM_SMALL_N 48
+#endif
+constexpr int64_t kSmallN = QMAT_GEMM_SMALL_N;
 
 }  // namespace
 
 hipError_t launch_gemm(int fmt, const void* blocks, const void* Xq8, float* Y, int64_t M,
                        int64_t K, int64_t N, hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
+  // a few tokens: the weights are streamed once per 16 tokens instead (the
+  // MFMA tiles would leave most of the GPU idle)
+  if (N <= kSmallN) return launch_gemm_small(fmt, blocks, Xq8, Y, M, K, N, stream);
   const int64_t tiles_m = (M + kBM - 1) / kBM, tiles_n = (N + kBN - 1) / kBN;
   const int64_t ntiles = tiles_m * tiles_n;
   const unsigned grid = (unsigned)(ntiles < kMaxGrid ? ntiles : kMaxGrid);

@@ -612,6 +612,303 @@ hipError_t launch_fmt(const void* blocks, const float* x, float* y, int64_t M, i
   return hipGetLastError();
 }
 
+// ------------------------------------------------ small-N decode GEMM --
+// Y[n][m] = sum_k W[m][k] X[n][k] for a few tokens at once, X given as Q8_0
+// blocks. As in the GEMV every weight block is read from memory once, but it
+// is applied to NT tokens: the codes are unpacked to int8 once per block and
+// multiplied with each token's int8 block by v_dot4_i32_i8 (exact), then
+// scaled by the two fp16 block scales in fp32.
+//
+// A workgroup owns G waves x R rows and all of K; each wave walks K in strips
+// of 64 slices (lane = slice). The activation records of a strip (NT tokens x
+// 64 slices: 32 int8 codes, dx, and dx * sum(codes) for Q4_K-style) are
+// unpacked once per workgroup into LDS and shared by its waves; the next
+// strip's records and weight blocks are requested while the current strip is
+// used, and its records go to the other LDS buffer afterwards.
+#ifndef QMAT_SMALL_CFG
+// rows per wave and waves per workgroup for 1-4, 8 and 16 tokens
+#define QMAT_SMALL_R4 1
+#define QMAT_SMALL_G4 16
+#define QMAT_SMALL_R8 1
+#define QMAT_SMALL_G8 16
+#define QMAT_SMALL_R16 1
+#define QMAT_SMALL_G16 16
+#endif
+
+// 32 int8 codes of a weight block in element order (word i = elements
+// 4i..4i+3), its scale S and, for Q4_K-style, its offset O (weight = S q - O).
+struct WBlk {
+  uint32_t w[8];
+  float S, O;
+};
+
+__device__ __forceinline__ uint32_t nib_s8(uint32_t c, int sh) {
+  return (((c >> sh) & 0x0F0F0F0Fu) + 0x78787878u) ^ 0x80808080u;  // c - 8 per byte
+}
+
+__device__ __forceinline__ WBlk unpack_w(const FmtQ4_0::Raw& r, const BlockLane& L, int /*j*/) {
+  WBlk b;
+  const uint32_t c[4] = {perm_b32(r.v.y, r.v.x, L.sel), perm_b32(r.v.z, r.v.y, L.sel),
+                         perm_b32(r.v.w, r.v.z, L.sel), perm_b32(r.s, r.v.w, L.sel)};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    b.w[i] = nib_s8(c[i], 0);      // elements 4i..4i+3 (low nibbles)
+    b.w[4 + i] = nib_s8(c[i], 4);  // elements 16+4i.. (high nibbles)
+  }
+  b.S = f16_bits_to_f32(L.mis ? r.s : r.v.x);
+  b.O = 0.0f;
+  return b;
+}
+
+__device__ __forceinline__ WBlk unpack_w(const FmtQ8_0::Raw& r, const BlockLane& L, int /*j*/) {
+  WBlk b;
+  const uint32_t w[9] = {r.v0.x, r.v0.y, r.v0.z, r.v0.w, r.v1.x, r.v1.y, r.v1.z, r.v1.w, r.s};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) b.w[i] = perm_b32(w[i + 1], w[i], L.sel);
+  b.S = f16_bits_to_f32(L.mis ? r.s : r.v0.x);
+  b.O = 0.0f;
+  return b;
+}
+
+__device__ __forceinline__ WBlk unpack_w(const FmtQ4_K::Raw& r, const BlockLane& /*L*/, int j) {
+  WBlk b;
+  const uint32_t c[4] = {r.c.x, r.c.y, r.c.z, r.c.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    b.w[i] = c[i] & 0x0F0F0F0Fu;
+    b.w[4 + i] = (c[i] >> 4) & 0x0F0F0F0Fu;
+  }
+  const int sub = j & 7;
+  const int ps = 6 * sub, pm = 48 + 6 * sub;
+  const uint32_t slo = ps < 32 ? r.h.y : r.h.z, shi = ps < 32 ? r.h.z : r.h.w;
+  const uint32_t mlo = pm < 64 ? r.h.z : r.h.w, mhi = pm < 64 ? r.h.w : 0u;
+  const uint32_t sc = __builtin_amdgcn_alignbit(shi, slo, ps & 31) & 63u;
+  const uint32_t mn = __builtin_amdgcn_alignbit(mhi, mlo, pm & 31) & 63u;
+  b.S = f16_bits_to_f32(r.h.x) * (float)sc;
+  b.O = f16_bits_to_f32(r.h.x >> 16) * (float)mn;
+  return b;
+}
+
+// LDS image of one strip's activation records for NT tokens: the two
+// 16-byte halves of the 32 codes, dx, and dx * sum(codes).
+template <int NT>
+struct XRecs {
+  uint32_t q[NT][2][kWave][4];
+  float dx[NT][kWave];
+  float xs[NT][kWave];
+};
+
+template <class F, int R, int G, int NT, bool kOdd>
+__global__ __launch_bounds__(G * kWave) void gemm_small_kernel(
+    const uint8_t* __restrict__ B, const uint8_t* __restrict__ Xq, float* __restrict__ Y,
+    int64_t M, int K, int64_t N, int64_t n0) {
+  static_assert((R * NT & (R * NT - 1)) == 0 && R * NT <= kWave, "values per lane");
+  constexpr bool kQ4K = F::kBytes == 144;
+  constexpr int kT = G * kWave;
+  constexpr int kRecs = (NT * kWave + kT - 1) / kT;  // records a thread stages per strip
+  __shared__ __attribute__((aligned(16))) XRecs<NT> xr[2];
+  const int tid = (int)threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+  const int ns = K >> 5;
+  const int nstrips = (ns + kWave - 1) / kWave;
+  const int64_t rb = F::row_bytes(K);
+  const int64_t xrb = (int64_t)ns * 34;
+  const int64_t mw = (int64_t)blockIdx.x * (G * R) + wv * R;  // this wave's first row
+
+  // activation records: raw loads of a strip, then unpack into LDS
+  struct XRaw {
+    u32x4 a, b;
+    uint32_t s;
+  };
+  XRaw xraw[kRecs];
+  auto load_x = [&](int strip) {
+#pragma unroll
+    for (int k = 0; k < kRecs; ++k) {
+      const int rec = tid + k * kT;
+      const int n = rec >> 6, jj = rec & 63;
+      const int j = strip * kWave + jj;
+      if (rec < NT * kWave && n0 + n < N && j < ns) {
+        const uint8_t* row = Xq + (n0 + n) * xrb;
+        const BlockLane L = block_lane((uint32_t)j * 34u, (uint32_t)((n0 + n) * xrb) & 2u, 34);
+        xraw[k].a = *reinterpret_cast<const u32x4_a4*>(row + L.o16);
+        xraw[k].b = *reinterpret_cast<const u32x4_a4*>(row + L.o16 + 16);
+        xraw[k].s = *reinterpret_cast<const uint16_t*>(row + L.o2);
+      }
+    }
+  };
+  auto store_x = [&](int strip, XRecs<NT>& dst) {
+#pragma unroll
+    for (int k = 0; k < kRecs; ++k) {
+      const int rec = tid + k * kT;
+      if (rec >= NT * kWave) continue;
+      const int n = rec >> 6, jj = rec & 63;
+      const int j = strip * kWave + jj;
+      uint32_t c[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+      float dx = 0.0f;
+      if (n0 + n < N && j < ns) {
+        const BlockLane L = block_lane((uint32_t)j * 34u, (uint32_t)((n0 + n) * xrb) & 2u, 34);
+        const uint32_t w[9] = {xraw[k].a.x, xraw[k].a.y, xraw[k].a.z, xraw[k].a.w,
+                               xraw[k].b.x, xraw[k].b.y, xraw[k].b.z, xraw[k].b.w, xraw[k].s};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) c[i] = perm_b32(w[i + 1], w[i], L.sel);
+        dx = f16_bits_to_f32(L.mis ? xraw[k].s : xraw[k].a.x);
+      }
+      *reinterpret_cast<u32x4*>(dst.q[n][0][jj]) = u32x4{c[0], c[1], c[2], c[3]};
+      *reinterpret_cast<u32x4*>(dst.q[n][1][jj]) = u32x4{c[4], c[5], c[6], c[7]};
+      dst.dx[n][jj] = dx;
+      if (kQ4K) {
+        int qs = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) qs = sdot4(c[i], 0x01010101u, qs);
+        dst.xs[n][jj] = dx * (float)qs;
+      }
+    }
+  };
+
+  // weight blocks of this wave's R rows, slice (strip * 64 + lane)
+  auto lane_of = [&](int strip, BlockLane (&L)[2]) {
+    const int j = strip * kWave + lane;
+    if (kQ4K) {
+      const uint32_t o = (uint32_t)(j >> 3) * 144u;
+      L[0].o16 = o;
+      L[0].o2 = o + 16u + 16u * (uint32_t)(j & 7);
+      L[0].sel = 0;
+      L[0].mis = false;
+      L[1] = L[0];
+    } else {
+      const uint32_t o = (uint32_t)j * (uint32_t)F::kBytes;
+      L[0] = block_lane(o, 0u, F::kBytes);
+      L[1] = block_lane(o, kOdd ? 2u : 0u, F::kBytes);
+    }
+  };
+  typename F::Raw wraw[R];
+  auto load_w = [&](int strip) {
+    if (strip * kWave + lane < ns) {
+      BlockLane L[2];
+      lane_of(strip, L);
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        // with an odd row stride, row m starts at 2 (m & 1) mod 4; rows past
+        // M re-read the last row of the same parity (M >= 2 here)
+        const int p = kOdd ? (int)((mw + r) & 1) : 0;
+        int64_t m = mw + r;
+        if (m >= M) m = kOdd ? M - 1 - ((M - 1 - p) & 1) : M - 1;
+        F::load(B + m * rb, L[p], wraw[r]);
+      }
+    }
+  };
+
+  float acc[R * NT];
+#pragma unroll
+  for (int i = 0; i < R * NT; ++i) acc[i] = 0.0f;
+
+  if (nstrips > 0) {
+    load_x(0);
+    load_w(0);
+    store_x(0, xr[0]);
+  }
+  __syncthreads();
+  for (int st = 0; st < nstrips; ++st) {
+    const bool more = st + 1 < nstrips;
+    if (more) load_x(st + 1);
+    const int j = st * kWave + lane;
+    const bool live = j < ns;
+    WBlk wb[R];
+    {
+      BlockLane L[2];
+      lane_of(st, L);
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        wb[r] = unpack_w(wraw[r], L[kOdd ? (int)((mw + r) & 1) : 0], j);
+        if (!live) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) wb[r].w[i] = 0u;
+          wb[r].S = 0.0f;
+          wb[r].O = 0.0f;
+        }
+      }
+    }
+    if (more) load_w(st + 1);
+    const XRecs<NT>& cur = xr[st & 1];
+    // token records one ahead of their use (two in registers at a time)
+    u32x4 qa[2], qb[2];
+    float dxv[2], xsv[2];
+    auto read_rec = [&](int n, int slot) {
+      qa[slot] = *reinterpret_cast<const u32x4*>(cur.q[n][0][lane]);
+      qb[slot] = *reinterpret_cast<const u32x4*>(cur.q[n][1][lane]);
+      dxv[slot] = cur.dx[n][lane];
+      if (kQ4K) xsv[slot] = cur.xs[n][lane];
+    };
+    read_rec(0, 0);
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      if (n + 1 < NT) read_rec(n + 1, (n + 1) & 1);
+      const u32x4 a = qa[n & 1], b = qb[n & 1];
+      const uint32_t xq[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        int32_t S = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) S = sdot4(wb[r].w[i], xq[i], S);
+        const float t = (float)S * dxv[n & 1];
+        if (kQ4K)
+          acc[r * NT + n] = fmaf(-wb[r].O, xsv[n & 1], fmaf(t, wb[r].S, acc[r * NT + n]));
+        else
+          acc[r * NT + n] = fmaf(t, wb[r].S, acc[r * NT + n]);
+      }
+      // Keep the reads one token ahead: token n's sums are complete before
+      // the next record is requested. (Left alone, the compiler reads all NT
+      // records up front and holds them in registers.)
+#pragma unroll
+      for (int r = 0; r < R; ++r) asm volatile("" : "+v"(acc[r * NT + n])::"memory");
+    }
+    if (more) store_x(st + 1, xr[(st + 1) & 1]);
+    __syncthreads();
+  }
+
+  // value v = r * NT + n, summed over the wave's 64 slices
+  constexpr int RN = R * NT;
+  constexpr int kShift = 6 - log2i<RN>();
+  const int v = (lane >> kShift) & (RN - 1);
+  const float sum = wave_reduce_rows<RN>(acc, lane);
+  if ((lane & ((1 << kShift) - 1)) == 0) {
+    const int r = v / NT, n = v % NT;
+    const int64_t m = mw + r;
+    if (m < M && n0 + n < N) Y[(n0 + n) * M + m] = sum;
+  }
+}
+
+template <class F, int NT>
+hipError_t launch_small_fmt(const void* blocks, const void* Xq8, float* Y, int64_t M, int64_t K,
+                            int64_t N, int64_t n0, hipStream_t stream) {
+  constexpr int R = NT <= 4 ? QMAT_SMALL_R4 : NT <= 8 ? QMAT_SMALL_R8 : QMAT_SMALL_R16;
+  constexpr int G = NT <= 4 ? QMAT_SMALL_G4 : NT <= 8 ? QMAT_SMALL_G8 : QMAT_SMALL_G16;
+  const int64_t ns = K / 32;
+  const int64_t grid = (M + R * G - 1) / (R * G);
+  const bool odd = F::kBytes != 144 && (ns & 1) != 0 && M > 1;
+  if (odd)
+    hipLaunchKernelGGL((gemm_small_kernel<F, R, G, NT, true>), dim3((unsigned)grid),
+                       dim3(G * kWave), 0, stream, static_cast<const uint8_t*>(blocks),
+                       static_cast<const uint8_t*>(Xq8), Y, M, (int)K, N, n0);
+  else
+    hipLaunchKernelGGL((gemm_small_kernel<F, R, G, NT, false>), dim3((unsigned)grid),
+                       dim3(G * kWave), 0, stream, static_cast<const uint8_t*>(blocks),
+                       static_cast<const uint8_t*>(Xq8), Y, M, (int)K, N, n0);
+  return hipGetLastError();
+}
+
+template <class F>
+hipError_t launch_small_chunk(const void* blocks, const void* Xq8, float* Y, int64_t M,
+                              int64_t K, int64_t N, int64_t n0, hipStream_t stream) {
+  const int64_t nt = N - n0 < 16 ? N - n0 : 16;
+  if (nt <= 1) return launch_small_fmt<F, 1>(blocks, Xq8, Y, M, K, N, n0, stream);
+  if (nt <= 2) return launch_small_fmt<F, 2>(blocks, Xq8, Y, M, K, N, n0, stream);
+  if (nt <= 4) return launch_small_fmt<F, 4>(blocks, Xq8, Y, M, K, N, n0, stream);
+  if (nt <= 8) return launch_small_fmt<F, 8>(blocks, Xq8, Y, M, K, N, n0, stream);
+  return launch_small_fmt<F, 16>(blocks, Xq8, Y, M, K, N, n0, stream);
+}
+
 }  // namespace
 
 hipError_t launch_gemv(int fmt, const void* blocks, const float* x, float* y, int64_t M,
@@ -628,6 +925,30 @@ hipError_t launch_gemv(int fmt, const void* blocks, const float* x, float* y, in
       return launch_fmt<FmtQ4_K, QMAT_GEMV_R_Q4_K, QMAT_GEMV_G_Q4_K, QMAT_GEMV_D_Q4_K>(
           blocks, x, y, M, K, stream);
   }
+}
+
+}  // namespace qmat
+
+namespace qmat {
+
+hipError_t launch_gemm_small(int fmt, const void* blocks, const void* Xq8, float* Y, int64_t M,
+                             int64_t K, int64_t N, hipStream_t stream) {
+  for (int64_t n0 = 0; n0 < N; n0 += 16) {
+    hipError_t e;
+    switch (fmt) {
+      case kFmtQ4_0:
+        e = launch_small_chunk<FmtQ4_0>(blocks, Xq8, Y, M, K, N, n0, stream);
+        break;
+      case kFmtQ8_0:
+        e = launch_small_chunk<FmtQ8_0>(blocks, Xq8, Y, M, K, N, n0, stream);
+        break;
+      default:
+        e = launch_small_chunk<FmtQ4_K>(blocks, Xq8, Y, M, K, N, n0, stream);
+        break;
+    }
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace qmat

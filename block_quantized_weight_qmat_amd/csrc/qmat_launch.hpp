@@ -17,6 +17,10 @@ hipError_t launch_quantize(int fmt, const float* W, void* blocks, int64_t rows, 
 hipError_t launch_gemv(int fmt, const void* blocks, const float* x, float* y, int64_t M,
                        int64_t K, hipStream_t stream);
 
+// Few-token product (the decode batch): W streamed once per 16 tokens.
+hipError_t launch_gemm_small(int fmt, const void* blocks, const void* Xq8, float* Y, int64_t M,
+                             int64_t K, int64_t N, hipStream_t stream);
+
 hipError_t launch_gemm(int fmt, const void* blocks, const void* Xq8, float* Y, int64_t M,
                        int64_t K, int64_t N, hipStream_t stream);
 

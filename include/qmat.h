@@ -157,6 +157,10 @@ int qmat_gemv(int fmt, const void *blocks, const float *x, float *y,
  *   Y: fp32 [N][M] (token-major), overwritten.
  *   K is at most 2^24 here (QMAT_E_SHAPE above that): the kernel addresses
  *   a 128-row tile with 32-bit byte offsets.
+ *   Up to 48 tokens (a decode batch) the weights are instead streamed once
+ *   per 16 tokens and each weight block is applied to every token's block
+ *   with int8 dot products; the arithmetic (exact block sums, the two fp16
+ *   block scales applied in fp32) and the accuracy bound are the same.
  *   Accuracy: relative L2 error against the exact (fp64) product of the
  *   dequantized operands is below 2e-3; the per-block integer dot products
  *   are exact. Q4_K's min term (dmin*mn_j times the block sums of X_q8) is

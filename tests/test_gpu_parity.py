@@ -331,6 +331,53 @@ def test_gemm_small_and_ragged(q, fmt):
         assert rel_l2(Y, ref) <= GEMM_TOL, (M, K, N, rel_l2(Y, ref))
 
 
+@pytest.mark.parametrize("fmt", [0, 1, 2])
+def test_gemm_decode_small_n(q, fmt):
+    """Few-token products (the decode batch path, up to 48 tokens, in chunks
+    of 16): every token count around the chunk sizes, odd row strides,
+    ragged row counts, and the switch to the MFMA path after 48 tokens."""
+    rng = np.random.default_rng(700 + fmt)
+    K1 = 256 * 9 if fmt == 2 else 32 * 345  # odd block count per row (Q4_0/Q8_0)
+    cases = [(97, K1, n) for n in (1, 2, 3, 4, 5, 7, 8, 9, 15, 16, 17, 31, 33, 48, 49)]
+    cases += [(1, 256, 3), (2, 512, 16), (1000, 1024, 4), (33, 2048, 12)]
+    if fmt != 2:
+        cases += [(5, 32, 2), (64, 32 * 37, 6)]
+    for M, K, N in cases:
+        say(f"gemm decode fmt={fmt} M={M} K={K} N={N}")
+        W = mixed_matrix(rng, M, K) if M > 2 else rng.normal(0, 0.02, (M, K)).astype(np.float32)
+        X = rng.normal(0, 1, (N, K)).astype(np.float32)
+        Y, ref = gemm_case(q, fmt, W, X)
+        assert Y.shape == (N, M)
+        assert rel_l2(Y, ref) <= GEMM_TOL, (M, K, N, rel_l2(Y, ref))
+
+
+def test_gemm_decode_full_size_sampled(q):
+    """The 4096 x 11008 layer with 4, 16 and 48 tokens (the decode batch
+    path), checked on sampled rows against the oracle, and deterministic."""
+    import torch
+    W, X = inputs.llama7b_layer(0)
+    M, K = W.shape
+    rng = np.random.default_rng(11)
+    Xs = rng.normal(0, 1, (48, K)).astype(np.float32)
+    for fmt in (0, 1, 2):
+        dW = q.quantize(fmt, dev_tensor(W))
+        Bh = host(dW)
+        rb = oracle.row_bytes(fmt, K)
+        for N in (4, 16, 48):
+            say(f"gemm decode full fmt={fmt} N={N}")
+            dXq = q.quantize(1, dev_tensor(Xs[:N]))
+            Xq = host(dXq)
+            Y = host(q.gemm(fmt, dW, dXq, M, K, N))
+            assert np.all(np.isfinite(Y))
+            rows = np.sort(rng.choice(M, 40, replace=False))
+            ref = oracle.gemm(fmt, Bh.reshape(M, rb)[rows], Xq, len(rows), K, N)
+            assert rel_l2(Y[:, rows], ref) <= GEMM_TOL, (fmt, N, rel_l2(Y[:, rows], ref))
+            if N == 16:
+                assert np.array_equal(Y, host(q.gemm(fmt, dW, dXq, M, K, N)))
+        del dW
+    torch.cuda.empty_cache()
+
+
 def test_gemm_k_zero(q):
     import torch
     say("gemm K=0")
