@@ -6,7 +6,11 @@
 // is therefore built around the HBM stream of packed blocks, and its integer
 // work per block is kept small enough to hide under that stream.
 //
-// Work split
+// Work split. Two kernels share the arithmetic below. Rows of 256 slices or
+// more (K >= 8192) use gemv_rows_kernel: a workgroup of 16 waves owns 16
+// rows, one per wave; each strip of activations is converted once per
+// workgroup into LDS digit records shared by the 16 rows (see the kernel).
+// Shorter rows use gemv_kernel:
 //   * A workgroup owns G groups of R consecutive rows and all of K. Its waves
 //     split K into strips of 64 slices; lane l of a strip owns one
 //     32-element slice (one Q4_0/Q8_0 block, or one sub-block of a Q4_K
@@ -577,6 +581,273 @@ __global__ __launch_bounds__(kMaxStrips * kWave) void gemv_kernel(const uint8_t*
   }
 }
 
+// -------------------------------------------------- GEMV, a row per wave --
+// A workgroup of kRowWaves waves owns kRowWaves rows, one per wave, and walks
+// K in strips of 64 slices (lane = slice). A strip's activations are
+// converted once per workgroup into digit records in LDS (four lanes per
+// slice, waves 0-3) and shared by all the rows. The next strip's weight
+// blocks and activations are requested while the current strip is used;
+// its records go to the other LDS buffer afterwards.
+#ifndef QMAT_GEMV_ROW_WAVES
+#define QMAT_GEMV_ROW_WAVES 16
+#define QMAT_GEMV_ROW_R 1
+#endif
+constexpr int kRowWaves = QMAT_GEMV_ROW_WAVES;
+static_assert(kRowWaves >= 4, "waves 0-3 convert the 64 slices of a strip");
+
+// max over the four lanes of a quad (quad_perm [1,0,3,2] then [2,3,0,1])
+__device__ __forceinline__ float quad_max(float v) {
+  v = __builtin_fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                                     0, __builtin_bit_cast(int, v), 0xB1, 0xF,
+                                                     0xF, false)));
+  return __builtin_fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                                          0, __builtin_bit_cast(int, v), 0x4E,
+                                                          0xF, 0xF, false)));
+}
+
+__device__ __forceinline__ int32_t quad_sum(int32_t v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);
+  return v + __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);
+}
+
+// The slice scale of slice_scale() computed by a quad from its 8 elements
+// per lane (va, vb are rescaled in place like v there).
+__device__ __forceinline__ float quad_scale(f32x4& va, f32x4& vb, float lim, float& inv) {
+  float am = max3f(fabsf(va.x), fabsf(va.y), fabsf(va.z));
+  am = max3f(am, fabsf(va.w), fabsf(vb.x));
+  am = max3f(am, fabsf(vb.y), fabsf(vb.z));
+  am = __builtin_fmaxf(am, fabsf(vb.w));
+  am = quad_max(am);
+  int e;
+  frexpf(am, &e);
+  int s = 19 - e;
+  if (ldexpf(am, s) >= lim + 0.5f) s -= 1;
+  s = min(s, 149);
+  inv = ldexpf(1.0f, -s);
+  if (__builtin_expect(s > 120, 0)) {
+    va = f32x4{ldexpf(va.x, 64), ldexpf(va.y, 64), ldexpf(va.z, 64), ldexpf(va.w, 64)};
+    vb = f32x4{ldexpf(vb.x, 64), ldexpf(vb.y, 64), ldexpf(vb.z, 64), ldexpf(vb.w, 64)};
+    s -= 64;
+  }
+  return ldexpf(1.0f, s);
+}
+
+// LDS image of a strip's converted activations. Word t of digit i of
+// slice l sits at d[i][l][t], so a lane reads its slice's digit words with
+// one 16-byte load each and the quads write 64 consecutive words.
+struct XNibLds {
+  uint32_t d[5][kWave][4];
+  float inv[kWave];
+  int32_t sx[kWave];
+};
+
+// xl / xh / xt words 0-3 and 4-7 of slice l at w[j][h][l]
+struct XByteLds {
+  uint32_t w[3][2][kWave][4];
+  float inv[kWave];
+};
+
+__device__ __forceinline__ void conv_nib(f32x4 va, f32x4 vb, int sl, int k, bool want_sum,
+                                         XNibLds& o) {
+  float inv;
+  const float scale = quad_scale(va, vb, kNibLim, inv);
+  const float magic = kMagicF + (float)kNibBias;
+  uint32_t aL, aH, aT, bL, bH, bT, d[2];
+  bias20(va, scale, magic, aL, aH, aT);
+  bias20(vb, scale, magic, bL, bH, bT);
+  uint32_t w[5];
+  nib_digits(aL, bL, d);
+  w[0] = d[0];
+  w[1] = d[1];
+  nib_digits(aH, bH, d);
+  w[2] = d[0];
+  w[3] = d[1];
+  nib_digits(aT, bT, d);
+  w[4] = d[0];
+#pragma unroll
+  for (int i = 0; i < 5; ++i) o.d[i][sl][k] = w[i];
+  int32_t sx = 0;
+  if (want_sum) {
+    uint32_t a[5];
+#pragma unroll
+    for (int i = 0; i < 5; ++i) a[i] = (uint32_t)sdot8(w[i], 0x11111111u, 0);
+    sx = quad_sum((int32_t)((((a[4] * 16u + a[3]) * 16u + a[2]) * 16u + a[1]) * 16u + a[0]));
+  }
+  if (k == 0) {
+    o.inv[sl] = inv;
+    o.sx[sl] = sx;
+  }
+}
+
+__device__ __forceinline__ void read_nib(const XNibLds& o, int l, XNib& xp) {
+#pragma unroll
+  for (int i = 0; i < 5; ++i) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(&o.d[i][l][0]);
+    xp.d[i][0] = v.x;
+    xp.d[i][1] = v.y;
+    xp.d[i][2] = v.z;
+    xp.d[i][3] = v.w;
+  }
+  xp.inv = o.inv[l];
+  xp.sx = o.sx[l];
+}
+
+__device__ __forceinline__ void conv_byte(f32x4 va, f32x4 vb, int sl, int k, bool /*want_sum*/,
+                                          XByteLds& o) {
+  float inv;
+  const float scale = quad_scale(va, vb, kByteLim, inv);
+  const float magic = kMagicF + (float)kByteBias;
+  uint32_t lo, hi, top;
+  bias20(va, scale, magic, lo, hi, top);
+  o.w[0][0][sl][k] = lo ^ 0x80808080u;
+  o.w[1][0][sl][k] = hi ^ 0x80808080u;
+  o.w[2][0][sl][k] = ((top & 0x0F0F0F0Fu) + 0x78787878u) ^ 0x80808080u;
+  bias20(vb, scale, magic, lo, hi, top);
+  o.w[0][1][sl][k] = lo ^ 0x80808080u;
+  o.w[1][1][sl][k] = hi ^ 0x80808080u;
+  o.w[2][1][sl][k] = ((top & 0x0F0F0F0Fu) + 0x78787878u) ^ 0x80808080u;
+  if (k == 0) o.inv[sl] = inv;
+}
+
+__device__ __forceinline__ void read_byte(const XByteLds& o, int l, XByte& xp) {
+  uint32_t* dst[3] = {xp.xl, xp.xh, xp.xt};
+#pragma unroll
+  for (int j = 0; j < 3; ++j)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(&o.w[j][h][l][0]);
+      dst[j][4 * h + 0] = v.x;
+      dst[j][4 * h + 1] = v.y;
+      dst[j][4 * h + 2] = v.z;
+      dst[j][4 * h + 3] = v.w;
+    }
+  xp.inv = o.inv[l];
+  xp.sx = 0;
+}
+
+template <class XP>
+struct XLds;
+template <>
+struct XLds<XNib> {
+  typedef XNibLds T;
+};
+template <>
+struct XLds<XByte> {
+  typedef XByteLds T;
+};
+
+__device__ __forceinline__ void conv_slice(f32x4 va, f32x4 vb, int sl, int k, bool want_sum,
+                                           XNibLds& o) {
+  conv_nib(va, vb, sl, k, want_sum, o);
+}
+__device__ __forceinline__ void conv_slice(f32x4 va, f32x4 vb, int sl, int k, bool want_sum,
+                                           XByteLds& o) {
+  conv_byte(va, vb, sl, k, want_sum, o);
+}
+__device__ __forceinline__ void read_slice(const XNibLds& o, int l, XNib& xp) { read_nib(o, l, xp); }
+__device__ __forceinline__ void read_slice(const XByteLds& o, int l, XByte& xp) {
+  read_byte(o, l, xp);
+}
+
+
+template <class F, int R, bool kOdd>
+__global__ __launch_bounds__(kRowWaves * kWave) void gemv_rows_kernel(
+    const uint8_t* __restrict__ B, const float* __restrict__ x, float* __restrict__ y,
+    int64_t M, int K) {
+  typedef typename XLds<typename F::XP>::T XL;
+  __shared__ __attribute__((aligned(16))) XL xl[2];
+  constexpr bool kQ4K = F::kBytes == 144;
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int ns = K >> 5;
+  const int nstrips = (ns + kWave - 1) / kWave;
+  const int64_t rb = F::row_bytes(K);
+  const int64_t m0 = ((int64_t)blockIdx.x * kRowWaves + wv) * R;  // this wave's first row
+  // with an odd row stride, row m starts at 2 (m & 1) mod 4; a row past M
+  // re-reads the last row of the same parity (M >= 2 then)
+  const uint8_t* rows[R];
+  uint32_t par[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int64_t m = m0 + r;
+    par[r] = kOdd ? (uint32_t)(m & 1) : 0u;
+    const int64_t mr = m < M ? m : (kOdd ? M - 1 - ((M - 1 - (int64_t)par[r]) & 1) : M - 1);
+    rows[r] = B + mr * rb;
+  }
+
+  // activation conversion: waves 0-3, slice 16 wv + lane / 4, part lane % 4
+  const bool conv = wv < 4;
+  const int csl = 16 * wv + (lane >> 2), ck = lane & 3;
+  f32x4 va = {0.0f, 0.0f, 0.0f, 0.0f}, vb = va;
+  auto load_x = [&](int st) {
+    const int sl = st * kWave + csl;
+    if (conv && sl < ns) {
+      const float* xs = x + (int64_t)sl * 32 + 4 * ck;
+      va = *reinterpret_cast<const f32x4*>(xs);
+      vb = *reinterpret_cast<const f32x4*>(xs + 16);
+    }
+  };
+  auto conv_x = [&](int st, XL& dst) {
+    if (conv && st * kWave + csl < ns) conv_slice(va, vb, csl, ck, kQ4K, dst);
+  };
+  auto lane_of = [&](int st, uint32_t p) {
+    const int j = st * kWave + lane;
+    BlockLane L;
+    if (kQ4K) {
+      const uint32_t o = (uint32_t)(j >> 3) * 144u;
+      L.o16 = o;
+      L.o2 = o + 16u + 16u * (uint32_t)(j & 7);
+      L.sel = 0;
+      L.mis = false;
+    } else {
+      L = block_lane((uint32_t)j * (uint32_t)F::kBytes, 2u * p, F::kBytes);
+    }
+    return L;
+  };
+  typename F::Raw nxt[R];
+  auto load_w = [&](int st) {
+    if (st * kWave + lane < ns) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) F::load(rows[r], lane_of(st, par[r]), nxt[r]);
+    }
+  };
+
+  if (nstrips > 0) {
+    load_x(0);
+    load_w(0);
+    conv_x(0, xl[0]);
+    if (1 < nstrips) load_x(1);
+  }
+  __syncthreads();
+  typename F::Acc ac = {};
+  float part[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) part[r] = 0.0f;
+  for (int st = 0; st < nstrips; ++st) {
+    typename F::Raw cur[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) cur[r] = nxt[r];
+    if (st + 1 < nstrips) load_w(st + 1);
+    const int j = st * kWave + lane;
+    if (j < ns) {
+      typename F::XP xp;
+      read_slice(xl[st & 1], lane, xp);
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+        part[r] = fmaf(F::apply(cur[r], lane_of(st, par[r]), xp, j, ac), xp.inv, part[r]);
+    }
+    if (st + 1 < nstrips) {
+      conv_x(st + 1, xl[(st + 1) & 1]);
+      if (st + 2 < nstrips) load_x(st + 2);
+    }
+    __syncthreads();
+  }
+  constexpr int kShift = 6 - log2i<R>();
+  const int r = (lane >> kShift) & (R - 1);
+  const float sum = wave_reduce_rows<R>(part, lane);
+  if ((lane & ((1 << kShift) - 1)) == 0 && m0 + r < M) y[m0 + r] = sum;
+}
+
 #ifndef QMAT_GEMV_CFG
 // rows per group, groups per workgroup, groups in flight
 #define QMAT_GEMV_R_Q4_0 2
@@ -590,10 +861,34 @@ __global__ __launch_bounds__(kMaxStrips * kWave) void gemv_kernel(const uint8_t*
 #define QMAT_GEMV_D_Q4_K 3
 #endif
 
+#ifndef QMAT_GEMV_ROWS
+#define QMAT_GEMV_ROWS 1
+#endif
+// rows of at least this many slices (4 strips) go to the row-per-wave kernel;
+// shorter rows have too few strips to hide its per-strip conversion and
+// barrier
+#ifndef QMAT_GEMV_ROWS_MIN_SLICES
+#define QMAT_GEMV_ROWS_MIN_SLICES 256
+#endif
+
 template <class F, int R, int G, int D>
 hipError_t launch_fmt(const void* blocks, const float* x, float* y, int64_t M, int64_t K,
                       hipStream_t stream) {
   const int64_t ns = K / 32;
+  if (QMAT_GEMV_ROWS && ns >= QMAT_GEMV_ROWS_MIN_SLICES) {
+    constexpr int RR = QMAT_GEMV_ROW_R;
+    const int64_t grid = (M + kRowWaves * RR - 1) / (kRowWaves * RR);
+    const bool odd = F::kBytes != 144 && (ns & 1) != 0 && M > 1;
+    if (odd)
+      hipLaunchKernelGGL((gemv_rows_kernel<F, RR, true>), dim3((unsigned)grid),
+                         dim3(kRowWaves * kWave), 0, stream, static_cast<const uint8_t*>(blocks),
+                         x, y, M, (int)K);
+    else
+      hipLaunchKernelGGL((gemv_rows_kernel<F, RR, false>), dim3((unsigned)grid),
+                         dim3(kRowWaves * kWave), 0, stream, static_cast<const uint8_t*>(blocks),
+                         x, y, M, (int)K);
+    return hipGetLastError();
+  }
   int waves = (int)((ns + kWave - 1) / kWave);
   if (waves < 1) waves = 1;
   if (waves > kMaxStrips) waves = kMaxStrips;

@@ -175,7 +175,8 @@ def test_gemv_small_and_ragged(q, fmt):
 def test_gemv_one_hot_gives_the_column(q, fmt):
     rng = np.random.default_rng(300)
     for M, K, k in [(40, 2048, k) for k in (0, 15, 16, 31, 32, 1000, 2047)] + \
-                   [(70, 4096, k) for k in (0, 2047, 2048, 4095)]:
+                   [(70, 4096, k) for k in (0, 2047, 2048, 4095)] + \
+                   [(35, 11008, k) for k in (0, 4100, 11007)]:
         W = rng.normal(0, 0.02, (M, K)).astype(np.float32)
         B = oracle.quantize(fmt, W)
         Wd = oracle.dequant(fmt, B, M, K)
@@ -198,17 +199,18 @@ def test_gemv_one_hot_gives_the_column(q, fmt):
 def test_gemv_activation_range(q, fmt):
     """Per-32 power-of-two prescaling keeps any finite x in fp16 range."""
     rng = np.random.default_rng(400)
-    K = 4096
-    cases = [(M, name, scale) for M in (24, 70)
+    # K = 4096 and K = 11008 take the two GEMV kernels (rows of fewer or more
+    # than 256 slices)
+    cases = [(M, K, name, scale) for M, K in ((24, 4096), (70, 4096), (37, 11008))
              for name, scale in (("tiny", 1e-30), ("huge", 1e30), ("subnormal", 1e-40),
                                  ("mixed", None), ("binade-top", "top"))]
-    for M, name, scale in cases:
-        say(f"gemv x-range fmt={fmt} M={M} {name}")
+    for M, K, name, scale in cases:
+        say(f"gemv x-range fmt={fmt} M={M} K={K} {name}")
         W = rng.normal(0, 0.02, (M, K)).astype(np.float32)
         x = rng.normal(0, 1, K)
         if scale == "top":
             # every slice's maximum is positive and just below a power of two
-            # (the top of the 16-bit fixed-point range after prescaling)
+            # (the top of the fixed-point digit range after prescaling)
             x = rng.uniform(-0.9, 0.9, K)
             x[::32] = 1.0 - 2.0 ** -rng.integers(9, 24, K // 32)
             x *= np.repeat(2.0 ** rng.integers(-8, 8, K // 32), 32)
