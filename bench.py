@@ -107,7 +107,8 @@ def summarize_pmc(fetch_csv: str, write_csv: str):
     (the same copy kernel also serves the other tensor copies)."""
     fetch = _counter_rows(fetch_csv, "FETCH_SIZE")
     write = _counter_rows(write_csv, "WRITE_SIZE")
-    is_gemv = lambda r: "gemv_kernel" in r["Kernel_Name"] and "FmtQ4_0" in r["Kernel_Name"]
+    is_gemv = lambda r: ("gemv_kernel" in r["Kernel_Name"] or "gemv_rows_kernel" in r["Kernel_Name"]) \
+        and "FmtQ4_0" in r["Kernel_Name"]
     is_copy = lambda r: "copy" in r["Kernel_Name"].lower()
     kib = COPY_BYTES / 1024.0
     copy_ids = {r["Dispatch_Id"] for r in write
