@@ -127,15 +127,6 @@ __device__ __forceinline__ BlkLane blk_lane(uint32_t o, uint32_t par, int bytes)
   return l;
 }
 
-// Buffer resource over [base, base + bytes) for raw buffer loads (gfx9
-// descriptor: stride 0, 32-bit dword data format); lane offsets are 32-bit
-// and the per-stage offset is a scalar register.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const uint8_t* base, int64_t bytes) {
-  const uint32_t n = bytes < (int64_t)0xFFFFFFFF ? (uint32_t)bytes : 0xFFFFFFFFu;
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, (int)n,
-                                           0x00020000);
-}
-
 __device__ __forceinline__ void load_lane(__amdgpu_buffer_rsrc_t rs, uint32_t soff,
                                           const BlkLane& l, int bytes, u32x4& va, u32x4& vb,
                                           uint32_t& s2) {

@@ -6,11 +6,11 @@
 // is therefore built around the HBM stream of packed blocks, and its integer
 // work per block is kept small enough to hide under that stream.
 //
-// Work split. Two kernels share the arithmetic below. Rows of 256 slices or
-// more (K >= 8192) use gemv_rows_kernel: a workgroup of 16 waves owns 16
-// rows, one per wave; each strip of activations is converted once per
+// Work split. Two kernels share the arithmetic below. Rows of 256 to 512
+// slices (K = 8192 .. 16384) use gemv_rows_kernel: a workgroup of 16 waves
+// owns 16 rows, one per wave; the activations are converted once per
 // workgroup into LDS digit records shared by the 16 rows (see the kernel).
-// Shorter rows use gemv_kernel:
+// Other rows use gemv_kernel:
 //   * A workgroup owns G groups of R consecutive rows and all of K. Its waves
 //     split K into strips of 64 slices; lane l of a strip owns one
 //     32-element slice (one Q4_0/Q8_0 block, or one sub-block of a Q4_K
@@ -281,13 +281,18 @@ struct FmtQ4_0 {
   typedef NibAcc Acc;
   struct Raw {
     u32x4 v;
-    uint32_t s;
+    uint16_t s;  // widened where it is used, after the load has landed
   };
   __device__ static int64_t row_bytes(int K) { return (int64_t)(K >> 5) * 18; }
   __device__ static void prep(f32x4 (&v)[8], XP& xp) { prep_nib(v, xp, false); }
   __device__ static void load(const uint8_t* __restrict__ row, const BlockLane& L, Raw& r) {
     r.v = *reinterpret_cast<const u32x4_a4*>(row + L.o16);
     r.s = *reinterpret_cast<const uint16_t*>(row + L.o2);
+  }
+  // the same bytes through a buffer resource over the row
+  __device__ static void load(__amdgpu_buffer_rsrc_t rs, const BlockLane& L, Raw& r) {
+    r.v = __builtin_amdgcn_raw_buffer_load_b128(rs, L.o16, 0, 0);
+    r.s = __builtin_amdgcn_raw_buffer_load_b16(rs, L.o2, 0, 0);
   }
   // D * sum (c - 8) X (still to be scaled by 2^-s)
   __device__ static float apply(const Raw& r, const BlockLane& L, const XP& xp, int /*j*/,
@@ -310,7 +315,7 @@ struct FmtQ8_0 {
   typedef ByteAcc Acc;
   struct Raw {
     u32x4 v0, v1;
-    uint32_t s;
+    uint16_t s;
   };
   __device__ static int64_t row_bytes(int K) { return (int64_t)(K >> 5) * 34; }
   __device__ static void prep(f32x4 (&v)[8], XP& xp) { prep_byte(v, xp, false); }
@@ -318,6 +323,11 @@ struct FmtQ8_0 {
     r.v0 = *reinterpret_cast<const u32x4_a4*>(row + L.o16);
     r.v1 = *reinterpret_cast<const u32x4_a4*>(row + L.o16 + 16);
     r.s = *reinterpret_cast<const uint16_t*>(row + L.o2);
+  }
+  __device__ static void load(__amdgpu_buffer_rsrc_t rs, const BlockLane& L, Raw& r) {
+    r.v0 = __builtin_amdgcn_raw_buffer_load_b128(rs, L.o16, 0, 0);
+    r.v1 = __builtin_amdgcn_raw_buffer_load_b128(rs, L.o16 + 16u, 0, 0);
+    r.s = __builtin_amdgcn_raw_buffer_load_b16(rs, L.o2, 0, 0);
   }
   __device__ static float apply(const Raw& r, const BlockLane& L, const XP& xp, int /*j*/,
                                Acc& ac) {
@@ -354,6 +364,10 @@ struct FmtQ4_K {
   __device__ static void load(const uint8_t* __restrict__ row, const BlockLane& L, Raw& r) {
     r.h = *reinterpret_cast<const u32x4*>(row + L.o16);
     r.c = *reinterpret_cast<const u32x4*>(row + L.o2);
+  }
+  __device__ static void load(__amdgpu_buffer_rsrc_t rs, const BlockLane& L, Raw& r) {
+    r.h = __builtin_amdgcn_raw_buffer_load_b128(rs, L.o16, 0, 0);
+    r.c = __builtin_amdgcn_raw_buffer_load_b128(rs, L.o2, 0, 0);
   }
   __device__ static float apply(const Raw& r, const BlockLane& /*L*/, const XP& xp, int j,
                                Acc& ac) {
@@ -582,214 +596,148 @@ __global__ __launch_bounds__(kMaxStrips * kWave) void gemv_kernel(const uint8_t*
 }
 
 // -------------------------------------------------- GEMV, a row per wave --
-// A workgroup of kRowWaves waves owns kRowWaves rows, one per wave, and walks
-// K in strips of 64 slices (lane = slice). A strip's activations are
-// converted once per workgroup into digit records in LDS (four lanes per
-// slice, waves 0-3) and shared by all the rows. The next strip's weight
-// blocks and activations are requested while the current strip is used;
-// its records go to the other LDS buffer afterwards.
+// A workgroup of kRowWaves waves owns kRowWaves rows, one per wave, and all
+// of K (at most kRowMaxSlices slices, 8 strips of 64). LDS holds one 8 KB
+// slot per strip. At the start, wave w copies strip w of the activations
+// from memory into slot w (all copies ahead of any weight load), requests
+// the weight blocks of its row's first kD strips, and then converts the slot
+// in place into digit records (one lane per slice, as in gemv_kernel),
+// shared by all the rows, and raises the slot's ready flag. Each wave
+// streams its row strip by strip (lane = slice) and waits only for the flag
+// of the strip it is about to use, not for the whole workgroup: the
+// converting waves run at raised priority, and the blocks of kD strips stay
+// in flight in kD register buffers that an unrolled loop rotates.
+//
+// Every weight load is issued on every lane and path: lanes out of range
+// read past the end of their buffer resource, which returns zeros without a
+// memory access. Zero blocks have scale 0 and the records of the padding
+// slices have inv = 0, so those lanes add exactly 0 and need no branch. This
+// keeps the compiler's load counting exact (a load skipped on some path
+// makes every later wait a full one).
 #ifndef QMAT_GEMV_ROW_WAVES
 #define QMAT_GEMV_ROW_WAVES 16
 #define QMAT_GEMV_ROW_R 1
 #endif
+// strips of weight blocks in flight per wave (measured best at 4096x11008;
+// more in flight lengthens the queues that the slowest workgroups wait in)
+#ifndef QMAT_GEMV_ROW_DEPTH_Q4_0
+#define QMAT_GEMV_ROW_DEPTH_Q4_0 1
+#define QMAT_GEMV_ROW_DEPTH_Q8_0 1
+#define QMAT_GEMV_ROW_DEPTH_Q4_K 2
+#endif
 constexpr int kRowWaves = QMAT_GEMV_ROW_WAVES;
-static_assert(kRowWaves >= 4, "waves 0-3 convert the 64 slices of a strip");
+constexpr int kRowSlot = 8192;  // one strip of fp32 activations
+// A wait for a ready flag gives up after this many polls (each with a short
+// sleep, some tens of milliseconds in all) instead of hanging the device if
+// a flag were never raised; the flags are raised unconditionally.
+constexpr int kRowSpinLimit = 1 << 20;
 
-// max over the four lanes of a quad (quad_perm [1,0,3,2] then [2,3,0,1])
-__device__ __forceinline__ float quad_max(float v) {
-  v = __builtin_fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
-                                                     0, __builtin_bit_cast(int, v), 0xB1, 0xF,
-                                                     0xF, false)));
-  return __builtin_fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
-                                                          0, __builtin_bit_cast(int, v), 0x4E,
-                                                          0xF, 0xF, false)));
+// LDS flags as relaxed workgroup-scope atomics: read afresh on every poll
+// but, unlike volatile accesses, without a wait for all outstanding memory
+// operations; the ordering with the records comes from explicit waits.
+__device__ __forceinline__ void flag_set(int* f, int v) {
+  __hip_atomic_store(f, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
-
-__device__ __forceinline__ int32_t quad_sum(int32_t v) {
-  v += __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);
-  return v + __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);
+__device__ __forceinline__ int flag_get(int* f) {
+  return __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
+constexpr int kRowMaxSlices = 8 * kWave;  // 8 slots: the 64 KB a workgroup may allocate
+static_assert(kRowWaves >= 8, "wave w converts strip w");
 
-// The slice scale of slice_scale() computed by a quad from its 8 elements
-// per lane (va, vb are rescaled in place like v there).
-__device__ __forceinline__ float quad_scale(f32x4& va, f32x4& vb, float lim, float& inv) {
-  float am = max3f(fabsf(va.x), fabsf(va.y), fabsf(va.z));
-  am = max3f(am, fabsf(va.w), fabsf(vb.x));
-  am = max3f(am, fabsf(vb.y), fabsf(vb.z));
-  am = __builtin_fmaxf(am, fabsf(vb.w));
-  am = quad_max(am);
-  int e;
-  frexpf(am, &e);
-  int s = 19 - e;
-  if (ldexpf(am, s) >= lim + 0.5f) s -= 1;
-  s = min(s, 149);
-  inv = ldexpf(1.0f, -s);
-  if (__builtin_expect(s > 120, 0)) {
-    va = f32x4{ldexpf(va.x, 64), ldexpf(va.y, 64), ldexpf(va.z, 64), ldexpf(va.w, 64)};
-    vb = f32x4{ldexpf(vb.x, 64), ldexpf(vb.y, 64), ldexpf(vb.z, 64), ldexpf(vb.w, 64)};
-    s -= 64;
-  }
-  return ldexpf(1.0f, s);
-}
-
-// LDS image of a strip's converted activations. Word t of digit i of
-// slice l sits at d[i][l][t], so a lane reads its slice's digit words with
-// one 16-byte load each and the quads write 64 consecutive words.
-struct XNibLds {
-  uint32_t d[5][kWave][4];
-  float inv[kWave];
-  int32_t sx[kWave];
-};
-
-// xl / xh / xt words 0-3 and 4-7 of slice l at w[j][h][l]
-struct XByteLds {
-  uint32_t w[3][2][kWave][4];
-  float inv[kWave];
-};
-
-__device__ __forceinline__ void conv_nib(f32x4 va, f32x4 vb, int sl, int k, bool want_sum,
-                                         XNibLds& o) {
-  float inv;
-  const float scale = quad_scale(va, vb, kNibLim, inv);
-  const float magic = kMagicF + (float)kNibBias;
-  uint32_t aL, aH, aT, bL, bH, bT, d[2];
-  bias20(va, scale, magic, aL, aH, aT);
-  bias20(vb, scale, magic, bL, bH, bT);
-  uint32_t w[5];
-  nib_digits(aL, bL, d);
-  w[0] = d[0];
-  w[1] = d[1];
-  nib_digits(aH, bH, d);
-  w[2] = d[0];
-  w[3] = d[1];
-  nib_digits(aT, bT, d);
-  w[4] = d[0];
+// Records of the 64 slices of a slot (they replace the activations). Nibble
+// digits: word t of digit i of slice l at byte 1024 i + 16 l + 4 t (a lane
+// reads consecutive 16-byte groups), inv at 5120 + 4 l, sx at 5376 + 4 l.
+// Byte digits: words 4h..4h+3 of kind j (xl, xh, xt) at 1024 (2j + h) +
+// 16 l, inv at 6144 + 4 l.
+__device__ __forceinline__ void put_rec(uint8_t* slot, int l, const XNib& xp, bool sum) {
 #pragma unroll
-  for (int i = 0; i < 5; ++i) o.d[i][sl][k] = w[i];
-  int32_t sx = 0;
-  if (want_sum) {
-    uint32_t a[5];
-#pragma unroll
-    for (int i = 0; i < 5; ++i) a[i] = (uint32_t)sdot8(w[i], 0x11111111u, 0);
-    sx = quad_sum((int32_t)((((a[4] * 16u + a[3]) * 16u + a[2]) * 16u + a[1]) * 16u + a[0]));
-  }
-  if (k == 0) {
-    o.inv[sl] = inv;
-    o.sx[sl] = sx;
-  }
+  for (int i = 0; i < 5; ++i)
+    *reinterpret_cast<u32x4*>(slot + 1024 * i + 16 * l) =
+        u32x4{xp.d[i][0], xp.d[i][1], xp.d[i][2], xp.d[i][3]};
+  reinterpret_cast<float*>(slot + 5120)[l] = xp.inv;
+  if (sum) reinterpret_cast<int32_t*>(slot + 5376)[l] = xp.sx;
 }
 
-__device__ __forceinline__ void read_nib(const XNibLds& o, int l, XNib& xp) {
+__device__ __forceinline__ void get_rec(const uint8_t* slot, int l, XNib& xp, bool sum) {
 #pragma unroll
   for (int i = 0; i < 5; ++i) {
-    const u32x4 v = *reinterpret_cast<const u32x4*>(&o.d[i][l][0]);
+    const u32x4 v = *reinterpret_cast<const u32x4*>(slot + 1024 * i + 16 * l);
     xp.d[i][0] = v.x;
     xp.d[i][1] = v.y;
     xp.d[i][2] = v.z;
     xp.d[i][3] = v.w;
   }
-  xp.inv = o.inv[l];
-  xp.sx = o.sx[l];
+  xp.inv = reinterpret_cast<const float*>(slot + 5120)[l];
+  xp.sx = sum ? reinterpret_cast<const int32_t*>(slot + 5376)[l] : 0;
 }
 
-__device__ __forceinline__ void conv_byte(f32x4 va, f32x4 vb, int sl, int k, bool /*want_sum*/,
-                                          XByteLds& o) {
-  float inv;
-  const float scale = quad_scale(va, vb, kByteLim, inv);
-  const float magic = kMagicF + (float)kByteBias;
-  uint32_t lo, hi, top;
-  bias20(va, scale, magic, lo, hi, top);
-  o.w[0][0][sl][k] = lo ^ 0x80808080u;
-  o.w[1][0][sl][k] = hi ^ 0x80808080u;
-  o.w[2][0][sl][k] = ((top & 0x0F0F0F0Fu) + 0x78787878u) ^ 0x80808080u;
-  bias20(vb, scale, magic, lo, hi, top);
-  o.w[0][1][sl][k] = lo ^ 0x80808080u;
-  o.w[1][1][sl][k] = hi ^ 0x80808080u;
-  o.w[2][1][sl][k] = ((top & 0x0F0F0F0Fu) + 0x78787878u) ^ 0x80808080u;
-  if (k == 0) o.inv[sl] = inv;
+__device__ __forceinline__ void put_rec(uint8_t* slot, int l, const XByte& xp, bool /*sum*/) {
+  const uint32_t* src[3] = {xp.xl, xp.xh, xp.xt};
+#pragma unroll
+  for (int j = 0; j < 3; ++j)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      *reinterpret_cast<u32x4*>(slot + 1024 * (2 * j + h) + 16 * l) =
+          u32x4{src[j][4 * h], src[j][4 * h + 1], src[j][4 * h + 2], src[j][4 * h + 3]};
+  reinterpret_cast<float*>(slot + 6144)[l] = xp.inv;
 }
 
-__device__ __forceinline__ void read_byte(const XByteLds& o, int l, XByte& xp) {
+__device__ __forceinline__ void get_rec(const uint8_t* slot, int l, XByte& xp, bool /*sum*/) {
   uint32_t* dst[3] = {xp.xl, xp.xh, xp.xt};
 #pragma unroll
   for (int j = 0; j < 3; ++j)
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(&o.w[j][h][l][0]);
+      const u32x4 v = *reinterpret_cast<const u32x4*>(slot + 1024 * (2 * j + h) + 16 * l);
       dst[j][4 * h + 0] = v.x;
       dst[j][4 * h + 1] = v.y;
       dst[j][4 * h + 2] = v.z;
       dst[j][4 * h + 3] = v.w;
     }
-  xp.inv = o.inv[l];
+  xp.inv = reinterpret_cast<const float*>(slot + 6144)[l];
   xp.sx = 0;
 }
 
-template <class XP>
-struct XLds;
-template <>
-struct XLds<XNib> {
-  typedef XNibLds T;
-};
-template <>
-struct XLds<XByte> {
-  typedef XByteLds T;
-};
-
-__device__ __forceinline__ void conv_slice(f32x4 va, f32x4 vb, int sl, int k, bool want_sum,
-                                           XNibLds& o) {
-  conv_nib(va, vb, sl, k, want_sum, o);
-}
-__device__ __forceinline__ void conv_slice(f32x4 va, f32x4 vb, int sl, int k, bool want_sum,
-                                           XByteLds& o) {
-  conv_byte(va, vb, sl, k, want_sum, o);
-}
-__device__ __forceinline__ void read_slice(const XNibLds& o, int l, XNib& xp) { read_nib(o, l, xp); }
-__device__ __forceinline__ void read_slice(const XByteLds& o, int l, XByte& xp) {
-  read_byte(o, l, xp);
-}
-
-
-template <class F, int R, bool kOdd>
+template <class F, int R, int kD, bool kOdd>
 __global__ __launch_bounds__(kRowWaves * kWave) void gemv_rows_kernel(
     const uint8_t* __restrict__ B, const float* __restrict__ x, float* __restrict__ y,
     int64_t M, int K) {
-  typedef typename XLds<typename F::XP>::T XL;
-  __shared__ __attribute__((aligned(16))) XL xl[2];
+  extern __shared__ __attribute__((aligned(16))) uint8_t slots[];
+  __shared__ int ready[8];  // strip s's records are in slot s when ready[s] != 0
+  typedef typename F::XP XP;
   constexpr bool kQ4K = F::kBytes == 144;
+  constexpr uint32_t kOut = 0x80000000u;  // an offset past the end of any row
   const int lane = threadIdx.x & 63;
-  const int wv = threadIdx.x >> 6;
+  const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int ns = K >> 5;
   const int nstrips = (ns + kWave - 1) / kWave;
   const int64_t rb = F::row_bytes(K);
   const int64_t m0 = ((int64_t)blockIdx.x * kRowWaves + wv) * R;  // this wave's first row
   // with an odd row stride, row m starts at 2 (m & 1) mod 4; a row past M
   // re-reads the last row of the same parity (M >= 2 then)
-  const uint8_t* rows[R];
+  __amdgpu_buffer_rsrc_t rrs[R];
   uint32_t par[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int64_t m = m0 + r;
     par[r] = kOdd ? (uint32_t)(m & 1) : 0u;
     const int64_t mr = m < M ? m : (kOdd ? M - 1 - ((M - 1 - (int64_t)par[r]) & 1) : M - 1);
-    rows[r] = B + mr * rb;
+    rrs[r] = make_rsrc(B + mr * rb, rb);
   }
 
-  // activation conversion: waves 0-3, slice 16 wv + lane / 4, part lane % 4
-  const bool conv = wv < 4;
-  const int csl = 16 * wv + (lane >> 2), ck = lane & 3;
-  f32x4 va = {0.0f, 0.0f, 0.0f, 0.0f}, vb = va;
-  auto load_x = [&](int st) {
-    const int sl = st * kWave + csl;
-    if (conv && sl < ns) {
-      const float* xs = x + (int64_t)sl * 32 + 4 * ck;
-      va = *reinterpret_cast<const f32x4*>(xs);
-      vb = *reinterpret_cast<const f32x4*>(xs + 16);
-    }
-  };
-  auto conv_x = [&](int st, XL& dst) {
-    if (conv && st * kWave + csl < ns) conv_slice(va, vb, csl, ck, kQ4K, dst);
-  };
+  // LDS holds whatever the last workgroup left: clear the flags first
+  if (threadIdx.x < 8) flag_set(&ready[threadIdx.x], 0);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+
+  // strip wv of the activations into slot wv, first among this wave's loads
+  const bool conv = wv < nstrips;
+  uint8_t* const own = slots + wv * kRowSlot;
+  if (conv) __builtin_amdgcn_s_setprio(2);
+  if (conv) x_to_lds(x + (int64_t)wv * kWave * 32, min(ns - wv * kWave, kWave), own, lane);
+  // every wave's weight loads queue behind all of the copies
+  asm volatile("s_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+
   auto lane_of = [&](int st, uint32_t p) {
     const int j = st * kWave + lane;
     BlockLane L;
@@ -804,44 +752,79 @@ __global__ __launch_bounds__(kRowWaves * kWave) void gemv_rows_kernel(
     }
     return L;
   };
-  typename F::Raw nxt[R];
-  auto load_w = [&](int st) {
-    if (st * kWave + lane < ns) {
+  typename F::Raw wb[kD][R];
+  auto load_w = [&](int st, typename F::Raw (&dst)[R]) {
+    const bool ok = st < nstrips && st * kWave + lane < ns;
 #pragma unroll
-      for (int r = 0; r < R; ++r) F::load(rows[r], lane_of(st, par[r]), nxt[r]);
+    for (int r = 0; r < R; ++r) {
+      BlockLane L = lane_of(st, par[r]);
+      if (!ok) L.o16 = L.o2 = kOut;
+      F::load(rrs[r], L, dst[r]);
     }
   };
-
-  if (nstrips > 0) {
-    load_x(0);
-    load_w(0);
-    conv_x(0, xl[0]);
-    if (1 < nstrips) load_x(1);
+  // strip by strip, in the order the loop below counts them
+#pragma unroll
+  for (int u = 0; u < kD; ++u) {
+    load_w(u, wb[u]);
+    __builtin_amdgcn_sched_barrier(0);
   }
-  __syncthreads();
+
+  // Loads complete in issue order: with only the weight loads left, the
+  // copy has landed. Every wave waits (a no-op without a copy), so that on
+  // no path does the compiler see copies into LDS still in flight, which
+  // would make it wait for all loads before each LDS read in the loop.
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm<kD * R * F::kLoads>());
+  __builtin_amdgcn_sched_barrier(0);
+  if (conv) {
+    f32x4 v[8];
+    x_from_lds(own, lane, v);
+    XP xp;
+    F::prep(v, xp);
+    if (wv * kWave + lane >= ns) xp.inv = 0.0f;  // padding slice
+    put_rec(own, lane, xp, kQ4K);
+    // records first (LDS completes a wave's accesses in order once waited
+    // for), then the flag; the memory clobbers keep the compiler's LDS
+    // accesses on their side
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (lane == 0) flag_set(&ready[wv], 1);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_setprio(0);
+  }
+
   typename F::Acc ac = {};
   float part[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) part[r] = 0.0f;
-  for (int st = 0; st < nstrips; ++st) {
-    typename F::Raw cur[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) cur[r] = nxt[r];
-    if (st + 1 < nstrips) load_w(st + 1);
+  // strip st from buffer w, then (if `next`) strip st + kD into w
+  auto step = [&](int st, typename F::Raw (&w)[R], bool next) {
     const int j = st * kWave + lane;
-    if (j < ns) {
-      typename F::XP xp;
-      read_slice(xl[st & 1], lane, xp);
+    for (int n = 0; flag_get(&ready[st]) == 0 && n < kRowSpinLimit; ++n)
+      __builtin_amdgcn_s_sleep(1);
+    asm volatile("" ::: "memory");
+    XP xp;
+    get_rec(slots + st * kRowSlot, lane, xp, kQ4K);
 #pragma unroll
-      for (int r = 0; r < R; ++r)
-        part[r] = fmaf(F::apply(cur[r], lane_of(st, par[r]), xp, j, ac), xp.inv, part[r]);
-    }
-    if (st + 1 < nstrips) {
-      conv_x(st + 1, xl[(st + 1) & 1]);
-      if (st + 2 < nstrips) load_x(st + 2);
-    }
-    __syncthreads();
+    for (int r = 0; r < R; ++r)
+      part[r] = fmaf(F::apply(w[r], lane_of(st, par[r]), xp, j, ac), xp.inv, part[r]);
+    if (next) load_w(st + kD, w);
+    // the next strip's arithmetic must not move above these loads
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // Whole rounds of kD strips while every strip they request exists:
+  // no path through this loop skips a load, so each wait counts exactly the
+  // loads after it. The last kD to 2 kD - 1 strips request only what
+  // exists (their waits may be full ones: nothing is left to overlap).
+  int s0 = 0;
+  for (; s0 + 2 * kD <= nstrips; s0 += kD) {
+#pragma unroll
+    for (int u = 0; u < kD; ++u) step(s0 + u, wb[u], true);
   }
+#pragma unroll
+  for (int u = 0; u < kD; ++u)
+    if (s0 + u < nstrips) step(s0 + u, wb[u], s0 + u + kD < nstrips);
+#pragma unroll
+  for (int u = 0; u + 1 < kD; ++u)
+    if (s0 + kD + u < nstrips) step(s0 + kD + u, wb[u], false);
   constexpr int kShift = 6 - log2i<R>();
   const int r = (lane >> kShift) & (R - 1);
   const float sum = wave_reduce_rows<R>(part, lane);
@@ -864,29 +847,30 @@ __global__ __launch_bounds__(kRowWaves * kWave) void gemv_rows_kernel(
 #ifndef QMAT_GEMV_ROWS
 #define QMAT_GEMV_ROWS 1
 #endif
-// rows of at least this many slices (4 strips) go to the row-per-wave kernel;
-// shorter rows have too few strips to hide its per-strip conversion and
-// barrier
+// rows of this many slices (4 strips) up to kRowMaxSlices go to the
+// row-per-wave kernel; shorter rows have too few strips to hide its
+// conversion of the activations in front of the stream
 #ifndef QMAT_GEMV_ROWS_MIN_SLICES
 #define QMAT_GEMV_ROWS_MIN_SLICES 256
 #endif
 
-template <class F, int R, int G, int D>
+template <class F, int R, int G, int D, int RD>
 hipError_t launch_fmt(const void* blocks, const float* x, float* y, int64_t M, int64_t K,
                       hipStream_t stream) {
   const int64_t ns = K / 32;
-  if (QMAT_GEMV_ROWS && ns >= QMAT_GEMV_ROWS_MIN_SLICES) {
+  if (QMAT_GEMV_ROWS && ns >= QMAT_GEMV_ROWS_MIN_SLICES && ns <= kRowMaxSlices) {
     constexpr int RR = QMAT_GEMV_ROW_R;
     const int64_t grid = (M + kRowWaves * RR - 1) / (kRowWaves * RR);
+    const size_t lds = (size_t)((ns + kWave - 1) / kWave) * kRowSlot;
     const bool odd = F::kBytes != 144 && (ns & 1) != 0 && M > 1;
     if (odd)
-      hipLaunchKernelGGL((gemv_rows_kernel<F, RR, true>), dim3((unsigned)grid),
-                         dim3(kRowWaves * kWave), 0, stream, static_cast<const uint8_t*>(blocks),
-                         x, y, M, (int)K);
+      hipLaunchKernelGGL((gemv_rows_kernel<F, RR, RD, true>), dim3((unsigned)grid),
+                         dim3(kRowWaves * kWave), lds, stream,
+                         static_cast<const uint8_t*>(blocks), x, y, M, (int)K);
     else
-      hipLaunchKernelGGL((gemv_rows_kernel<F, RR, false>), dim3((unsigned)grid),
-                         dim3(kRowWaves * kWave), 0, stream, static_cast<const uint8_t*>(blocks),
-                         x, y, M, (int)K);
+      hipLaunchKernelGGL((gemv_rows_kernel<F, RR, RD, false>), dim3((unsigned)grid),
+                         dim3(kRowWaves * kWave), lds, stream,
+                         static_cast<const uint8_t*>(blocks), x, y, M, (int)K);
     return hipGetLastError();
   }
   int waves = (int)((ns + kWave - 1) / kWave);
@@ -1211,13 +1195,16 @@ hipError_t launch_gemv(int fmt, const void* blocks, const float* x, float* y, in
   if (M == 0) return hipSuccess;
   switch (fmt) {
     case kFmtQ4_0:
-      return launch_fmt<FmtQ4_0, QMAT_GEMV_R_Q4_0, QMAT_GEMV_G_Q4_0, QMAT_GEMV_D_Q4_0>(
+      return launch_fmt<FmtQ4_0, QMAT_GEMV_R_Q4_0, QMAT_GEMV_G_Q4_0, QMAT_GEMV_D_Q4_0,
+                        QMAT_GEMV_ROW_DEPTH_Q4_0>(
           blocks, x, y, M, K, stream);
     case kFmtQ8_0:
-      return launch_fmt<FmtQ8_0, QMAT_GEMV_R_Q8_0, QMAT_GEMV_G_Q8_0, QMAT_GEMV_D_Q8_0>(
+      return launch_fmt<FmtQ8_0, QMAT_GEMV_R_Q8_0, QMAT_GEMV_G_Q8_0, QMAT_GEMV_D_Q8_0,
+                        QMAT_GEMV_ROW_DEPTH_Q8_0>(
           blocks, x, y, M, K, stream);
     default:
-      return launch_fmt<FmtQ4_K, QMAT_GEMV_R_Q4_K, QMAT_GEMV_G_Q4_K, QMAT_GEMV_D_Q4_K>(
+      return launch_fmt<FmtQ4_K, QMAT_GEMV_R_Q4_K, QMAT_GEMV_G_Q4_K, QMAT_GEMV_D_Q4_K,
+                        QMAT_GEMV_ROW_DEPTH_Q4_K>(
           blocks, x, y, M, K, stream);
   }
 }

@@ -53,6 +53,16 @@ __device__ __forceinline__ float dot2(uint32_t a, half2_t b, float c) {
   return __builtin_amdgcn_fdot2(as_half2(a), b, c, false);
 }
 
+// Buffer resource over [base, base + bytes) for raw buffer loads (gfx9
+// descriptor: stride 0, 32-bit dword data format). Lane offsets are 32-bit;
+// a load at or past `bytes` returns zeros without a memory access, which
+// lets a kernel issue the same loads on every lane and path.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const uint32_t n = bytes < (int64_t)0xFFFFFFFF ? (uint32_t)bytes : 0xFFFFFFFFu;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n,
+                                           0x00020000);
+}
+
 __device__ __forceinline__ float shfl_xor_f(float v, int mask) {
   return __shfl_xor(v, mask, kWave);
 }

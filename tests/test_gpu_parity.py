@@ -159,10 +159,14 @@ def gemv_case(q, fmt, W, x):
 def test_gemv_small_and_ragged(q, fmt):
     rng = np.random.default_rng(200 + fmt)
     shapes = [(1, 256), (3, 512), (17, 2048), (31, 11008 if fmt == 2 else 32 * 345), (70, 4096),
-              (129, 1024), (9, 256 * 40), (6, 256 * 72), (64, 256 * 9), (200, 256 * 43)]
+              (129, 1024), (9, 256 * 40), (6, 256 * 72), (64, 256 * 9), (200, 256 * 43),
+              # rows of 256..512 slices take the row-per-wave kernel: its first
+              # and last sizes, an odd strip count, and just past its limit
+              (33, 8192), (20, 16384), (18, 256 * 33), (7, 256 * 65)]
     if fmt != 2:
         shapes += [(1, 32), (5, 32 * 37), (2, 64), (40, 32 * 1001), (100, 32 * 345),
-                   (65, 32 * 1001), (130, 32 * 65)]
+                   (65, 32 * 1001), (130, 32 * 65), (19, 32 * 257), (21, 32 * 511),
+                   (7, 32 * 513)]
     for M, K in shapes:
         say(f"gemv fmt={fmt} M={M} K={K}")
         W = mixed_matrix(rng, M, K) if M > 2 else rng.normal(0, 0.02, (M, K)).astype(np.float32)
