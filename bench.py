@@ -43,6 +43,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -91,8 +92,13 @@ def rel_l2(a, ref):
 
 
 def source_hash(path: str) -> str:
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of a C/HIP source's code: comments and blank space removed, so
+    that editing a comment does not mark the kernel as changed."""
+    with open(path, encoding="utf-8") as f:
+        text = f.read()
+    code = re.sub(r"//[^\n]*|/\*.*?\*/", " ", text, flags=re.S)
+    code = " ".join(code.split())
+    return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
 # ------------------------------------------------------------------ counters
