@@ -8,7 +8,7 @@ does, and this package never imports the product path.
 The arithmetic lives in ``qmat_oracle.c`` (plain C, fp64 accumulation,
 IEEE fp32 quantizers); this file only marshals numpy arrays. Every function
 cites its source passage in the C file. Format ids: 0 = Q4_0, 1 = Q8_0,
-2 = Q4_K-style.
+2 = Q4_K-style, 3 = Q6_K-style.
 """
 from __future__ import annotations
 
@@ -22,8 +22,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "qmat_oracle.c")
 LIB = os.path.join(HERE, "liboracle.so")
 
-Q4_0, Q8_0, Q4_K = 0, 1, 2
-FORMATS = {"q4_0": Q4_0, "q8_0": Q8_0, "q4_k": Q4_K}
+Q4_0, Q8_0, Q4_K, Q6_K = 0, 1, 2, 3
+FORMATS = {"q4_0": Q4_0, "q8_0": Q8_0, "q4_k": Q4_K, "q6_k": Q6_K}
 
 CFLAGS = ["-std=c11", "-O2", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
           "-fno-fast-math", "-fexcess-precision=standard", "-Wall", "-Wextra"]

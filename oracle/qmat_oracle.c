@@ -26,7 +26,12 @@
  * offset 8; Q8_0 scale amax/127; round half away from zero; fp32→fp16 round
  * to nearest even keeping subnormals; codes from the stored (rounded) scale;
  * an all-zero block gets the zero code; the Q4_K field packing and
- * min-offset rule as written below (this library's own layout).
+ * min-offset rule as written below (this library's own layout); the Q6_K
+ * superblock as sixteen 16-weight sub-blocks with int8 scales (the only
+ * k-quant split that gives the 210 bytes per 256 weights implied by
+ * [LC05]'s 121.71 MiB q6_K embedding: eight 32-weight sub-blocks with 6-bit
+ * scales and mins give 208, with int8 scales alone 202), symmetric codes
+ * under scale amax/31, and this library's own byte order.
  *
  * Parity pins (tests/test_oracle_pins.py): fp16 codec against numpy on every
  * half and on a float32 sweep; block sizes against the sizes the pages print
@@ -34,8 +39,9 @@
  * hand-built golden blocks for byte layout and nibble order; the round-trip
  * bound scale/2; brute-force code optimality; idempotence; exact-grid
  * inputs; one-hot and all-ones activations; brute-force 4×64 products.
- * The Q4_K code arithmetic has no value printed on the pages to pin it to:
- * beyond layout, round-trip and optimality it is "parity unpinned".
+ * The Q4_K and Q6_K code arithmetic has no value printed on the pages to
+ * pin it to: beyond size, layout, round-trip, optimality and exact-grid
+ * inputs it is "parity unpinned".
  *
  * Arithmetic: quantizers use IEEE fp32 with correctly rounded + - * / and no
  * contraction (build with -ffp-contract=off); dequantization and every
@@ -49,7 +55,7 @@
 #include <omp.h>
 #endif
 
-enum { ORC_Q4_0 = 0, ORC_Q8_0 = 1, ORC_Q4_K = 2 };
+enum { ORC_Q4_0 = 0, ORC_Q8_0 = 1, ORC_Q4_K = 2, ORC_Q6_K = 3 };
 
 /* ---------------------------------------------------------------- fp16 -- */
 
@@ -115,12 +121,15 @@ void oracle_f16_to_f64_array(const uint16_t *in, double *out, int64_t n) {
 
 /* [LCHW]: Q4_0 block = 32 weights, 18 bytes. [LC05 table]: Q8_0 groups 32
  * weights under one fp16 scale with 8-bit values (34 bytes); k-quants use a
- * 256-weight superblock (144 bytes in this layout: 2+2+12+128). */
+ * 256-weight superblock (Q4_K 144 bytes in this layout: 2+2+12+128; Q6_K
+ * 210 bytes, [LC05] section 量化类型 and the 121.71 MiB embedding of section
+ * KV Cache 类型: 2 + 8 groups of (2 scales + 16 + 8 code bytes)). */
 int64_t oracle_block_elems(int fmt) {
   switch (fmt) {
     case ORC_Q4_0: return 32;
     case ORC_Q8_0: return 32;
     case ORC_Q4_K: return 256;
+    case ORC_Q6_K: return 256;
     default: return 0;
   }
 }
@@ -130,6 +139,7 @@ int64_t oracle_block_bytes(int fmt) {
     case ORC_Q4_0: return 2 + 16;
     case ORC_Q8_0: return 2 + 32;
     case ORC_Q4_K: return 2 + 2 + 12 + 128;
+    case ORC_Q6_K: return 2 + 8 * (2 + 16 + 8);
     default: return 0;
   }
 }
@@ -258,6 +268,70 @@ static void quant_q4_k_block(const float *x, uint8_t *blk) {
   }
 }
 
+/* Q6_K-style quantizer, one superblock of 256 ([LC05] section 量化类型:
+ * 256-weight superblock whose sub-block scales are themselves quantized;
+ * Q6_K is the near-lossless 6-bit member). Sub-block j is the 16 weights
+ * 16j..16j+15. Steps in order:
+ *   1. s_j = amax_j / 31 (symmetric: codes -31..31 around zero)
+ *   2. d = max s_j / 127, stored as fp16
+ *   3. sc_j = rnd(s_j / D), clamped to [0, 127] (int8)
+ *   4. S_j = D * sc_j (exact in fp32)
+ *   5. q_i = clamp(rnd(x_i / S_j), -32, 31), stored as the 6-bit code q+32
+ * Byte order: fp16 d, then for each 32-weight group g = 0..7 (sub-blocks
+ * 2g and 2g+1): sc_2g, sc_2g+1 as int8; 16 bytes whose byte t holds the
+ * low 4 bits of code 32g+t (low nibble) and of code 32g+16+t (high
+ * nibble); two little-endian 32-bit words H0, H1 where bits 2w..2w+1 of
+ * byte b of H0 are the high 2 bits of code 32g+4w+b, and of H1 those of
+ * code 32g+16+4w+b. */
+static void quant_q6_k_block(const float *x, uint8_t *blk) {
+  float s[16];
+  for (int j = 0; j < 16; ++j) {
+    float amax = 0.0f;
+    for (int i = 0; i < 16; ++i) {
+      float a = fabsf(x[16 * j + i]);
+      if (a > amax) amax = a;
+    }
+    s[j] = amax / 31.0f;
+  }
+  float smax = 0.0f;
+  for (int j = 0; j < 16; ++j)
+    if (s[j] > smax) smax = s[j];
+  float d = smax / 127.0f;
+  uint16_t hd = oracle_f32_to_f16(d);
+  float D = oracle_f16_to_f32(hd);
+  int sc[16];
+  uint8_t code[256];
+  for (int j = 0; j < 16; ++j) {
+    sc[j] = (D == 0.0f) ? 0 : (int)clampf(rnd(s[j] / D), 0.0f, 127.0f);
+    float S = D * (float)sc[j];
+    for (int i = 0; i < 16; ++i) {
+      int q = 0;
+      if (S != 0.0f) q = (int)clampf(rnd(x[16 * j + i] / S), -32.0f, 31.0f);
+      code[16 * j + i] = (uint8_t)(q + 32);
+    }
+  }
+  put_f16(blk, hd);
+  for (int g = 0; g < 8; ++g) {
+    uint8_t *grp = blk + 2 + 26 * g;
+    const uint8_t *c = code + 32 * g;
+    int8_t sa = (int8_t)sc[2 * g], sb = (int8_t)sc[2 * g + 1];
+    memcpy(grp, &sa, 1);
+    memcpy(grp + 1, &sb, 1);
+    for (int t = 0; t < 16; ++t)
+      grp[2 + t] = (uint8_t)((c[t] & 15) | ((c[16 + t] & 15) << 4));
+    uint32_t h0 = 0, h1 = 0;
+    for (int w = 0; w < 4; ++w)
+      for (int b = 0; b < 4; ++b) {
+        h0 |= (uint32_t)(c[4 * w + b] >> 4) << (8 * b + 2 * w);
+        h1 |= (uint32_t)(c[16 + 4 * w + b] >> 4) << (8 * b + 2 * w);
+      }
+    for (int b = 0; b < 4; ++b) {
+      grp[18 + b] = (uint8_t)(h0 >> (8 * b));
+      grp[22 + b] = (uint8_t)(h1 >> (8 * b));
+    }
+  }
+}
+
 /* Quantize a [rows][K] fp32 matrix into rows*(K/block_elems) blocks, row
  * after row. Returns 0, or -1 for an unknown format or a ragged K. */
 int oracle_quantize(int fmt, const float *W, uint8_t *out, int64_t rows,
@@ -272,7 +346,8 @@ int oracle_quantize(int fmt, const float *W, uint8_t *out, int64_t rows,
       uint8_t *blk = out + (r * nb + b) * bb;
       if (fmt == ORC_Q4_0) quant_q4_0_block(x, blk);
       else if (fmt == ORC_Q8_0) quant_q8_0_block(x, blk);
-      else quant_q4_k_block(x, blk);
+      else if (fmt == ORC_Q4_K) quant_q4_k_block(x, blk);
+      else quant_q6_k_block(x, blk);
     }
   }
   return 0;
@@ -290,7 +365,16 @@ static int field6(const uint8_t *p, int f) {
   return v;
 }
 
-/* Dequantize one block into fp64 (exact for all three formats). */
+/* Code e (0..31) of a Q6_K group: low 4 bits from the nibble bytes, high
+ * 2 bits from H0 (e < 16) or H1 (layout at quant_q6_k_block). */
+static int code6(const uint8_t *grp, int e) {
+  int half = e >> 4, r = e & 15, t = r, w = r >> 2, b = r & 3;
+  int lo = half ? (grp[2 + t] >> 4) : (grp[2 + t] & 15);
+  int hi = (grp[18 + 4 * half + b] >> (2 * w)) & 3;
+  return lo | (hi << 4);
+}
+
+/* Dequantize one block into fp64 (exact for all four formats). */
 static void dequant_block(int fmt, const uint8_t *blk, double *w) {
   if (fmt == ORC_Q4_0) {
     double D = oracle_f16_to_f64(get_f16(blk));
@@ -305,6 +389,16 @@ static void dequant_block(int fmt, const uint8_t *blk, double *w) {
       int8_t q;
       memcpy(&q, blk + 2 + i, 1);
       w[i] = D * (double)q;
+    }
+  } else if (fmt == ORC_Q6_K) {
+    double D = oracle_f16_to_f64(get_f16(blk));
+    for (int g = 0; g < 8; ++g) {
+      const uint8_t *grp = blk + 2 + 26 * g;
+      for (int e = 0; e < 32; ++e) {
+        int8_t sc;
+        memcpy(&sc, grp + (e >> 4), 1);
+        w[32 * g + e] = D * (double)sc * (double)(code6(grp, e) - 32);
+      }
     }
   } else {
     double D = oracle_f16_to_f64(get_f16(blk));

@@ -15,7 +15,7 @@ import numpy as np
 import pytest
 
 import oracle as oracle_pkg
-from oracle import Oracle, Q4_0, Q8_0, Q4_K
+from oracle import Oracle, Q4_0, Q8_0, Q4_K, Q6_K
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 MIB = 1024.0 * 1024.0
@@ -91,8 +91,9 @@ def pin_block_sizes(orc: Oracle):
     assert round(q8bpw, 1) == facts["legacy_bits_per_weight"]["q8_0_about"]
     ks = facts["kquant_superblock"]
     assert orc.block_elems(Q4_K) == ks["weights"] == ks["sub_blocks"] * ks["sub_block_weights"]
+    assert orc.block_elems(Q6_K) == ks["weights"]
     # the quantizers emit exactly these sizes
-    for f in (Q4_0, Q8_0, Q4_K):
+    for f in (Q4_0, Q8_0, Q4_K, Q6_K):
         be, bb = orc.block_elems(f), orc.block_bytes(f)
         out = orc.quantize(f, np.zeros((3, 2 * be), np.float32))
         assert out.shape == (3, 2 * bb)
@@ -141,8 +142,8 @@ def pin_qwen3_file_sizes(orc: Oracle):
     # q6_K block size implied by the 121.71 MiB embedding (256 weights/block)
     emb_mib = facts["qwen3_0p6b_vocab_and_embedding"]["embedding_q6_K_mib"]
     q6_bytes = round(emb_mib * MIB / (emb[1] * emb[2] / 256))
-    assert q6_bytes == 210
-    assert round(emb[1] * emb[2] / 256 * q6_bytes / MIB, 2) == emb_mib
+    assert q6_bytes == 210 == orc.block_bytes(Q6_K)
+    assert round(emb[1] * orc.row_bytes(Q6_K, emb[2]) / MIB, 2) == emb_mib
 
     # Q4_K_M file: embedding + 28 of the layer matrices in q6_K (attn_v and
     # ffn_down, split a/28-a), the rest in Q4_K; only a = 14 reproduces the
@@ -223,8 +224,53 @@ def pin_q4k_layout(orc: Oracle):
     assert np.array_equal(orc.quantize(Q4_K, vals.astype(np.float32)[None, :])[0], blk)
 
 
+def _q6k_pack(d, sc, codes):
+    """Q6_K-style superblock bytes written from the layout text: fp16 d, then
+    per 32-weight group g: int8 scales of sub-blocks 2g and 2g+1, 16 bytes
+    with code 32g+t's low 4 bits in the low nibble of byte t and code
+    32g+16+t's in the high nibble, then little-endian words H0, H1 whose byte
+    b holds the high 2 bits of codes 32g+4w+b (H0) or 32g+16+4w+b (H1) at
+    bits 2w..2w+1."""
+    out = bytearray(np.float16(d).tobytes())
+    for g in range(8):
+        c = codes[32 * g:32 * g + 32]
+        out += bytes([sc[2 * g] & 0xFF, sc[2 * g + 1] & 0xFF])
+        out += bytes((c[t] & 15) | ((c[16 + t] & 15) << 4) for t in range(16))
+        for half in (0, 16):
+            h = 0
+            for w in range(4):
+                for b in range(4):
+                    h |= (c[half + 4 * w + b] >> 4) << (8 * b + 2 * w)
+            out += h.to_bytes(4, "little")
+    return np.frombuffer(bytes(out), dtype=np.uint8)
+
+
+def _q6k_handmade():
+    """A Q6_K superblock: d = 2^-8, sub-block scales with maximum 127, codes
+    in 1..63 with one code of magnitude 31 per sub-block (so quantizing the
+    values must give back exactly these bytes). Returns (bytes, values)."""
+    d = 2.0 ** -8
+    sc = [127, 1, 64, 33, 5, 127, 90, 12, 7, 100, 45, 3, 127, 60, 2, 77]
+    codes = [1 + (7 * e + 11 * (e // 16) + 3) % 63 for e in range(256)]
+    for j in range(16):
+        codes[16 * j + (j % 16)] = 63 if j % 2 == 0 else 1
+    vals = np.array([d * sc[e // 16] * (codes[e] - 32) for e in range(256)])
+    return _q6k_pack(d, sc, codes), vals
+
+
+def pin_q6k_layout(orc: Oracle):
+    blk, vals = _q6k_handmade()
+    assert blk.size == orc.block_bytes(Q6_K)
+    assert np.array_equal(orc.dequant(Q6_K, blk, 1, 256)[0], vals)
+    assert np.array_equal(orc.quantize(Q6_K, vals.astype(np.float32)[None, :])[0], blk)
+
+
 def test_golden_blocks(orc):
     pin_golden_blocks(orc)
+
+
+def test_q6k_layout(orc):
+    pin_q6k_layout(orc)
 
 
 def test_q4k_layout(orc):
@@ -295,6 +341,21 @@ def pin_round_trip_bound(orc: Oracle):
     assert np.all(err[inside] <= (np.broadcast_to(S[..., None], w.shape)[inside] / 2) * (1 + 1e-6) + 1e-300)
     dist = np.where(w < lo, lo - w, w - hi)
     assert np.allclose(err[~inside], dist[~inside], rtol=1e-12, atol=0)
+    # Q6_K: within [-32 S_j, 31 S_j] the error is at most S_j/2, reached;
+    # outside, clamped to the nearer end
+    W = _test_blocks(rng, 500, 256)
+    B = orc.quantize(Q6_K, W)
+    Wd = orc.dequant(Q6_K, B, W.shape[0], 256).reshape(-1, 16, 16)
+    S, _ = _q6k_fields(B, orc)
+    w = W.astype(np.float64).reshape(-1, 16, 16)
+    lo, hi = -32 * S[..., None], 31 * S[..., None]
+    inside = (w >= lo) & (w <= hi)
+    err = np.abs(Wd - w)
+    Sb = np.broadcast_to(S[..., None], w.shape)
+    assert np.all(err[inside] <= Sb[inside] / 2 * (1 + 1e-6) + 1e-300)
+    assert np.any(err[inside] > 0.45 * Sb[inside])
+    dist = np.where(w < lo, lo - w, w - hi)
+    assert np.allclose(err[~inside], dist[~inside], rtol=1e-12, atol=0)
 
 
 def _q4k_scales(B: np.ndarray, orc: Oracle):
@@ -304,6 +365,21 @@ def _q4k_scales(B: np.ndarray, orc: Oracle):
     sc = np.array([[(v >> (6 * j)) & 63 for j in range(8)] for v in V], dtype=np.float64)
     mn = np.array([[(v >> (6 * (8 + j))) & 63 for j in range(8)] for v in V], dtype=np.float64)
     return d[:, None] * sc, dm[:, None] * mn
+
+
+def _q6k_fields(B: np.ndarray, orc: Oracle):
+    """Per superblock: the 16 sub-block scales S_j = d*sc_j (fp64) and the 256
+    codes (0..63), read with the layout of _q6k_pack."""
+    d = orc.f16_to_f64_array(B[:, 0].astype(np.uint16) | (B[:, 1].astype(np.uint16) << 8))
+    G = B[:, 2:].reshape(-1, 8, 26)
+    sc = G[:, :, 0:2].view(np.int8).astype(np.float64).reshape(-1, 16)
+    nib = G[:, :, 2:18].astype(np.int64)
+    lo = np.concatenate([nib & 15, nib >> 4], axis=2)            # [n, 8, 32]
+    H = G[:, :, 18:26].astype(np.int64).reshape(-1, 8, 2, 4)      # [n, g, half, byte b]
+    e = np.arange(16)
+    hi = (H[:, :, :, e & 3] >> (2 * (e >> 2))) & 3              # [n, g, half, 16]
+    codes = lo + 16 * hi.reshape(-1, 8, 32)
+    return d[:, None] * sc, codes.reshape(-1, 256)
 
 
 def _codes_q40(B):
@@ -349,6 +425,18 @@ def pin_code_optimality(orc: Oracle):
     best = np.abs(w[..., None] - lv).min(axis=-1)
     chosen = np.abs(w - (S[..., None] * qk - O[..., None]))
     assert np.all(chosen <= best + 1e-6 * S[..., None])
+    # Q6_K codes: nearest of the 64 levels S_j (c - 32)
+    W = _test_blocks(rng, 300, 256)
+    B = orc.quantize(Q6_K, W)
+    S, c = _q6k_fields(B, orc)
+    w = W.astype(np.float64).reshape(-1, 16, 16)
+    q = c.reshape(-1, 16, 16).astype(np.float64) - 32
+    lv = S[..., None, None] * (np.arange(64) - 32)[None, None, None, :]
+    best = np.abs(w[..., None] - lv).min(axis=-1)
+    chosen = np.abs(w - S[..., None] * q)
+    assert np.all(chosen <= best + 1e-6 * S[..., None])
+    # a zero scale gives the zero code
+    assert np.all(c.reshape(-1, 16, 16)[S == 0] == 32)
 
 
 def pin_idempotence(orc: Oracle):
@@ -384,6 +472,31 @@ def pin_exact_grid(orc: Oracle):
         assert np.array_equal(codes_of(B), q)
 
 
+def pin_q6k_exact_grid(orc: Oracle):
+    """Random superblocks on the Q6_K grid (d a normal binary16 value,
+    largest scale 127, every non-zero sub-block holding a code of magnitude
+    31; some sub-blocks all zero): quantizing their values returns exactly
+    the bytes _q6k_pack writes for them."""
+    rng = np.random.default_rng(13)
+    for _ in range(200):
+        d = float(np.uint16(rng.integers(0x0800, 0x3800)).view(np.float16))
+        sc = rng.integers(1, 128, 16)
+        sc[rng.integers(0, 16)] = 127
+        codes = rng.integers(1, 64, 256)
+        for j in range(16):
+            codes[16 * j + rng.integers(0, 16)] = rng.choice([1, 63])
+        zero = rng.random(16) < 0.15
+        zero[np.argmax(sc)] = False
+        for j in np.flatnonzero(zero):
+            sc[j] = 0
+            codes[16 * j:16 * j + 16] = 32
+        vals = np.array([d * sc[e // 16] * (codes[e] - 32) for e in range(256)])
+        assert np.array_equal(vals.astype(np.float32).astype(np.float64), vals)
+        blk = _q6k_pack(d, [int(v) for v in sc], [int(v) for v in codes])
+        assert np.array_equal(orc.quantize(Q6_K, vals.astype(np.float32)[None, :])[0], blk)
+        assert np.array_equal(orc.dequant(Q6_K, blk, 1, 256)[0], vals)
+
+
 def pin_zero_blocks(orc: Oracle):
     Z = np.zeros((2, 256), np.float32)
     b4 = orc.quantize(Q4_0, Z)
@@ -392,7 +505,9 @@ def pin_zero_blocks(orc: Oracle):
     assert np.all(b8 == 0)
     bk = orc.quantize(Q4_K, Z)
     assert np.all(bk == 0)
-    for f in (Q4_0, Q8_0, Q4_K):
+    b6 = orc.quantize(Q6_K, Z)
+    assert np.array_equal(b6[0], _q6k_pack(0.0, [0] * 16, [32] * 256))
+    for f in (Q4_0, Q8_0, Q4_K, Q6_K):
         assert np.all(orc.dequant(f, orc.quantize(f, Z), 2, 256) == 0)
 
 
@@ -416,12 +531,16 @@ def test_zero_blocks(orc):
     pin_zero_blocks(orc)
 
 
+def test_q6k_exact_grid(orc):
+    pin_q6k_exact_grid(orc)
+
+
 # ----------------------------------------------------------------- matmul --
 
 def pin_gemv_special_cases(orc: Oracle):
     rng = np.random.default_rng(21)
     M, K = 6, 512
-    for fmt in (Q4_0, Q8_0, Q4_K):
+    for fmt in (Q4_0, Q8_0, Q4_K, Q6_K):
         W = rng.normal(0, 0.02, (M, K)).astype(np.float32)
         B = orc.quantize(fmt, W)
         Wd = orc.dequant(fmt, B, M, K)
@@ -460,6 +579,27 @@ def pin_brute_force_4x64(orc: Oracle):
                 assert Y[n][m] == s
         assert np.allclose(y, np.array(Wd) @ x.astype(np.float64), rtol=1e-14, atol=1e-15)
         assert np.allclose(Y, Xd @ np.array(Wd).T, rtol=1e-14, atol=1e-15)
+    # the superblock formats on one 256-wide row pair, against the values
+    # the layout text gives for a hand-built superblock
+    blk, vals = _q6k_handmade()
+    B = np.concatenate([blk, blk[::-1].copy()])[None, :].reshape(1, -1)
+    K = 512
+    Wd = orc.dequant(Q6_K, B, 1, K)[0]
+    assert np.array_equal(Wd[:256], vals)
+    x = rng.normal(0, 1, K).astype(np.float32)
+    X = rng.normal(0, 1, (2, K)).astype(np.float32)
+    Xq = orc.quantize(Q8_0, X)
+    Xd = orc.dequant(Q8_0, Xq, 2, K)
+    s = 0.0
+    for k in range(K):
+        s += float(Wd[k]) * float(x[k])
+    assert orc.gemv(Q6_K, B, x, 1, K)[0] == s
+    Y = orc.gemm(Q6_K, B, Xq, 1, K, 2)
+    for n in range(2):
+        s = 0.0
+        for k in range(K):
+            s += float(Wd[k]) * float(Xd[n][k])
+        assert Y[n][0] == s
 
 
 def pin_on_grid_products(orc: Oracle):
@@ -500,9 +640,9 @@ def test_on_grid_products(orc):
 
 ALL_PINS = [pin_f16_decode_all, pin_f16_encode_sweep, pin_block_sizes,
             pin_qwen3_file_sizes, pin_golden_blocks, pin_q4k_layout,
-            pin_round_trip_bound, pin_code_optimality, pin_idempotence,
-            pin_exact_grid, pin_zero_blocks, pin_gemv_special_cases,
-            pin_brute_force_4x64, pin_on_grid_products]
+            pin_q6k_layout, pin_round_trip_bound, pin_code_optimality,
+            pin_idempotence, pin_exact_grid, pin_q6k_exact_grid, pin_zero_blocks,
+            pin_gemv_special_cases, pin_brute_force_4x64, pin_on_grid_products]
 
 MUTANTS = {
     "nibble_order_swapped": ("blk[2 + t] = (uint8_t)(code[t] | (code[t + 16] << 4));",
@@ -522,6 +662,12 @@ MUTANTS = {
                          "dst[1] = (uint8_t)(h & 0xFFu);\n  dst[0] = (uint8_t)(h >> 8);"),
     "q4k_min_sign": ("float O = Dm * (float)mnq[j];", "float O = -Dm * (float)mnq[j];"),
     "q4k_field_order": ("int v = f < 8 ? sc[f] : mnq[f - 8];", "int v = f < 8 ? mnq[f] : sc[f - 8];"),
+    "q6k_scale_over_32": ("s[j] = amax / 31.0f;", "s[j] = amax / 32.0f;"),
+    "q6k_code_offset_31": ("w[32 * g + e] = D * (double)sc * (double)(code6(grp, e) - 32);",
+                           "w[32 * g + e] = D * (double)sc * (double)(code6(grp, e) - 31);"),
+    "q6k_high_bits_words_swapped": ("int hi = (grp[18 + 4 * half + b] >> (2 * w)) & 3;",
+                                    "int hi = (grp[22 - 4 * half + b] >> (2 * w)) & 3;"),
+    "q6k_one_scale_per_group": ("memcpy(&sc, grp + (e >> 4), 1);", "memcpy(&sc, grp, 1);"),
     "gemv_drops_last_element": ("for (int64_t k = 0; k < K; ++k) s += w[k] * (double)x[k];",
                                 "for (int64_t k = 0; k + 1 < K; ++k) s += w[k] * (double)x[k];"),
     "gemm_transposed_store": ("Y[n * M + m] = s;", "Y[(m * N + n) % (M * N)] = s;"),
