@@ -15,8 +15,8 @@ import os
 
 import torch
 
-Q4_0, Q8_0, Q4_K = 0, 1, 2
-FORMATS = {"q4_0": Q4_0, "q8_0": Q8_0, "q4_k": Q4_K}
+Q4_0, Q8_0, Q4_K, Q6_K = 0, 1, 2, 3
+FORMATS = {"q4_0": Q4_0, "q8_0": Q8_0, "q4_k": Q4_K, "q6_k": Q6_K}
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqmat.so")
 _lib = None
 
@@ -63,7 +63,7 @@ def load_library():
 
 def _fmt(fmt) -> int:
     f = FORMATS[fmt.lower()] if isinstance(fmt, str) else int(fmt)
-    if f not in (Q4_0, Q8_0, Q4_K):
+    if f not in (Q4_0, Q8_0, Q4_K, Q6_K):
         raise ValueError(f"unknown format {fmt!r}")
     return f
 

@@ -16,7 +16,12 @@ constexpr int64_t kMaxDim = 0x7FFFFFFFLL;
 // 32-bit byte offsets: 129 Q8_0 rows of K = 2^24 take 2.3e9 bytes.
 constexpr int64_t kMaxGemmK = 1LL << 24;
 
-bool fmt_ok(int fmt) { return fmt == QMAT_Q4_0 || fmt == QMAT_Q8_0 || fmt == QMAT_Q4_K; }
+bool fmt_ok(int fmt) {
+  return fmt == QMAT_Q4_0 || fmt == QMAT_Q8_0 || fmt == QMAT_Q4_K || fmt == QMAT_Q6_K;
+}
+
+// formats the products accept (Q6_K-style: quantize only, so far)
+bool product_fmt_ok(int fmt) { return fmt_ok(fmt) && fmt != QMAT_Q6_K; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -51,6 +56,7 @@ int64_t qmat_block_elems(int fmt) {
     case QMAT_Q4_0: return 32;
     case QMAT_Q8_0: return 32;
     case QMAT_Q4_K: return 256;
+    case QMAT_Q6_K: return 256;
     default: return 0;
   }
 }
@@ -60,6 +66,7 @@ int64_t qmat_block_bytes(int fmt) {
     case QMAT_Q4_0: return 18;
     case QMAT_Q8_0: return 34;
     case QMAT_Q4_K: return 144;
+    case QMAT_Q6_K: return 210;
     default: return 0;
   }
 }
@@ -97,7 +104,7 @@ int qmat_quantize(int fmt, const float* W, void* blocks, int64_t rows, int64_t K
 
 int qmat_gemv(int fmt, const void* blocks, const float* x, float* y, int64_t M, int64_t K,
               void* stream) {
-  if (!fmt_ok(fmt)) return QMAT_E_FMT;
+  if (!product_fmt_ok(fmt)) return QMAT_E_FMT;
   int rc = check_shape(fmt, M, K);
   if (rc != QMAT_OK) return rc;
   if (M == 0) return QMAT_OK;  // nothing to read or write
@@ -109,7 +116,7 @@ int qmat_gemv(int fmt, const void* blocks, const float* x, float* y, int64_t M, 
 
 int qmat_gemm(int fmt, const void* blocks, const void* X_q8, float* Y, int64_t M, int64_t K,
               int64_t N, void* stream) {
-  if (!fmt_ok(fmt)) return QMAT_E_FMT;
+  if (!product_fmt_ok(fmt)) return QMAT_E_FMT;
   int rc = check_shape(fmt, M, K);
   if (rc != QMAT_OK) return rc;
   if ((rc = check_shape(QMAT_Q8_0, N, K)) != QMAT_OK) return rc;

@@ -10,6 +10,7 @@ namespace qmat {
 constexpr int kFmtQ4_0 = 0;
 constexpr int kFmtQ8_0 = 1;
 constexpr int kFmtQ4_K = 2;
+constexpr int kFmtQ6_K = 3;
 
 hipError_t launch_quantize(int fmt, const float* W, void* blocks, int64_t rows, int64_t K,
                            hipStream_t stream);

@@ -268,6 +268,96 @@ __global__ __launch_bounds__(kQThreads) void quantize_q4k_kernel(
   }
 }
 
+// Q6_K-style: one lane per 32-weight group (two 16-weight sub-blocks), so
+// 8 lanes per superblock and 8 superblocks per wave, staged like the Q4_K
+// kernel. Steps as the format's rule: s_j = amax_j / 31; d = max s_j / 127
+// (fp16); sc_j = clamp(rnd(s_j / D), 0, 127); S_j = D sc_j; codes
+// clamp(rnd(x / S_j), -32, 31) + 32. A wave's 8 packed superblocks (1680
+// bytes, 16-byte aligned) are assembled in LDS with 2-byte writes (group
+// starts are even) and written out with 16-byte stores.
+__global__ __launch_bounds__(kQThreads) void quantize_q6k_kernel(
+    const float* __restrict__ W, uint8_t* __restrict__ out, int64_t nsuper) {
+  constexpr int kSB = 210;
+  __shared__ __attribute__((aligned(16))) float xs[kQkWaves][kQkSuperPerWave * 256];
+  __shared__ __attribute__((aligned(16))) uint8_t ob[kQkWaves][kQkSuperPerWave * kSB];
+
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int g = lane & 7;  // group within the superblock
+  constexpr int kPerWG = kQkWaves * kQkSuperPerWave;
+  const int64_t nchunks = (nsuper + kPerWG - 1) / kPerWG;
+  float* mine = xs[wv];
+
+  for (int64_t chunk = blockIdx.x; chunk < nchunks; chunk += gridDim.x) {
+    const int64_t s0 = chunk * kPerWG + (int64_t)wv * kQkSuperPerWave;
+    const int64_t left = nsuper - s0;
+    const int nsb = left <= 0 ? 0 : (left < kQkSuperPerWave ? (int)left : kQkSuperPerWave);
+
+    // 8 superblocks = 64 groups of 32, staged like 64 blocks
+    stage_blocks(W + s0 * 256, 8 * nsb, mine, lane);
+    const bool valid = (lane >> 3) < nsb;
+    float v[32];
+    read_block(mine, lane, valid, v);
+
+    // 1. the two sub-blocks' scales (|x| >= +0: max order does not matter)
+    float aa = 0.0f, ab = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      aa = fmaxf(aa, fabsf(v[e]));
+      ab = fmaxf(ab, fabsf(v[16 + e]));
+    }
+    const float sa = aa / 31.0f, sb = ab / 31.0f;
+    // 2. super-scale: max over the superblock's 16 sub-blocks, from +0
+    const float d = max8_from0(sa > sb ? sa : sb) / 127.0f;
+    const uint32_t hd = f32_to_f16_bits(d);
+    const float D = f16_bits_to_f32(hd);
+    // 3. int8 sub-block scales; 4. their exact values
+    const int sca = (D == 0.0f) ? 0 : (int)clampf(roundf(sa / D), 0.0f, 127.0f);
+    const int scb = (D == 0.0f) ? 0 : (int)clampf(roundf(sb / D), 0.0f, 127.0f);
+    const float Sa = D * (float)sca, Sb = D * (float)scb;
+    // 5. codes c = q + 32 (32 where the scale is 0); code 32g+t's low 4
+    //    bits go to the low nibble of byte t, code 32g+16+t's to its high
+    //    nibble; the high 2 bits of code 32g+4w+b (32g+16+4w+b) go to bits
+    //    2w..2w+1 of byte b of H0 (H1)
+    const float ya = Sa != 0.0f ? 1.0f / Sa : 0.0f, yb = Sb != 0.0f ? 1.0f / Sb : 0.0f;
+    uint32_t nib[4] = {0u, 0u, 0u, 0u}, h0 = 0u, h1 = 0u;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int qa = Sa != 0.0f ? (int)clampf(roundf(div_shared(v[e], Sa, ya)), -32.0f, 31.0f) : 0;
+      const int qb =
+          Sb != 0.0f ? (int)clampf(roundf(div_shared(v[16 + e], Sb, yb)), -32.0f, 31.0f) : 0;
+      const uint32_t ca = (uint32_t)(qa + 32), cb = (uint32_t)(qb + 32);
+      nib[e >> 2] |= ((ca & 15u) << (8 * (e & 3))) | ((cb & 15u) << (8 * (e & 3) + 4));
+      h0 |= (ca >> 4) << (8 * (e & 3) + 2 * (e >> 2));
+      h1 |= (cb >> 4) << (8 * (e & 3) + 2 * (e >> 2));
+    }
+
+    // the group's 26 bytes at superblock offset 2 + 26 g, then d at 0
+    uint16_t* o = reinterpret_cast<uint16_t*>(ob[wv] + (lane >> 3) * kSB + 2 + 26 * g);
+    o[0] = (uint16_t)((sca & 0xFF) | ((scb & 0xFF) << 8));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      o[1 + 2 * i] = (uint16_t)nib[i];
+      o[2 + 2 * i] = (uint16_t)(nib[i] >> 16);
+    }
+    o[9] = (uint16_t)h0;
+    o[10] = (uint16_t)(h0 >> 16);
+    o[11] = (uint16_t)h1;
+    o[12] = (uint16_t)(h1 >> 16);
+    if (g == 0) reinterpret_cast<uint16_t*>(ob[wv] + (lane >> 3) * kSB)[0] = (uint16_t)hd;
+
+    // the wave's superblocks are contiguous and start 16-byte aligned
+    // (s0 is a multiple of 8 and 8 * 210 = 1680 of 16)
+    const int nbytes = nsb * kSB;
+    uint8_t* dst = out + s0 * kSB;
+    for (int i = lane; i < (nbytes >> 4); i += kWave)
+      reinterpret_cast<u32x4*>(dst)[i] = reinterpret_cast<const u32x4*>(ob[wv])[i];
+    const int t0 = nbytes & ~15;
+    for (int i = t0 + 2 * lane; i < nbytes; i += 2 * kWave)
+      *reinterpret_cast<uint16_t*>(dst + i) = *reinterpret_cast<const uint16_t*>(ob[wv] + i);
+  }
+}
+
 constexpr int64_t kMaxGrid = 1 << 24;
 
 int64_t grid_for(int64_t chunks) { return chunks < kMaxGrid ? chunks : kMaxGrid; }
@@ -277,12 +367,16 @@ int64_t grid_for(int64_t chunks) { return chunks < kMaxGrid ? chunks : kMaxGrid;
 hipError_t launch_quantize(int fmt, const float* W, void* blocks, int64_t rows, int64_t K,
                            hipStream_t stream) {
   uint8_t* out = static_cast<uint8_t*>(blocks);
-  if (fmt == kFmtQ4_K) {
+  if (fmt == kFmtQ4_K || fmt == kFmtQ6_K) {
     const int64_t nsuper = rows * (K / 256);
     const int64_t chunks = (nsuper + kQkWaves * kQkSuperPerWave - 1) / (kQkWaves * kQkSuperPerWave);
     if (chunks == 0) return hipSuccess;
-    hipLaunchKernelGGL(quantize_q4k_kernel, dim3((unsigned)grid_for(chunks)), dim3(kQThreads), 0,
-                       stream, W, out, nsuper);
+    if (fmt == kFmtQ4_K)
+      hipLaunchKernelGGL(quantize_q4k_kernel, dim3((unsigned)grid_for(chunks)), dim3(kQThreads),
+                         0, stream, W, out, nsuper);
+    else
+      hipLaunchKernelGGL(quantize_q6k_kernel, dim3((unsigned)grid_for(chunks)), dim3(kQThreads),
+                         0, stream, W, out, nsuper);
   } else {
     const int64_t nb = rows * (K / 32);
     const int64_t chunks = (nb + kQThreads - 1) / kQThreads;  // one block per thread

@@ -20,6 +20,9 @@
  *   [BARE] xdnf.cn llama.cpp article; section 3.2 (dequant snippet: low
  *          nibbles are the first 16 elements of a block, high nibbles the
  *          last 16; fp16 parameters precede the nibbles).
+ *   [LC05 KV] [LC05] section "KV Cache 类型与 Flash Attention" (the q6_K
+ *          token embedding of 1024 x 151936 weights is 121.71 MiB, so q6_K
+ *          stores 210 bytes per 256 weights).
  *
  * Block formats (byte-exact; little-endian; fp16 = IEEE binary16):
  *   Q4_0  (32 weights, 18 B)  [LCHW], [LC05 table], [KVQ], [BARE 3.2]
@@ -40,6 +43,21 @@
  *         [16:144] codes; sub-block j uses bytes 16+16j .. 16+16j+15 with
  *                 the Q4_0 nibble order; q in [0,15];
  *                 weight = (d*sc_j)*q - (dmin*mn_j).
+ *   Q6_K  (256 weights = 16 sub-blocks of 16, 210 B)  [LC05 table] (the
+ *         k-quant superblock, Q6_K its near-lossless member), [LC05 KV]
+ *         (210 B). Sixteen 16-weight sub-blocks with int8 scales are the
+ *         split that fills 210 bytes with 6-bit codes; the byte packing is
+ *         this library's own, not GGUF's q6_K:
+ *         [0:2]   fp16 super-scale d
+ *         then for each group g = 0..7 of 32 weights (sub-blocks 2g, 2g+1),
+ *         26 bytes at 2+26g:
+ *           [+0], [+1]  int8 sc_2g, sc_2g+1
+ *           [+2:+18]    byte t: low 4 bits of code 32g+t (low nibble) and
+ *                       of code 32g+16+t (high nibble)
+ *           [+18:+22]   little-endian word H0: bits 2w..2w+1 of its byte b
+ *                       are the high 2 bits of code 32g+4w+b
+ *           [+22:+26]   H1: the same for code 32g+16+4w+b
+ *         code c in [0,63]; weight = (d*sc_j)*(c-32), j = element / 16.
  *
  * Matrix layout: a [rows][K] matrix is rows*(K/block_elems) blocks, row
  * after row, blocks running along K, no padding. Rows are therefore
@@ -78,7 +96,8 @@ extern "C" {
 typedef enum qmat_fmt {
   QMAT_Q4_0 = 0,
   QMAT_Q8_0 = 1,
-  QMAT_Q4_K = 2
+  QMAT_Q4_K = 2,
+  QMAT_Q6_K = 3
 } qmat_fmt;
 
 typedef enum qmat_status {
@@ -91,10 +110,11 @@ typedef enum qmat_status {
   QMAT_E_ALIGN = 5  /* a pointer is not 16-byte aligned                   */
 } qmat_status;
 
-/* Elements per block: 32 (Q4_0, Q8_0), 256 (Q4_K); 0 for an unknown fmt. */
+/* Elements per block: 32 (Q4_0, Q8_0), 256 (Q4_K, Q6_K); 0 if unknown. */
 int64_t qmat_block_elems(int fmt);
 
-/* Bytes per block: 18 (Q4_0) [LCHW], 34 (Q8_0), 144 (Q4_K); 0 if unknown. */
+/* Bytes per block: 18 (Q4_0) [LCHW], 34 (Q8_0), 144 (Q4_K), 210 (Q6_K)
+ * [LC05 KV]; 0 if unknown. */
 int64_t qmat_block_bytes(int fmt);
 
 /* Bytes of one packed row of K elements; -1 for an unknown fmt, a negative
@@ -122,6 +142,9 @@ const char *qmat_strerror(int status);
  *           clamp(rnd(scale_j/D),0,63), clamp(rnd(off_j/Dmin),0,63);
  *           q = clamp(rnd((w + Dmin*mn_j)/(D*sc_j)),0,15) (0 if D*sc_j==0).
  *           [LC05 table] two-level scaling with 6-bit sub-block scales.
+ *     Q6_K: per 16-weight sub-block j: s_j = amax_j/31; d = max s_j / 127
+ *           (stored fp16); sc_j = clamp(rnd(s_j/D),0,127);
+ *           c = clamp(rnd(w/(D*sc_j)),-32,31)+32 (32 if D*sc_j==0).
  *   Non-finite inputs or a scale above 65504 give unspecified bytes (never
  *   a fault).
  */
@@ -133,7 +156,8 @@ int qmat_quantize(int fmt, const float *W, void *blocks, int64_t rows,
  *   y[m] = sum_k dequant(W)[m][k] * x[k],  m < M.
  *   [LC05 "带宽决定 Decode"]: every weight byte is read once per token, so
  *   this is bound by HBM bandwidth.
- *   blocks: W in fmt (Q4_0, Q8_0 or Q4_K), M rows of K.
+ *   blocks: W in fmt (Q4_0, Q8_0 or Q4_K; Q6_K gives QMAT_E_FMT), M rows
+ *   of K.
  *   x: fp32 [K]; y: fp32 [M], overwritten.
  *   Accuracy: relative L2 error against the exact (fp64) product of the
  *   dequantized weights with x is below 1e-3 for finite x; internally each
@@ -151,7 +175,8 @@ int qmat_gemv(int fmt, const void *blocks, const float *x, float *y,
  *   [LC05 "算力决定 Prefill"]: one weight read serves many tokens, so this
  *   is bound by the matrix cores (int8 MFMA over each 32-element block,
  *   then the two fp16 block scales applied in fp32).
- *   blocks: W in fmt (Q4_0, Q8_0 or Q4_K), M rows of K.
+ *   blocks: W in fmt (Q4_0, Q8_0 or Q4_K; Q6_K gives QMAT_E_FMT), M rows
+ *   of K.
  *   X_q8: Q8_0 blocks of the activations, N rows of K, exactly as
  *         qmat_quantize(QMAT_Q8_0, X, X_q8, N, K, stream) writes them.
  *   Y: fp32 [N][M] (token-major), overwritten.

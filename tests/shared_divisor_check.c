@@ -3,7 +3,8 @@
  * q = RN(q0 + r*y) (one fma), the rounded code round(q), clamped to the
  * format's range, must equal round(RN(a/b)) clamped the same way.
  * Divisors b: every positive finite fp16 value (Q4_0 / Q8_0 scales) and
- * fp16 values times 1..63 (Q4_K-style sub-block scales). Numerators a:
+ * fp16 values times 1..127 (Q4_K-style sub-block scales, 1..63, and
+ * Q6_K-style ones, 1..127). Numerators a:
  * quotients spread over the code ranges, the neighbourhood (a few ulps) of
  * every half-integer quotient, and random bit patterns.
  * Usage: shared_divisor_check N_SAMPLES SEED; prints "ok" or the first
@@ -33,7 +34,7 @@ int main(int argc, char **argv) {
   for (long long it = 0; it < n; ++it) {
     float b = half_to_float((uint16_t)(1 + next() % 0x7BFF));  /* positive finite fp16 */
     int q4k = it & 1;
-    if (q4k) b *= (float)(1 + next() % 63);
+    if (q4k) b *= (float)(1 + next() % 127);
     float a;
     switch ((it >> 1) % 3) {
       case 0:
@@ -55,8 +56,8 @@ int main(int argc, char **argv) {
     if (!isfinite(ref) || fabsf(ref) > 1e30f) continue; /* no valid block reaches these */
     float y = 1.0f / b, q0 = a * y, q = fmaf(fmaf(-q0, b, a), y, q0);
     ++checked;
-    float lo[3] = {-8.0f, -127.0f, 0.0f}, hi[3] = {7.0f, 127.0f, 15.0f};
-    for (int f = 0; f < 3; ++f) {
+    float lo[4] = {-8.0f, -127.0f, 0.0f, -32.0f}, hi[4] = {7.0f, 127.0f, 15.0f, 31.0f};
+    for (int f = 0; f < 4; ++f) {
       if (code(q, lo[f], hi[f]) != code(ref, lo[f], hi[f])) {
         if (++bad <= 5) printf("mismatch a=%a b=%a ieee=%a shared=%a\n", a, b, ref, q);
         break;

@@ -45,16 +45,17 @@ def test_enum_values_match_header():
     text = open(HEADER).read()
     vals = dict(re.findall(r"\b(QMAT_[A-Z0-9_]+)\s*=\s*(\d+)", text))
     assert vals["QMAT_Q4_0"] == "0" and vals["QMAT_Q8_0"] == "1" and vals["QMAT_Q4_K"] == "2"
-    assert binding.Q4_0 == 0 and binding.Q8_0 == 1 and binding.Q4_K == 2
+    assert vals["QMAT_Q6_K"] == "3"
+    assert binding.Q4_0 == 0 and binding.Q8_0 == 1 and binding.Q4_K == 2 and binding.Q6_K == 3
     assert [vals[k] for k in ("QMAT_OK", "QMAT_E_FMT", "QMAT_E_SHAPE", "QMAT_E_NULL",
                               "QMAT_E_HIP", "QMAT_E_ALIGN")] == ["0", "1", "2", "3", "4", "5"]
 
 
 def test_sizes_agree_with_oracle(lib):
-    for f in (0, 1, 2):
+    for f in (0, 1, 2, 3):
         assert lib.qmat_block_elems(f) == oracle.block_elems(f)
         assert lib.qmat_block_bytes(f) == oracle.block_bytes(f)
-        for K in (0, 256, 11008 if f != 2 else 4096, 2 ** 20):
+        for K in (0, 256, 11008 if f < 2 else 4096, 2 ** 20):
             assert lib.qmat_row_bytes(f, K) == oracle.row_bytes(f, K)
     assert lib.qmat_block_elems(7) == 0 and lib.qmat_block_bytes(-1) == 0
     assert lib.qmat_row_bytes(0, 33) == -1 and lib.qmat_row_bytes(2, 32) == -1
@@ -71,7 +72,7 @@ A = 0x10000  # a 16-byte aligned fake address: never dereferenced (rejected firs
 
 
 def test_bad_format(lib):
-    assert lib.qmat_quantize(3, A, A, 1, 32, None) == E_FMT
+    assert lib.qmat_quantize(4, A, A, 1, 32, None) == E_FMT
     assert lib.qmat_gemv(-1, A, A, A, 1, 32, None) == E_FMT
     assert lib.qmat_gemm(5, A, A, A, 1, 32, 1, None) == E_FMT
 
@@ -79,6 +80,7 @@ def test_bad_format(lib):
 def test_bad_shapes(lib):
     assert lib.qmat_quantize(0, A, A, 1, 48, None) == E_SHAPE      # K % 32
     assert lib.qmat_quantize(2, A, A, 1, 288, None) == E_SHAPE     # K % 256
+    assert lib.qmat_quantize(3, A, A, 1, 288, None) == E_SHAPE     # K % 256
     assert lib.qmat_quantize(1, A, A, -1, 32, None) == E_SHAPE
     assert lib.qmat_gemv(0, A, A, A, -5, 32, None) == E_SHAPE
     assert lib.qmat_gemv(0, A, A, A, 1, -32, None) == E_SHAPE

@@ -91,10 +91,11 @@ SMALL_SHAPES = {
     0: [(1, 32), (3, 32 * 37), (5, 256), (64, 1024), (33, 2048), (7, 32 * 345)],
     1: [(1, 32), (3, 32 * 37), (5, 256), (64, 1024), (33, 2048), (7, 32 * 345)],
     2: [(1, 256), (3, 768), (17, 4096), (5, 11008)],
+    3: [(1, 256), (3, 768), (17, 4096), (5, 11008), (9, 256 * 9)],
 }
 
 
-@pytest.mark.parametrize("fmt", [0, 1, 2])
+@pytest.mark.parametrize("fmt", [0, 1, 2, 3])
 def test_quantize_bytes_identical_small(q, fmt):
     rng = np.random.default_rng(100 + fmt)
     for rows, K in SMALL_SHAPES[fmt]:
@@ -125,14 +126,15 @@ def test_quantize_edge_values(q):
         got = host(q.quantize(fmt, dev_tensor(W)))
         assert np.array_equal(got, oracle.quantize(fmt, W)), fmt
     Wk = np.tile(W.reshape(1, -1), (3, 1))  # 3 superblocks of 256
-    got = host(q.quantize(2, dev_tensor(Wk)))
-    assert np.array_equal(got, oracle.quantize(2, Wk))
+    for fmt in (2, 3):
+        got = host(q.quantize(fmt, dev_tensor(Wk)))
+        assert np.array_equal(got, oracle.quantize(fmt, Wk)), fmt
 
 
 def test_quantize_bytes_identical_full_sizes(q):
     for orient in (0, 1):
         W, _ = inputs.llama7b_layer(orient)
-        for fmt in (0, 1, 2):
+        for fmt in (0, 1, 2, 3):
             say(f"quantize full llama7b_layer orient={orient} fmt={fmt} {W.shape}")
             got = host(q.quantize(fmt, dev_tensor(W)))
             assert np.array_equal(got, oracle.quantize(fmt, W))
