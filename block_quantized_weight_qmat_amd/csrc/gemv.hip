@@ -220,6 +220,7 @@ __device__ __forceinline__ int32_t nib_dot(const uint32_t (&w)[4], const XNib& x
 struct XByte {
   uint32_t xl[8], xh[8], xt[8];
   int32_t sx;
+  int32_t sxh[2];  // sums of X over elements 0..15 and 16..31 (Q6_K only)
   float inv;
 };
 
@@ -234,7 +235,7 @@ struct ByteAcc {
 constexpr uint32_t kByteBias = 0x88080u;
 constexpr float kByteLim = (float)(0xFFFFF - kByteBias);  // 491391
 
-__device__ __forceinline__ void prep_byte(f32x4 (&v)[8], XByte& xp, bool /*want_sum*/) {
+__device__ __forceinline__ void prep_byte(f32x4 (&v)[8], XByte& xp, bool want_sum) {
   const float scale = slice_scale(v, kByteLim, xp.inv);
   const float magic = kMagicF + (float)kByteBias;  // exact: below 2^24
 #pragma unroll
@@ -247,6 +248,21 @@ __device__ __forceinline__ void prep_byte(f32x4 (&v)[8], XByte& xp, bool /*want_
     xp.xt[i] = ((top & 0x0F0F0F0Fu) + 0x78787878u) ^ 0x80808080u;
   }
   xp.sx = 0;
+  xp.sxh[0] = xp.sxh[1] = 0;
+  if (want_sum) {
+    // X = xl + 256 xh + 65536 xt per element; each half's sum is exact
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      int32_t l = 0, m = 0, t = 0;
+#pragma unroll
+      for (int i = 4 * h; i < 4 * h + 4; ++i) {
+        l = sdot4(xp.xl[i], 0x01010101u, l);
+        m = sdot4(xp.xh[i], 0x01010101u, m);
+        t = sdot4(xp.xt[i], 0x01010101u, t);
+      }
+      xp.sxh[h] = (t * 256 + m) * 256 + l;
+    }
+  }
 }
 
 // A lane's fixed load offsets and alignment case for one 18- or 34-byte
@@ -261,6 +277,8 @@ struct BlockLane {
   uint32_t o2;   // offset of the 2-byte load
   uint32_t sel;  // v_perm selector realigning the codes to 4-byte words
   bool mis;      // block starts at 2 mod 4
+  uint32_t o8;   // Q6_K: offset of the 8-byte load
+  uint32_t od;   // Q6_K: offset of the superblock's scale d
 };
 
 __device__ __forceinline__ BlockLane block_lane(uint32_t o, uint32_t p, uint32_t bytes) {
@@ -283,7 +301,12 @@ struct FmtQ4_0 {
     u32x4 v;
     uint16_t s;  // widened where it is used, after the load has landed
   };
-  __device__ static int64_t row_bytes(int K) { return (int64_t)(K >> 5) * 18; }
+  static constexpr bool kSum = false;  // records need sums of X
+  __host__ __device__ static int64_t row_bytes(int64_t K) { return (K >> 5) * 18; }
+  // loads of slice j in a row whose start has alignment parity p (0 or 2)
+  __device__ static BlockLane lane(int j, uint32_t p) {
+    return block_lane((uint32_t)j * 18u, p, 18);
+  }
   __device__ static void prep(f32x4 (&v)[8], XP& xp) { prep_nib(v, xp, false); }
   __device__ static void load(const uint8_t* __restrict__ row, const BlockLane& L, Raw& r) {
     r.v = *reinterpret_cast<const u32x4_a4*>(row + L.o16);
@@ -317,7 +340,11 @@ struct FmtQ8_0 {
     u32x4 v0, v1;
     uint16_t s;
   };
-  __device__ static int64_t row_bytes(int K) { return (int64_t)(K >> 5) * 34; }
+  static constexpr bool kSum = false;
+  __host__ __device__ static int64_t row_bytes(int64_t K) { return (K >> 5) * 34; }
+  __device__ static BlockLane lane(int j, uint32_t p) {
+    return block_lane((uint32_t)j * 34u, p, 34);
+  }
   __device__ static void prep(f32x4 (&v)[8], XP& xp) { prep_byte(v, xp, false); }
   __device__ static void load(const uint8_t* __restrict__ row, const BlockLane& L, Raw& r) {
     r.v0 = *reinterpret_cast<const u32x4_a4*>(row + L.o16);
@@ -359,7 +386,20 @@ struct FmtQ4_K {
   struct Raw {
     u32x4 h, c;
   };
-  __device__ static int64_t row_bytes(int K) { return (int64_t)(K >> 8) * 144; }
+  static constexpr bool kSum = true;
+  __host__ __device__ static int64_t row_bytes(int64_t K) { return (K >> 8) * 144; }
+  // the superblock header and the sub-block's 16 code bytes (rows are
+  // 16-byte aligned: p is 0)
+  __device__ static BlockLane lane(int j, uint32_t /*p*/) {
+    BlockLane L;
+    const uint32_t o = (uint32_t)(j >> 3) * 144u;
+    L.o16 = o;
+    L.o2 = o + 16u + 16u * (uint32_t)(j & 7);
+    L.sel = 0;
+    L.mis = false;
+    L.o8 = L.od = 0;
+    return L;
+  }
   __device__ static void prep(f32x4 (&v)[8], XP& xp) { prep_nib(v, xp, true); }
   __device__ static void load(const uint8_t* __restrict__ row, const BlockLane& L, Raw& r) {
     r.h = *reinterpret_cast<const u32x4*>(row + L.o16);
@@ -385,6 +425,96 @@ struct FmtQ4_K {
     // sum q X = sum (q - 8) X + 8 sum X
     const int32_t Q8 = nib_dot(w, xp, ac);
     return fmaf(S, (float)Q8, fmaf(8.0f, S, -O) * (float)xp.sx);
+  }
+};
+
+// ------------------------------------------------------------------ Q6_K --
+// 210-byte superblocks: fp16 d, then per 32-weight group g (slice j = 8 s +
+// g of superblock s) 26 bytes at 2 + 26 g: int8 scales of sub-blocks 2g and
+// 2g+1, 16 bytes of low nibbles (byte t: code t | code 16+t), high-bit
+// words H0, H1 (bits 2w..2w+1 of byte b: code 4w+b, code 16+4w+b).
+// weight = d sc_j (c - 32). A lane loads its group as 16 + 8 + 2 bytes at
+// 4-byte-aligned offsets (which pieces depends on the group's alignment)
+// plus d, realigns with one v_perm selector, rebuilds the 6-bit codes as
+// bytes and takes exact byte-digit dot products per 16-weight half:
+// sum (c - 32) X = sum c X - 32 sum X, the half sums of X coming with the
+// converted activations.
+struct ByteAcc2 {
+  ByteAcc h[2];
+};
+
+struct FmtQ6_K {
+  static constexpr int kBytes = 210;
+  static constexpr int kLoads = 4;
+  static constexpr bool kSum = true;
+  typedef XByte XP;
+  typedef ByteAcc2 Acc;
+  struct Raw {
+    u32x4 v;
+    uint32_t u0, u1;
+    uint16_t s;  // widened where it is used, after the load has landed
+    uint16_t d;
+  };
+  __host__ __device__ static int64_t row_bytes(int64_t K) { return (K >> 8) * 210; }
+  __device__ static void prep(f32x4 (&v)[8], XP& xp) { prep_byte(v, xp, true); }
+  // group bytes [G, G + 26): if G is 4-byte aligned, 16 bytes at G, 8 at
+  // G + 16, 2 at G + 24; else 2 at G, 16 at G + 2, 8 at G + 18
+  __device__ static BlockLane lane(int j, uint32_t p) {
+    BlockLane L;
+    const uint32_t sb = (uint32_t)(j >> 3) * 210u, G = sb + 2u + 26u * (uint32_t)(j & 7);
+    L.mis = ((G + p) & 2u) != 0;
+    L.o16 = L.mis ? G + 2u : G;
+    L.o8 = L.mis ? G + 18u : G + 16u;
+    L.o2 = L.mis ? G : G + 24u;
+    L.od = sb;
+    L.sel = L.mis ? 0x03020100u : 0x05040302u;
+    return L;
+  }
+  __device__ static void load(const uint8_t* __restrict__ row, const BlockLane& L, Raw& r) {
+    r.v = *reinterpret_cast<const u32x4_a4*>(row + L.o16);
+    r.u0 = *reinterpret_cast<const uint32_t*>(row + L.o8);
+    r.u1 = *reinterpret_cast<const uint32_t*>(row + L.o8 + 4);
+    r.s = *reinterpret_cast<const uint16_t*>(row + L.o2);
+    r.d = *reinterpret_cast<const uint16_t*>(row + L.od);
+  }
+  __device__ static void load(__amdgpu_buffer_rsrc_t rs, const BlockLane& L, Raw& r) {
+    r.v = __builtin_amdgcn_raw_buffer_load_b128(rs, L.o16, 0, 0);
+    const uint2 u = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, L.o8, 0, 0));
+    r.u0 = u.x;
+    r.u1 = u.y;
+    r.s = __builtin_amdgcn_raw_buffer_load_b16(rs, L.o2, 0, 0);
+    r.d = __builtin_amdgcn_raw_buffer_load_b16(rs, L.od, 0, 0);
+  }
+  __device__ static float apply(const Raw& r, const BlockLane& L, const XP& xp, int /*j*/,
+                               Acc& ac) {
+    // the group's words: 16 nibble bytes N, then H0, H1; in the aligned
+    // case they start 2 bytes into the loaded words, after the scales
+    const uint32_t x[7] = {r.v.x, r.v.y, r.v.z, r.v.w, r.u0, r.u1, (uint32_t)r.s};
+    uint32_t N[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) N[k] = perm_b32(x[k + 1], x[k], L.sel);
+    const uint32_t H[2] = {perm_b32(x[5], x[4], L.sel), perm_b32(x[6], x[5], L.sel)};
+    const uint32_t scw = L.mis ? (uint32_t)r.s : r.v.x;
+    const float sc[2] = {(float)(int8_t)(scw & 0xFFu), (float)(int8_t)((scw >> 8) & 0xFFu)};
+    float out = 0.0f;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      ByteAcc& a = ac.h[h];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        // codes of elements 16h + 4w .. 16h + 4w + 3 as bytes 0..63
+        const uint32_t lo = h ? (N[w] >> 4) & 0x0F0F0F0Fu : N[w] & 0x0F0F0F0Fu;
+        const uint32_t c = lo | (((H[h] >> (2 * w)) & 0x03030303u) << 4);
+        a.l = sdot4(c, xp.xl[4 * h + w], a.l);
+        a.h = sdot4(c, xp.xh[4 * h + w], a.h);
+        a.t = sdot4(c, xp.xt[4 * h + w], a.t);
+      }
+      const uint32_t tot = ((uint32_t)a.t * 256u + (uint32_t)a.h) * 256u + (uint32_t)a.l;
+      const int32_t S = (int32_t)(tot - a.prev) - 32 * xp.sxh[h];  // sum (c - 32) X
+      a.prev = tot;
+      out = fmaf(sc[h], (float)S, out);
+    }
+    return f16_bits_to_f32(r.d) * out;
   }
 };
 
@@ -529,18 +659,8 @@ __global__ __launch_bounds__(kMaxStrips * kWave) void gemv_kernel(const uint8_t*
     x_to_lds(x + (int64_t)base * 32, ns - base, strip, lane);
     if (j < ns) {
       BlockLane L[2];
-      if (F::kBytes == 144) {  // Q4_K: header and the sub-block's 16 code bytes
-        const uint32_t o = (uint32_t)(j >> 3) * 144u;
-        L[0].o16 = o;
-        L[0].o2 = o + 16u + 16u * (uint32_t)(j & 7);
-        L[0].sel = 0;
-        L[0].mis = false;
-        L[1] = L[0];
-      } else {
-        const uint32_t o = (uint32_t)j * (uint32_t)F::kBytes;
-        L[0] = block_lane(o, 0u, F::kBytes);
-        L[1] = block_lane(o, kOdd ? 2u : 0u, F::kBytes);
-      }
+      L[0] = F::lane(j, 0u);
+      L[1] = F::lane(j, kOdd ? 2u : 0u);
       typename F::Raw raw[D][R];
       auto load_group = [&](int g, typename F::Raw(&dst)[R]) {
 #pragma unroll
@@ -624,6 +744,7 @@ __global__ __launch_bounds__(kMaxStrips * kWave) void gemv_kernel(const uint8_t*
 #define QMAT_GEMV_ROW_DEPTH_Q4_0 1
 #define QMAT_GEMV_ROW_DEPTH_Q8_0 1
 #define QMAT_GEMV_ROW_DEPTH_Q4_K 2
+#define QMAT_GEMV_ROW_DEPTH_Q6_K 1
 #endif
 constexpr int kRowWaves = QMAT_GEMV_ROW_WAVES;
 constexpr int kRowSlot = 8192;  // one strip of fp32 activations
@@ -648,7 +769,7 @@ static_assert(kRowWaves >= 8, "wave w converts strip w");
 // digits: word t of digit i of slice l at byte 1024 i + 16 l + 4 t (a lane
 // reads consecutive 16-byte groups), inv at 5120 + 4 l, sx at 5376 + 4 l.
 // Byte digits: words 4h..4h+3 of kind j (xl, xh, xt) at 1024 (2j + h) +
-// 16 l, inv at 6144 + 4 l.
+// 16 l, inv at 6144 + 4 l, half sums of X (Q6_K) at 6400 + 4 l, 6656 + 4 l.
 __device__ __forceinline__ void put_rec(uint8_t* slot, int l, const XNib& xp, bool sum) {
 #pragma unroll
   for (int i = 0; i < 5; ++i)
@@ -671,7 +792,7 @@ __device__ __forceinline__ void get_rec(const uint8_t* slot, int l, XNib& xp, bo
   xp.sx = sum ? reinterpret_cast<const int32_t*>(slot + 5376)[l] : 0;
 }
 
-__device__ __forceinline__ void put_rec(uint8_t* slot, int l, const XByte& xp, bool /*sum*/) {
+__device__ __forceinline__ void put_rec(uint8_t* slot, int l, const XByte& xp, bool sum) {
   const uint32_t* src[3] = {xp.xl, xp.xh, xp.xt};
 #pragma unroll
   for (int j = 0; j < 3; ++j)
@@ -680,9 +801,13 @@ __device__ __forceinline__ void put_rec(uint8_t* slot, int l, const XByte& xp, b
       *reinterpret_cast<u32x4*>(slot + 1024 * (2 * j + h) + 16 * l) =
           u32x4{src[j][4 * h], src[j][4 * h + 1], src[j][4 * h + 2], src[j][4 * h + 3]};
   reinterpret_cast<float*>(slot + 6144)[l] = xp.inv;
+  if (sum) {
+    reinterpret_cast<int32_t*>(slot + 6400)[l] = xp.sxh[0];
+    reinterpret_cast<int32_t*>(slot + 6656)[l] = xp.sxh[1];
+  }
 }
 
-__device__ __forceinline__ void get_rec(const uint8_t* slot, int l, XByte& xp, bool /*sum*/) {
+__device__ __forceinline__ void get_rec(const uint8_t* slot, int l, XByte& xp, bool sum) {
   uint32_t* dst[3] = {xp.xl, xp.xh, xp.xt};
 #pragma unroll
   for (int j = 0; j < 3; ++j)
@@ -696,6 +821,8 @@ __device__ __forceinline__ void get_rec(const uint8_t* slot, int l, XByte& xp, b
     }
   xp.inv = reinterpret_cast<const float*>(slot + 6144)[l];
   xp.sx = 0;
+  xp.sxh[0] = sum ? reinterpret_cast<const int32_t*>(slot + 6400)[l] : 0;
+  xp.sxh[1] = sum ? reinterpret_cast<const int32_t*>(slot + 6656)[l] : 0;
 }
 
 template <class F, int R, int kD, bool kOdd>
@@ -705,7 +832,6 @@ __global__ __launch_bounds__(kRowWaves * kWave) void gemv_rows_kernel(
   extern __shared__ __attribute__((aligned(16))) uint8_t slots[];
   __shared__ int ready[8];  // strip s's records are in slot s when ready[s] != 0
   typedef typename F::XP XP;
-  constexpr bool kQ4K = F::kBytes == 144;
   constexpr uint32_t kOut = 0x80000000u;  // an offset past the end of any row
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -738,27 +864,14 @@ __global__ __launch_bounds__(kRowWaves * kWave) void gemv_rows_kernel(
   asm volatile("s_barrier" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
 
-  auto lane_of = [&](int st, uint32_t p) {
-    const int j = st * kWave + lane;
-    BlockLane L;
-    if (kQ4K) {
-      const uint32_t o = (uint32_t)(j >> 3) * 144u;
-      L.o16 = o;
-      L.o2 = o + 16u + 16u * (uint32_t)(j & 7);
-      L.sel = 0;
-      L.mis = false;
-    } else {
-      L = block_lane((uint32_t)j * (uint32_t)F::kBytes, 2u * p, F::kBytes);
-    }
-    return L;
-  };
+  auto lane_of = [&](int st, uint32_t p) { return F::lane(st * kWave + lane, 2u * p); };
   typename F::Raw wb[kD][R];
   auto load_w = [&](int st, typename F::Raw (&dst)[R]) {
     const bool ok = st < nstrips && st * kWave + lane < ns;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       BlockLane L = lane_of(st, par[r]);
-      if (!ok) L.o16 = L.o2 = kOut;
+      if (!ok) L.o16 = L.o2 = L.o8 = L.od = kOut;
       F::load(rrs[r], L, dst[r]);
     }
   };
@@ -781,7 +894,7 @@ __global__ __launch_bounds__(kRowWaves * kWave) void gemv_rows_kernel(
     XP xp;
     F::prep(v, xp);
     if (wv * kWave + lane >= ns) xp.inv = 0.0f;  // padding slice
-    put_rec(own, lane, xp, kQ4K);
+    put_rec(own, lane, xp, F::kSum);
     // records first (LDS completes a wave's accesses in order once waited
     // for), then the flag; the memory clobbers keep the compiler's LDS
     // accesses on their side
@@ -802,7 +915,7 @@ __global__ __launch_bounds__(kRowWaves * kWave) void gemv_rows_kernel(
       __builtin_amdgcn_s_sleep(1);
     asm volatile("" ::: "memory");
     XP xp;
-    get_rec(slots + st * kRowSlot, lane, xp, kQ4K);
+    get_rec(slots + st * kRowSlot, lane, xp, F::kSum);
 #pragma unroll
     for (int r = 0; r < R; ++r)
       part[r] = fmaf(F::apply(w[r], lane_of(st, par[r]), xp, j, ac), xp.inv, part[r]);
@@ -842,6 +955,9 @@ __global__ __launch_bounds__(kRowWaves * kWave) void gemv_rows_kernel(
 #define QMAT_GEMV_R_Q4_K 2
 #define QMAT_GEMV_G_Q4_K 8
 #define QMAT_GEMV_D_Q4_K 3
+#define QMAT_GEMV_R_Q6_K 2
+#define QMAT_GEMV_G_Q6_K 4
+#define QMAT_GEMV_D_Q6_K 2
 #endif
 
 #ifndef QMAT_GEMV_ROWS
@@ -862,7 +978,7 @@ hipError_t launch_fmt(const void* blocks, const float* x, float* y, int64_t M, i
     constexpr int RR = QMAT_GEMV_ROW_R;
     const int64_t grid = (M + kRowWaves * RR - 1) / (kRowWaves * RR);
     const size_t lds = (size_t)((ns + kWave - 1) / kWave) * kRowSlot;
-    const bool odd = F::kBytes != 144 && (ns & 1) != 0 && M > 1;
+    const bool odd = (F::row_bytes(K) & 2) != 0 && M > 1;  // rows start 2 mod 4
     if (odd)
       hipLaunchKernelGGL((gemv_rows_kernel<F, RR, RD, true>), dim3((unsigned)grid),
                          dim3(kRowWaves * kWave), lds, stream,
@@ -879,7 +995,7 @@ hipError_t launch_fmt(const void* blocks, const float* x, float* y, int64_t M, i
   const int64_t grid = (M + R * G - 1) / (R * G);
   const size_t lds = (size_t)waves * kXStripBytes;
   // a single row has only the even parity: the aligned variant covers it
-  const bool odd = F::kBytes != 144 && (ns & 1) != 0 && M > 1;
+  const bool odd = (F::row_bytes(K) & 2) != 0 && M > 1;  // rows start 2 mod 4
   if (odd)
     hipLaunchKernelGGL((gemv_kernel<F, R, G, D, true>), dim3((unsigned)grid),
                        dim3(waves * kWave), lds, stream, static_cast<const uint8_t*>(blocks), x,
@@ -1165,7 +1281,7 @@ hipError_t launch_small_fmt(const void* blocks, const void* Xq8, float* Y, int64
   constexpr int G = NT <= 4 ? QMAT_SMALL_G4 : NT <= 8 ? QMAT_SMALL_G8 : QMAT_SMALL_G16;
   const int64_t ns = K / 32;
   const int64_t grid = (M + R * G - 1) / (R * G);
-  const bool odd = F::kBytes != 144 && (ns & 1) != 0 && M > 1;
+  const bool odd = (F::row_bytes(K) & 2) != 0 && M > 1;  // rows start 2 mod 4
   if (odd)
     hipLaunchKernelGGL((gemm_small_kernel<F, R, G, NT, true>), dim3((unsigned)grid),
                        dim3(G * kWave), 0, stream, static_cast<const uint8_t*>(blocks),
@@ -1202,9 +1318,13 @@ hipError_t launch_gemv(int fmt, const void* blocks, const float* x, float* y, in
       return launch_fmt<FmtQ8_0, QMAT_GEMV_R_Q8_0, QMAT_GEMV_G_Q8_0, QMAT_GEMV_D_Q8_0,
                         QMAT_GEMV_ROW_DEPTH_Q8_0>(
           blocks, x, y, M, K, stream);
-    default:
+    case kFmtQ4_K:
       return launch_fmt<FmtQ4_K, QMAT_GEMV_R_Q4_K, QMAT_GEMV_G_Q4_K, QMAT_GEMV_D_Q4_K,
                         QMAT_GEMV_ROW_DEPTH_Q4_K>(
+          blocks, x, y, M, K, stream);
+    default:
+      return launch_fmt<FmtQ6_K, QMAT_GEMV_R_Q6_K, QMAT_GEMV_G_Q6_K, QMAT_GEMV_D_Q6_K,
+                        QMAT_GEMV_ROW_DEPTH_Q6_K>(
           blocks, x, y, M, K, stream);
   }
 }

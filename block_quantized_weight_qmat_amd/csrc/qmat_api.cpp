@@ -20,8 +20,9 @@ bool fmt_ok(int fmt) {
   return fmt == QMAT_Q4_0 || fmt == QMAT_Q8_0 || fmt == QMAT_Q4_K || fmt == QMAT_Q6_K;
 }
 
-// formats the products accept (Q6_K-style: quantize only, so far)
-bool product_fmt_ok(int fmt) { return fmt_ok(fmt) && fmt != QMAT_Q6_K; }
+// formats the prefill product accepts (Q6_K-style: quantize and GEMV only,
+// so far)
+bool gemm_fmt_ok(int fmt) { return fmt_ok(fmt) && fmt != QMAT_Q6_K; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -104,7 +105,7 @@ int qmat_quantize(int fmt, const float* W, void* blocks, int64_t rows, int64_t K
 
 int qmat_gemv(int fmt, const void* blocks, const float* x, float* y, int64_t M, int64_t K,
               void* stream) {
-  if (!product_fmt_ok(fmt)) return QMAT_E_FMT;
+  if (!fmt_ok(fmt)) return QMAT_E_FMT;
   int rc = check_shape(fmt, M, K);
   if (rc != QMAT_OK) return rc;
   if (M == 0) return QMAT_OK;  // nothing to read or write
@@ -116,7 +117,7 @@ int qmat_gemv(int fmt, const void* blocks, const float* x, float* y, int64_t M, 
 
 int qmat_gemm(int fmt, const void* blocks, const void* X_q8, float* Y, int64_t M, int64_t K,
               int64_t N, void* stream) {
-  if (!product_fmt_ok(fmt)) return QMAT_E_FMT;
+  if (!gemm_fmt_ok(fmt)) return QMAT_E_FMT;
   int rc = check_shape(fmt, M, K);
   if (rc != QMAT_OK) return rc;
   if ((rc = check_shape(QMAT_Q8_0, N, K)) != QMAT_OK) return rc;

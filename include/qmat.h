@@ -156,8 +156,7 @@ int qmat_quantize(int fmt, const float *W, void *blocks, int64_t rows,
  *   y[m] = sum_k dequant(W)[m][k] * x[k],  m < M.
  *   [LC05 "带宽决定 Decode"]: every weight byte is read once per token, so
  *   this is bound by HBM bandwidth.
- *   blocks: W in fmt (Q4_0, Q8_0 or Q4_K; Q6_K gives QMAT_E_FMT), M rows
- *   of K.
+ *   blocks: W in fmt (Q4_0, Q8_0, Q4_K or Q6_K), M rows of K.
  *   x: fp32 [K]; y: fp32 [M], overwritten.
  *   Accuracy: relative L2 error against the exact (fp64) product of the
  *   dequantized weights with x is below 1e-3 for finite x; internally each

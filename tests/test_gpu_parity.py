@@ -157,15 +157,15 @@ def gemv_case(q, fmt, W, x):
     return y, ref, B
 
 
-@pytest.mark.parametrize("fmt", [0, 1, 2])
+@pytest.mark.parametrize("fmt", [0, 1, 2, 3])
 def test_gemv_small_and_ragged(q, fmt):
     rng = np.random.default_rng(200 + fmt)
-    shapes = [(1, 256), (3, 512), (17, 2048), (31, 11008 if fmt == 2 else 32 * 345), (70, 4096),
+    shapes = [(1, 256), (3, 512), (17, 2048), (31, 11008 if fmt >= 2 else 32 * 345), (70, 4096),
               (129, 1024), (9, 256 * 40), (6, 256 * 72), (64, 256 * 9), (200, 256 * 43),
               # rows of 256..512 slices take the row-per-wave kernel: its first
               # and last sizes, an odd strip count, and just past its limit
               (33, 8192), (20, 16384), (18, 256 * 33), (7, 256 * 65)]
-    if fmt != 2:
+    if fmt < 2:
         shapes += [(1, 32), (5, 32 * 37), (2, 64), (40, 32 * 1001), (100, 32 * 345),
                    (65, 32 * 1001), (130, 32 * 65), (19, 32 * 257), (21, 32 * 511),
                    (7, 32 * 513)]
@@ -177,7 +177,7 @@ def test_gemv_small_and_ragged(q, fmt):
         assert rel_l2(y, ref) <= GEMV_TOL, (M, K, rel_l2(y, ref))
 
 
-@pytest.mark.parametrize("fmt", [0, 1, 2])
+@pytest.mark.parametrize("fmt", [0, 1, 2, 3])
 def test_gemv_one_hot_gives_the_column(q, fmt):
     rng = np.random.default_rng(300)
     for M, K, k in [(40, 2048, k) for k in (0, 15, 16, 31, 32, 1000, 2047)] + \
@@ -201,7 +201,7 @@ def test_gemv_one_hot_gives_the_column(q, fmt):
         assert np.allclose(y, -3.0 * Wd[:, k], rtol=2 ** -22, atol=0)
 
 
-@pytest.mark.parametrize("fmt", [0, 1, 2])
+@pytest.mark.parametrize("fmt", [0, 1, 2, 3])
 def test_gemv_activation_range(q, fmt):
     """Per-32 power-of-two prescaling keeps any finite x in fp16 range."""
     rng = np.random.default_rng(400)
@@ -258,8 +258,14 @@ def test_gemv_workloads_full(q):
             assert rel_l2(y, ref) <= GEMV_TOL
     for shape in (0, 1):
         W, x = inputs.q4k_rows(shape)
-        say(f"gemv q4k_rows {W.shape}")
-        y, ref, _ = gemv_case(q, 2, W, x)
+        for fmt in (2, 3):
+            say(f"gemv q4k_rows {W.shape} fmt={fmt}")
+            y, ref, _ = gemv_case(q, fmt, W, x)
+            assert rel_l2(y, ref) <= GEMV_TOL
+    for orient in (0, 1):
+        W, x = inputs.llama7b_layer(orient)
+        say(f"gemv llama7b_layer orient={orient} fmt=3")
+        y, ref, _ = gemv_case(q, 3, W, x)
         assert rel_l2(y, ref) <= GEMV_TOL
 
 
