@@ -63,10 +63,10 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_q4_0_llama7b_traffic.json")
 GEMV_SRC = os.path.join(ROOT, "block_quantized_weight_qmat_amd", "csrc", "gemv.hip")
 ALL_OPS = ["quantize_q4_0", "quantize_q8_0", "quantize_q4_k", "gemv_q4_0", "gemv_q8_0",
            "gemv_q4_k", "quantize_act_q8_0", "gemm_q4_0"]
-# the few-token decode batch (qmat_gemm with N <= 48): timed per kernel,
-# not part of the step
+# timed per kernel, not part of the step: the few-token decode batch
+# (qmat_gemm with N <= 48) and the Q6_K-style quantizer and GEMV
 DECODE_NS = (4, 16)
-EXTRA_OPS = [f"decode_q4_0_n{n}" for n in DECODE_NS]
+EXTRA_OPS = [f"decode_q4_0_n{n}" for n in DECODE_NS] + ["quantize_q6_k", "gemv_q6_k"]
 
 
 def parse():
@@ -216,7 +216,7 @@ def main():
     _, X_np = inputs.prefill()
     Wf = torch.from_numpy(W_np).to(dev)
     x = torch.from_numpy(x_np).to(dev)
-    fmts = {"q4_0": 0, "q8_0": 1, "q4_k": 2}
+    fmts = {"q4_0": 0, "q8_0": 1, "q4_k": 2, "q6_k": 3}
     packed = {f: binding.quantize(i, Wf) for f, i in fmts.items()}
     torch.cuda.synchronize()
 

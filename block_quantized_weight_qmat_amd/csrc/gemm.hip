@@ -620,6 +620,8 @@ hipError_t launch_gemm(int fmt, const void* blocks, const void* Xq8, float* Y, i
   // a few tokens: the weights are streamed once per 16 tokens instead (the
   // MFMA tiles would leave most of the GPU idle)
   if (N <= kSmallN) return launch_gemm_small(fmt, blocks, Xq8, Y, M, K, N, stream);
+  // Q6_K-style weights: the decode-batch kernel, 16 tokens per pass over W
+  if (fmt == kFmtQ6_K) return launch_gemm_small(fmt, blocks, Xq8, Y, M, K, N, stream);
   const int64_t tiles_m = (M + kBM - 1) / kBM, tiles_n = (N + kBN - 1) / kBN;
   const int64_t ntiles = tiles_m * tiles_n;
   const unsigned grid = (unsigned)(ntiles < kMaxGrid ? ntiles : kMaxGrid);

@@ -1031,10 +1031,11 @@ hipError_t launch_fmt(const void* blocks, const float* x, float* y, int64_t M, i
 #endif
 
 // 32 int8 codes of a weight block in element order (word i = elements
-// 4i..4i+3), its scale S and, for Q4_K-style, its offset O (weight = S q - O).
+// 4i..4i+3), its scale S and, for Q4_K-style, its offset O (weight = S q - O);
+// for Q6_K-style S scales elements 0..15 and Sb elements 16..31.
 struct WBlk {
   uint32_t w[8];
-  float S, O;
+  float S, O, Sb;
 };
 
 __device__ __forceinline__ uint32_t nib_s8(uint32_t c, int sh) {
@@ -1061,6 +1062,30 @@ __device__ __forceinline__ WBlk unpack_w(const FmtQ8_0::Raw& r, const BlockLane&
 #pragma unroll
   for (int i = 0; i < 8; ++i) b.w[i] = perm_b32(w[i + 1], w[i], L.sel);
   b.S = f16_bits_to_f32(L.mis ? r.s : r.v0.x);
+  b.O = 0.0f;
+  return b;
+}
+
+__device__ __forceinline__ WBlk unpack_w(const FmtQ6_K::Raw& r, const BlockLane& L, int /*j*/) {
+  WBlk b;
+  const uint32_t x[7] = {r.v.x, r.v.y, r.v.z, r.v.w, r.u0, r.u1, (uint32_t)r.s};
+  const uint32_t H[2] = {perm_b32(x[5], x[4], L.sel), perm_b32(x[6], x[5], L.sel)};
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t N = perm_b32(x[w + 1], x[w], L.sel);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      // codes 0..63 of elements 16h+4w.., then c - 32 per byte (c + 96 has
+      // no carry out of its byte; flipping bit 7 then gives c - 32 mod 256)
+      const uint32_t lo = h ? (N >> 4) & 0x0F0F0F0Fu : N & 0x0F0F0F0Fu;
+      const uint32_t c = lo | (((H[h] >> (2 * w)) & 0x03030303u) << 4);
+      b.w[4 * h + w] = (c + 0x60606060u) ^ 0x80808080u;
+    }
+  }
+  const uint32_t scw = L.mis ? (uint32_t)r.s : r.v.x;
+  const float D = f16_bits_to_f32(r.d);
+  b.S = D * (float)(int8_t)(scw & 0xFFu);
+  b.Sb = D * (float)(int8_t)((scw >> 8) & 0xFFu);
   b.O = 0.0f;
   return b;
 }
@@ -1099,6 +1124,7 @@ __global__ __launch_bounds__(G * kWave) void gemm_small_kernel(
     int64_t M, int K, int64_t N, int64_t n0) {
   static_assert((R * NT & (R * NT - 1)) == 0 && R * NT <= kWave, "values per lane");
   constexpr bool kQ4K = F::kBytes == 144;
+  constexpr bool kQ6K = F::kBytes == 210;
   constexpr int kT = G * kWave;
   constexpr int kRecs = (NT * kWave + kT - 1) / kT;  // records a thread stages per strip
   __shared__ __attribute__((aligned(16))) XRecs<NT> xr[2];
@@ -1162,34 +1188,22 @@ __global__ __launch_bounds__(G * kWave) void gemm_small_kernel(
   };
 
   // weight blocks of this wave's R rows, slice (strip * 64 + lane)
-  auto lane_of = [&](int strip, BlockLane (&L)[2]) {
-    const int j = strip * kWave + lane;
-    if (kQ4K) {
-      const uint32_t o = (uint32_t)(j >> 3) * 144u;
-      L[0].o16 = o;
-      L[0].o2 = o + 16u + 16u * (uint32_t)(j & 7);
-      L[0].sel = 0;
-      L[0].mis = false;
-      L[1] = L[0];
-    } else {
-      const uint32_t o = (uint32_t)j * (uint32_t)F::kBytes;
-      L[0] = block_lane(o, 0u, F::kBytes);
-      L[1] = block_lane(o, kOdd ? 2u : 0u, F::kBytes);
-    }
+  // with an odd row stride, row m starts at 2 (m & 1) mod 4 (the lane's
+  // offsets are computed for that parity directly: an array of both would
+  // be indexed at run time and live in scratch memory)
+  auto lane_of = [&](int strip, int r) {
+    return F::lane(strip * kWave + lane, kOdd ? 2u * (uint32_t)((mw + r) & 1) : 0u);
   };
   typename F::Raw wraw[R];
   auto load_w = [&](int strip) {
     if (strip * kWave + lane < ns) {
-      BlockLane L[2];
-      lane_of(strip, L);
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        // with an odd row stride, row m starts at 2 (m & 1) mod 4; rows past
-        // M re-read the last row of the same parity (M >= 2 here)
+        // rows past M re-read the last row of the same parity (M >= 2 here)
         const int p = kOdd ? (int)((mw + r) & 1) : 0;
         int64_t m = mw + r;
         if (m >= M) m = kOdd ? M - 1 - ((M - 1 - p) & 1) : M - 1;
-        F::load(B + m * rb, L[p], wraw[r]);
+        F::load(B + m * rb, lane_of(strip, r), wraw[r]);
       }
     }
   };
@@ -1211,16 +1225,15 @@ __global__ __launch_bounds__(G * kWave) void gemm_small_kernel(
     const bool live = j < ns;
     WBlk wb[R];
     {
-      BlockLane L[2];
-      lane_of(st, L);
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        wb[r] = unpack_w(wraw[r], L[kOdd ? (int)((mw + r) & 1) : 0], j);
+        wb[r] = unpack_w(wraw[r], lane_of(st, r), j);
         if (!live) {
 #pragma unroll
           for (int i = 0; i < 8; ++i) wb[r].w[i] = 0u;
           wb[r].S = 0.0f;
           wb[r].O = 0.0f;
+          wb[r].Sb = 0.0f;
         }
       }
     }
@@ -1243,6 +1256,18 @@ __global__ __launch_bounds__(G * kWave) void gemm_small_kernel(
       const uint32_t xq[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
       for (int r = 0; r < R; ++r) {
+        if (kQ6K) {
+          // two 16-element halves with their own scales
+          int32_t Sa = 0, Sb = 0;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            Sa = sdot4(wb[r].w[i], xq[i], Sa);
+            Sb = sdot4(wb[r].w[4 + i], xq[4 + i], Sb);
+          }
+          acc[r * NT + n] = fmaf((float)Sb * dxv[n & 1], wb[r].Sb,
+                                 fmaf((float)Sa * dxv[n & 1], wb[r].S, acc[r * NT + n]));
+          continue;
+        }
         int32_t S = 0;
 #pragma unroll
         for (int i = 0; i < 8; ++i) S = sdot4(wb[r].w[i], xq[i], S);
@@ -1344,8 +1369,11 @@ hipError_t launch_gemm_small(int fmt, const void* blocks, const void* Xq8, float
       case kFmtQ8_0:
         e = launch_small_chunk<FmtQ8_0>(blocks, Xq8, Y, M, K, N, n0, stream);
         break;
-      default:
+      case kFmtQ4_K:
         e = launch_small_chunk<FmtQ4_K>(blocks, Xq8, Y, M, K, N, n0, stream);
+        break;
+      default:
+        e = launch_small_chunk<FmtQ6_K>(blocks, Xq8, Y, M, K, N, n0, stream);
         break;
     }
     if (e != hipSuccess) return e;

@@ -20,10 +20,6 @@ bool fmt_ok(int fmt) {
   return fmt == QMAT_Q4_0 || fmt == QMAT_Q8_0 || fmt == QMAT_Q4_K || fmt == QMAT_Q6_K;
 }
 
-// formats the prefill product accepts (Q6_K-style: quantize and GEMV only,
-// so far)
-bool gemm_fmt_ok(int fmt) { return fmt_ok(fmt) && fmt != QMAT_Q6_K; }
-
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // A buffer that must exist (non-empty) must be non-NULL and 16-byte aligned.
@@ -117,7 +113,7 @@ int qmat_gemv(int fmt, const void* blocks, const float* x, float* y, int64_t M, 
 
 int qmat_gemm(int fmt, const void* blocks, const void* X_q8, float* Y, int64_t M, int64_t K,
               int64_t N, void* stream) {
-  if (!gemm_fmt_ok(fmt)) return QMAT_E_FMT;
+  if (!fmt_ok(fmt)) return QMAT_E_FMT;
   int rc = check_shape(fmt, M, K);
   if (rc != QMAT_OK) return rc;
   if ((rc = check_shape(QMAT_Q8_0, N, K)) != QMAT_OK) return rc;

@@ -174,17 +174,17 @@ int qmat_gemv(int fmt, const void *blocks, const float *x, float *y,
  *   [LC05 "算力决定 Prefill"]: one weight read serves many tokens, so this
  *   is bound by the matrix cores (int8 MFMA over each 32-element block,
  *   then the two fp16 block scales applied in fp32).
- *   blocks: W in fmt (Q4_0, Q8_0 or Q4_K; Q6_K gives QMAT_E_FMT), M rows
- *   of K.
+ *   blocks: W in fmt (Q4_0, Q8_0, Q4_K or Q6_K), M rows of K.
  *   X_q8: Q8_0 blocks of the activations, N rows of K, exactly as
  *         qmat_quantize(QMAT_Q8_0, X, X_q8, N, K, stream) writes them.
  *   Y: fp32 [N][M] (token-major), overwritten.
  *   K is at most 2^24 here (QMAT_E_SHAPE above that): the kernel addresses
  *   a 128-row tile with 32-bit byte offsets.
- *   Up to 48 tokens (a decode batch) the weights are instead streamed once
- *   per 16 tokens and each weight block is applied to every token's block
- *   with int8 dot products; the arithmetic (exact block sums, the two fp16
- *   block scales applied in fp32) and the accuracy bound are the same.
+ *   Up to 48 tokens (a decode batch), and for Q6_K weights at any N, the
+ *   weights are instead streamed once per 16 tokens and each weight block
+ *   is applied to every token's block with int8 dot products; the
+ *   arithmetic (exact block sums, the fp16 block scales applied in fp32;
+ *   Q6_K: per 16-weight half) and the accuracy bound are the same.
  *   Accuracy: relative L2 error against the exact (fp64) product of the
  *   dequantized operands is below 2e-3; the per-block integer dot products
  *   are exact. Q4_K's min term (dmin*mn_j times the block sums of X_q8) is

@@ -329,12 +329,12 @@ def gemm_case(q, fmt, W, X):
     return Y, ref
 
 
-@pytest.mark.parametrize("fmt", [0, 1, 2])
+@pytest.mark.parametrize("fmt", [0, 1, 2, 3])
 def test_gemm_small_and_ragged(q, fmt):
     rng = np.random.default_rng(500 + fmt)
     shapes = [(96, 1024, 40), (130, 2048, 3), (257, 768, 17), (128, 4096, 64), (1, 256, 1),
               (200, 256 * 9, 130)]
-    if fmt != 2:
+    if fmt < 2:
         shapes += [(1, 32, 1), (33, 32 * 37, 5), (65, 32 * 5, 66)]
     for M, K, N in shapes:
         say(f"gemm fmt={fmt} M={M} K={K} N={N}")
@@ -345,16 +345,16 @@ def test_gemm_small_and_ragged(q, fmt):
         assert rel_l2(Y, ref) <= GEMM_TOL, (M, K, N, rel_l2(Y, ref))
 
 
-@pytest.mark.parametrize("fmt", [0, 1, 2])
+@pytest.mark.parametrize("fmt", [0, 1, 2, 3])
 def test_gemm_decode_small_n(q, fmt):
     """Few-token products (the decode batch path, up to 48 tokens, in chunks
     of 16): every token count around the chunk sizes, odd row strides,
     ragged row counts, and the switch to the MFMA path after 48 tokens."""
     rng = np.random.default_rng(700 + fmt)
-    K1 = 256 * 9 if fmt == 2 else 32 * 345  # odd block count per row (Q4_0/Q8_0)
+    K1 = 256 * 9 if fmt >= 2 else 32 * 345  # odd block count per row
     cases = [(97, K1, n) for n in (1, 2, 3, 4, 5, 7, 8, 9, 15, 16, 17, 31, 33, 48, 49)]
     cases += [(1, 256, 3), (2, 512, 16), (1000, 1024, 4), (33, 2048, 12)]
-    if fmt != 2:
+    if fmt < 2:
         cases += [(5, 32, 2), (64, 32 * 37, 6)]
     for M, K, N in cases:
         say(f"gemm decode fmt={fmt} M={M} K={K} N={N}")
@@ -373,7 +373,7 @@ def test_gemm_decode_full_size_sampled(q):
     M, K = W.shape
     rng = np.random.default_rng(11)
     Xs = rng.normal(0, 1, (48, K)).astype(np.float32)
-    for fmt in (0, 1, 2):
+    for fmt in (0, 1, 2, 3):
         dW = q.quantize(fmt, dev_tensor(W))
         Bh = host(dW)
         rb = oracle.row_bytes(fmt, K)
@@ -412,7 +412,7 @@ def test_prefill_full_size_sampled(q):
     B, Xq = host(dB), host(dXq)
     assert np.array_equal(B, oracle.quantize(0, W))
     assert np.array_equal(Xq, oracle.quantize(1, X))
-    for fmt in (0, 1, 2):
+    for fmt in (0, 1, 2, 3):
         say(f"prefill full gemm fmt={fmt}")
         if fmt == 0:
             dW = dB
