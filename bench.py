@@ -64,9 +64,9 @@ GEMV_SRC = os.path.join(ROOT, "block_quantized_weight_qmat_amd", "csrc", "gemv.h
 ALL_OPS = ["quantize_q4_0", "quantize_q8_0", "quantize_q4_k", "gemv_q4_0", "gemv_q8_0",
            "gemv_q4_k", "quantize_act_q8_0", "gemm_q4_0"]
 # timed per kernel, not part of the step: the few-token decode batch
-# (qmat_gemm with N <= 48) and the Q6_K-style quantizer and GEMV
+# (qmat_gemm with N <= 48) and the Q6_K-style quantizer, GEMV and GEMM
 DECODE_NS = (4, 16)
-EXTRA_OPS = [f"decode_q4_0_n{n}" for n in DECODE_NS] + ["quantize_q6_k", "gemv_q6_k"]
+EXTRA_OPS = [f"decode_q4_0_n{n}" for n in DECODE_NS] + ["quantize_q6_k", "gemv_q6_k", "gemm_q6_k"]
 
 
 def parse():
@@ -254,6 +254,7 @@ def main():
             i, cold[f][s % len(cold[f])], x, M, K, out=y[f])
     table["quantize_act_q8_0"] = lambda s: binding.quantize(1, X_rot[s % len(X_rot)], out=Xq)
     table["gemm_q4_0"] = lambda s: binding.gemm(0, packed["q4_0"], Xq, M, K, N, out=Y)
+    table["gemm_q6_k"] = lambda s: binding.gemm(3, packed["q6_k"], Xq, M, K, N, out=Y)
     for n in DECODE_NS:
         table[f"decode_q4_0_n{n}"] = lambda s, n=n: binding.gemm(
             0, cold["q4_0"][s % len(cold["q4_0"])], Xq_dec[n], M, K, n, out=Y_dec[n])

@@ -10,6 +10,8 @@
 //   Y[n][m] += dw[m,b] * dx[n,b] * S[m,n,b]                 (fp32, VALU)
 // wq is the signed code (c - 8) for Q4_0, q for Q8_0, and the unsigned code q
 // for Q4_K-style, whose per-sub-block offset adds -O[m,b] * dx[n,b] * sum(xq).
+// Q6_K-style blocks (wq = c - 32) have a scale per 16-element half: each half
+// is its own MFMA (the other half's operand lanes zeroed) and scaled alone.
 //
 // Scale step in two fp32 FMAs per element: the MFMA accumulates onto the
 // integer constant 0x4B400000, the bit pattern of 1.5 * 2^23, so its int32
@@ -291,16 +293,26 @@ template <int FMT, int kLT>
 struct TileLoader {
   static constexpr int kWItems = kBM * kKB / kLT;
   static constexpr int kXItems = kBN * kKB / kLT;
-  static constexpr int wbytes = FMT == kFmtQ4_0 ? 18 : FMT == kFmtQ8_0 ? 34 : 144;
-  static constexpr int stage_wbytes = FMT == kFmtQ4_K ? 144 : kKB * wbytes;
+  static constexpr bool kQ6K = FMT == kFmtQ6_K;
+  static constexpr int wbytes = FMT == kFmtQ4_0 ? 18 : FMT == kFmtQ8_0 ? 34 : FMT == kFmtQ4_K ? 144 : 210;
+  // a stage is 8 blocks: one superblock for Q4_K/Q6_K
+  static constexpr int stage_wbytes = FMT == kFmtQ4_K || kQ6K ? wbytes : kKB * wbytes;
   struct Regs {
-    u32x4 wa[kWItems], wb[kWItems];  // Q8_0: 2 x 16 B; Q4_0: 16 B; Q4_K: header, codes
-    uint32_t ws[kWItems];            // 2-byte piece (Q4_0/Q8_0)
+    u32x4 wa[kWItems], wb[kWItems];  // Q8_0: 2 x 16 B; Q4_0: 16 B; Q4_K: header, codes;
+                                     // Q6_K: 16 B and (in wb.x, wb.y) 8 B of the group
+    uint32_t ws[kWItems];            // 2-byte piece (Q4_0/Q8_0/Q6_K)
+    uint32_t wdd[kWItems];           // Q6_K: the superblock's fp16 d
     u32x4 xa[kXItems], xb[kXItems];
     uint32_t xs[kXItems];
   };
   BlkLane wl[kWItems], xl[kXItems];
   int tid, nb;
+  // Q6_K group of an item: its 26 bytes start at wl.o16 (relative to the
+  // stage base) and are 2 mod 4 in even stages when wl.sel is 1; a stage is
+  // 210 bytes, so odd stages flip that
+  __device__ __forceinline__ static bool q6_mis(const BlkLane& l, int s) {
+    return (l.sel ^ (uint32_t)(s & 1)) != 0;
+  }
 
   __device__ __forceinline__ void setup(int64_t M, int64_t N, int64_t m0, int64_t n0,
                                         int64_t wrb, int64_t xrb, int tid_, int nb_) {
@@ -319,6 +331,11 @@ struct TileLoader {
         wl[it].o16 = ro;                                    // superblock header
         wl[it].o2 = ro + 16u + 16u * (uint32_t)(item & 7);  // sub-block codes
         wl[it].sel = 0u;
+        wl[it].hsel = 0u;
+      } else if (kQ6K) {
+        wl[it].o16 = ro + 2u + 26u * (uint32_t)(item & 7);  // the group's bytes
+        wl[it].o2 = ro;                                     // d
+        wl[it].sel = ((wl[it].o16 + wpar) & 2u) != 0 ? 1u : 0u;
         wl[it].hsel = 0u;
       } else {
         wl[it] = blk_lane(ro + (uint32_t)(item & 7) * (uint32_t)wbytes, wpar, wbytes);
@@ -345,6 +362,18 @@ struct TileLoader {
         if (FMT == kFmtQ4_K) {
           r.wa[it] = __builtin_amdgcn_raw_buffer_load_b128(wrs, wl[it].o16, wso, 0);
           r.wb[it] = __builtin_amdgcn_raw_buffer_load_b128(wrs, wl[it].o2, wso, 0);
+        } else if (kQ6K) {
+          // group bytes [G, G + 26): aligned: 16 at G, 8 at G + 16, 2 at
+          // G + 24; else 2 at G, 16 at G + 2, 8 at G + 18
+          const uint32_t G = wl[it].o16;
+          const bool mis = q6_mis(wl[it], s);
+          r.wa[it] = __builtin_amdgcn_raw_buffer_load_b128(wrs, mis ? G + 2u : G, wso, 0);
+          const uint2 u = __builtin_bit_cast(
+              uint2, __builtin_amdgcn_raw_buffer_load_b64(wrs, mis ? G + 18u : G + 16u, wso, 0));
+          r.wb[it].x = u.x;
+          r.wb[it].y = u.y;
+          r.ws[it] = __builtin_amdgcn_raw_buffer_load_b16(wrs, mis ? G : G + 24u, wso, 0);
+          r.wdd[it] = __builtin_amdgcn_raw_buffer_load_b16(wrs, wl[it].o2, wso, 0);
         } else {
           load_lane(wrs, wso, wl[it], wbytes, r.wa[it], r.wb[it], r.ws[it]);
         }
@@ -377,6 +406,30 @@ struct TileLoader {
           store16(dst.w(bb, 0, rr), c[0], c[1], c[2], c[3]);
           store16(dst.w(bb, 1, rr), c[4], c[5], c[6], c[7]);
           dst.wd[bb][rr] = f16_bits_to_f32(h);
+        } else if (kQ6K) {
+          // realign the group: 16 nibble bytes N, then H0, H1; codes
+          // c = lo | hi << 4 become c - 32 per byte (c + 96 has no carry
+          // out of its byte; flipping bit 7 gives c - 32 mod 256)
+          const bool mis = q6_mis(wl[it], s);
+          const uint32_t sel = mis ? 0x03020100u : 0x05040302u;
+          const uint32_t x[7] = {r.wa[it].x, r.wa[it].y, r.wa[it].z, r.wa[it].w,
+                                 r.wb[it].x, r.wb[it].y, r.ws[it]};
+          const uint32_t H0 = perm_b32(x[5], x[4], sel), H1 = perm_b32(x[6], x[5], sel);
+          uint32_t qa[4], qb[4];
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const uint32_t N = perm_b32(x[w + 1], x[w], sel);
+            const uint32_t ca = (N & 0x0F0F0F0Fu) | (((H0 >> (2 * w)) & 0x03030303u) << 4);
+            const uint32_t cb = ((N >> 4) & 0x0F0F0F0Fu) | (((H1 >> (2 * w)) & 0x03030303u) << 4);
+            qa[w] = (ca + 0x60606060u) ^ 0x80808080u;
+            qb[w] = (cb + 0x60606060u) ^ 0x80808080u;
+          }
+          store16(dst.w(bb, 0, rr), qa[0], qa[1], qa[2], qa[3]);
+          store16(dst.w(bb, 1, rr), qb[0], qb[1], qb[2], qb[3]);
+          const uint32_t scw = mis ? r.ws[it] : r.wa[it].x;
+          const float D = f16_bits_to_f32(r.wdd[it]);
+          dst.wd[bb][rr] = D * (float)(int8_t)(scw & 0xFFu);          // elements 0..15
+          dst.wo[bb][rr] = D * (float)(int8_t)((scw >> 8) & 0xFFu);   // elements 16..31
         } else {
           const u32x4 hd = r.wa[it], cv = r.wb[it];
           const int sub = bb;  // a stage is one superblock
@@ -418,11 +471,49 @@ struct TileLoader {
 
 // One K-stage of a wave's NT 32 x 32 tiles (rows 32 wm.., column tiles
 // wn0..) from LDS into the fp32 accumulators; nbs blocks of the stage exist.
+// Q6_K-style stage: per block, the MFMA of each 16-element half (lanes of
+// the other half give zero weight operands: the products pair operand bytes
+// of the same lane half, which hold the same elements on both sides), each
+// scaled by its own row scale.
+template <int NT>
+__device__ __forceinline__ void compute_stage_q6(const Stage& cur, int nbs, int wm, int wn0,
+                                                 int l32, int half, const i32x16& cmagic,
+                                                 float (&acc)[NT][16]) {
+  for (int bb = 0; bb < nbs; ++bb) {
+    Ops<NT> op;
+    load_ops(cur, bb, wm, wn0, l32, half, op);
+    const i32x4 z = {0, 0, 0, 0};
+    const i32x4 a0 = half == 0 ? op.a : z, a1 = half == 0 ? z : op.a;
+    i32x16 d0[NT], d1[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      d0[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, op.b[t], cmagic, 0, 0, 0);
+      d1[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, op.b[t], cmagic, 0, 0, 0);
+    }
+    Scales<NT> sc0, sc1;
+    load_scales(cur, bb, wm, wn0, l32, half, sc0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f32x4 t = *reinterpret_cast<const f32x4*>(&cur.wo[bb][wm * 32 + 8 * q + 4 * half]);
+      sc1.dw[4 * q + 0] = t.x;
+      sc1.dw[4 * q + 1] = t.y;
+      sc1.dw[4 * q + 2] = t.z;
+      sc1.dw[4 * q + 3] = t.w;
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) sc1.dx[t] = sc0.dx[t];
+    apply_scales(sc0, d0, acc);
+    apply_scales(sc1, d1, acc);
+  }
+}
+
 template <int FMT, int NT>
 __device__ __forceinline__ void compute_stage(const Stage& cur, int nbs, int wm, int wn0,
                                               int l32, int half, const i32x16& cmagic,
                                               float (&acc)[NT][16]) {
-  if (nbs == kKB) {
+  if (FMT == kFmtQ6_K) {
+    compute_stage_q6<NT>(cur, nbs, wm, wn0, l32, half, cmagic, acc);
+  } else if (nbs == kKB) {
     // Full stage, software-pipelined: the column scales of all 8 blocks are
     // read up front; in step bb the MFMAs of block bb+1 are issued
     // (operands read one step earlier), the operands of block bb+2 and the
@@ -537,7 +628,8 @@ __global__ __launch_bounds__(kThreads + kLoadThreads) void gemm_kernel(
   const int l32 = lane & 31;
   const int nb = K >> 5;  // 32-element blocks along K
   const int nstage = (nb + kKB - 1) / kKB;
-  const int64_t wrb = FMT == kFmtQ4_K ? (int64_t)(K >> 8) * 144 : (int64_t)nb * TL::wbytes;
+  const int64_t wrb = FMT == kFmtQ4_K || FMT == kFmtQ6_K ? (int64_t)(K >> 8) * TL::wbytes
+                                                          : (int64_t)nb * TL::wbytes;
   const int64_t xrb = (int64_t)nb * 34;
   const int64_t lin = first_tile(ntiles);
 
@@ -620,8 +712,6 @@ hipError_t launch_gemm(int fmt, const void* blocks, const void* Xq8, float* Y, i
   // a few tokens: the weights are streamed once per 16 tokens instead (the
   // MFMA tiles would leave most of the GPU idle)
   if (N <= kSmallN) return launch_gemm_small(fmt, blocks, Xq8, Y, M, K, N, stream);
-  // Q6_K-style weights: the decode-batch kernel, 16 tokens per pass over W
-  if (fmt == kFmtQ6_K) return launch_gemm_small(fmt, blocks, Xq8, Y, M, K, N, stream);
   const int64_t tiles_m = (M + kBM - 1) / kBM, tiles_n = (N + kBN - 1) / kBN;
   const int64_t ntiles = tiles_m * tiles_n;
   const unsigned grid = (unsigned)(ntiles < kMaxGrid ? ntiles : kMaxGrid);
@@ -637,8 +727,11 @@ hipError_t launch_gemm(int fmt, const void* blocks, const void* Xq8, float* Y, i
     case kFmtQ8_0:
       QMAT_GEMM_LAUNCH(kFmtQ8_0);
       break;
-    default:
+    case kFmtQ4_K:
       QMAT_GEMM_LAUNCH(kFmtQ4_K);
+      break;
+    default:
+      QMAT_GEMM_LAUNCH(kFmtQ6_K);
       break;
   }
 #undef QMAT_GEMM_LAUNCH
