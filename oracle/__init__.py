@@ -80,6 +80,8 @@ class Oracle:
         lib.oracle_gemv.restype = ctypes.c_int
         lib.oracle_gemm.argtypes = [ctypes.c_int, p, p, p, i64, i64, i64]
         lib.oracle_gemm.restype = ctypes.c_int
+        lib.oracle_kv_write.argtypes = [ctypes.c_int, p, p, p, i64, i64, i64, i64]
+        lib.oracle_kv_write.restype = ctypes.c_int
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = ctypes.c_int
         self.lib = lib
@@ -169,6 +171,23 @@ class Oracle:
         if rc != 0:
             raise ValueError(f"oracle_gemm failed ({rc})")
         return Y
+
+
+    def kv_write(self, fmt, rows: np.ndarray, bias, cache: np.ndarray, cell0: int) -> np.ndarray:
+        """Quantize rows [n][dim] (minus bias [dim] if given) into a copy of
+        cache (uint8 [cells][row_bytes]) at rows cell0..; returns the copy."""
+        f = _fmt(fmt)
+        rows = np.ascontiguousarray(rows, dtype=np.float32)
+        n, dim = rows.shape
+        out = np.array(cache, dtype=np.uint8, copy=True, order="C")
+        cells = out.shape[0]
+        assert out.shape[1] == self.row_bytes(f, dim)
+        b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
+        rc = self.lib.oracle_kv_write(f, _ptr(rows), None if b is None else _ptr(b), _ptr(out),
+                                      cell0, n, cells, dim)
+        if rc != 0:
+            raise ValueError(f"oracle_kv_write failed ({rc})")
+        return out
 
 
 _default = None

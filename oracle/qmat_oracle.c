@@ -17,7 +17,8 @@
  *          weight a 4-bit integer, 18 bytes per block.
  *   [KVQ]  lpnh.cn KV-cache article, section "kv-mean-center 进阶技巧",
  *          paragraph "问题": Q4_0 is symmetric, value ≈ scale × q, with no
- *          zero point.
+ *          zero point; the same section subtracts a fixed per-channel bias
+ *          from K before it is quantized into the cache.
  *   [BARE] xdnf.cn llama.cpp article, section 3.2: its dequant snippet reads
  *          the fp16 parameters first, then 16 code bytes whose low nibbles
  *          are the block's first 16 elements and high nibbles the last 16,
@@ -348,6 +349,32 @@ int oracle_quantize(int fmt, const float *W, uint8_t *out, int64_t rows,
       else if (fmt == ORC_Q8_0) quant_q8_0_block(x, blk);
       else if (fmt == ORC_Q4_K) quant_q4_k_block(x, blk);
       else quant_q6_k_block(x, blk);
+    }
+  }
+  return 0;
+}
+
+/* KV-cache write ([KVQ] section "量化 KV Cache 的一键配置方法": K and V are
+ * stored as q8_0 or q4_0 blocks; section "kv-mean-center 进阶技巧": a fixed
+ * per-(head, channel) bias is subtracted from K before Q4_0 quantization).
+ * Row i of `rows` ([n][dim] fp32), minus `bias` ([dim], fp32 subtraction)
+ * when given, is quantized into cache row cell0 + i; every other cache byte
+ * is left as it was. Returns 0, or -1 for a bad format or shape. */
+int oracle_kv_write(int fmt, const float *rows, const float *bias, uint8_t *cache,
+                    int64_t cell0, int64_t n, int64_t cells, int64_t dim) {
+  if (fmt != ORC_Q4_0 && fmt != ORC_Q8_0) return -1;
+  if (dim < 0 || dim % 32 != 0 || n < 0 || cell0 < 0 || cell0 + n > cells) return -1;
+  int64_t nb = dim / 32, bb = oracle_block_bytes(fmt);
+  float x[32];
+  for (int64_t i = 0; i < n; ++i) {
+    for (int64_t b = 0; b < nb; ++b) {
+      for (int e = 0; e < 32; ++e) {
+        float v = rows[i * dim + b * 32 + e];
+        x[e] = bias ? v - bias[b * 32 + e] : v;
+      }
+      uint8_t *blk = cache + ((cell0 + i) * nb + b) * bb;
+      if (fmt == ORC_Q4_0) quant_q4_0_block(x, blk);
+      else quant_q8_0_block(x, blk);
     }
   }
   return 0;

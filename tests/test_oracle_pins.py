@@ -636,13 +636,96 @@ def test_on_grid_products(orc):
     pin_on_grid_products(orc)
 
 
+# ------------------------------------------------------------ KV cache --
+
+def _q4_0_pack(D, q):
+    """Q4_0 blocks from the layout text (fp16 scale, byte t = code t | code
+    t+16 << 4, code = q + 8) for scales D [nblk] and integers q [nblk][32]."""
+    out = bytearray()
+    for d, qq in zip(D, q):
+        c = [int(v) + 8 for v in qq]
+        out += np.float16(d).tobytes() + bytes(c[t] | (c[t + 16] << 4) for t in range(16))
+    return np.frombuffer(bytes(out), dtype=np.uint8)
+
+
+def pin_kv_write(orc: Oracle):
+    """KV rows written as Q4_0/Q8_0 blocks at their cells, minus the
+    per-channel bias when one is given; other cells untouched."""
+    rng = np.random.default_rng(31)
+    dim, cells, n, cell0 = 256, 9, 4, 3
+    # rows = bias + D q exactly, |q| = 7 present in every block: centred, the
+    # quantizer must return exactly D and q (lpnh.cn KV-cache article, section
+    # kv-mean-center 进阶技巧: subtract the fixed bias before Q4_0 quantization)
+    bias = rng.integers(-128, 129, dim) * 2.0 ** -4
+    D = 2.0 ** -rng.integers(5, 9, (n, dim // 32))
+    q = rng.integers(-7, 8, (n, dim // 32, 32))
+    q[:, :, 0] = 7 * rng.choice([-1, 1], (n, dim // 32))
+    rows = (bias.reshape(1, -1) + (D[..., None] * q).reshape(n, dim))
+    assert np.array_equal(rows.astype(np.float32).astype(np.float64), rows)
+    cache = rng.integers(0, 256, (cells, orc.row_bytes(Q4_0, dim)), dtype=np.uint8)
+    out = orc.kv_write(Q4_0, rows.astype(np.float32), bias.astype(np.float32), cache, cell0)
+    want = _q4_0_pack(D.reshape(-1), q.reshape(-1, 32)).reshape(n, -1)
+    assert np.array_equal(out[cell0:cell0 + n], want)
+    keep = np.r_[0:cell0, cell0 + n:cells]
+    assert np.array_equal(out[keep], cache[keep])
+    # without a bias the rows are quantized as they are
+    for fmt in (Q4_0, Q8_0):
+        c0 = np.zeros((cells, orc.row_bytes(fmt, dim)), np.uint8)
+        o2 = orc.kv_write(fmt, rows.astype(np.float32), None, c0, 0)
+        assert np.array_equal(orc.dequant(fmt, o2[:n], n, dim),
+                              orc.dequant(fmt, orc.quantize(fmt, rows.astype(np.float32)), n, dim))
+    # shapes and formats outside the contract are refused
+    for bad in (lambda: orc.kv_write(Q4_K, np.zeros((1, 256), np.float32), None,
+                                     np.zeros((2, orc.row_bytes(Q4_K, 256)), np.uint8), 0),
+                lambda: orc.kv_write(Q8_0, np.zeros((2, 64), np.float32), None,
+                                     np.zeros((2, orc.row_bytes(Q8_0, 64)), np.uint8), 1)):
+        with pytest.raises(ValueError):
+            bad()
+
+
+def pin_kv_mean_center(orc: Oracle):
+    """The article's argument for the bias: a query's scores against the
+    centred keys differ from the raw ones by the same constant q.k_mean for
+    every key, and softmax ignores a constant added to a row; and centring
+    channels with a large mean shrinks the Q4_0 error."""
+    rng = np.random.default_rng(41)
+    nk, dim = 50, 128
+    mean = rng.normal(0, 4, dim)
+    K = (mean + rng.normal(0, 0.3, (nk, dim))).astype(np.float32)
+    qv = rng.normal(0, 1, (7, dim))
+    def softmax(z):
+        z = z - z.max(axis=1, keepdims=True)
+        e = np.exp(z)
+        return e / e.sum(axis=1, keepdims=True)
+    s_raw = qv @ K.astype(np.float64).T
+    s_cen = qv @ (K.astype(np.float64) - mean).T
+    assert np.allclose(s_raw - s_cen, (qv @ mean)[:, None], rtol=1e-12, atol=1e-9)
+    assert np.allclose(softmax(s_raw), softmax(s_cen), rtol=1e-10, atol=1e-15)
+    bias = mean.astype(np.float32)
+    c = np.zeros((nk, orc.row_bytes(Q4_0, dim)), np.uint8)
+    raw = orc.dequant(Q4_0, orc.kv_write(Q4_0, K, None, c, 0), nk, dim)
+    cen = orc.dequant(Q4_0, orc.kv_write(Q4_0, K, bias, c, 0), nk, dim) + bias
+    e_raw = np.linalg.norm(raw - K)
+    e_cen = np.linalg.norm(cen - K)
+    assert e_cen < e_raw / 5, (e_cen, e_raw)
+
+
+def test_kv_write(orc):
+    pin_kv_write(orc)
+
+
+def test_kv_mean_center(orc):
+    pin_kv_mean_center(orc)
+
+
 # ---------------------------------------------------------- planted mistakes
 
 ALL_PINS = [pin_f16_decode_all, pin_f16_encode_sweep, pin_block_sizes,
             pin_qwen3_file_sizes, pin_golden_blocks, pin_q4k_layout,
             pin_q6k_layout, pin_round_trip_bound, pin_code_optimality,
             pin_idempotence, pin_exact_grid, pin_q6k_exact_grid, pin_zero_blocks,
-            pin_gemv_special_cases, pin_brute_force_4x64, pin_on_grid_products]
+            pin_gemv_special_cases, pin_brute_force_4x64, pin_on_grid_products,
+            pin_kv_write, pin_kv_mean_center]
 
 MUTANTS = {
     "nibble_order_swapped": ("blk[2 + t] = (uint8_t)(code[t] | (code[t + 16] << 4));",
@@ -668,6 +751,9 @@ MUTANTS = {
     "q6k_high_bits_words_swapped": ("int hi = (grp[18 + 4 * half + b] >> (2 * w)) & 3;",
                                     "int hi = (grp[22 - 4 * half + b] >> (2 * w)) & 3;"),
     "q6k_one_scale_per_group": ("memcpy(&sc, grp + (e >> 4), 1);", "memcpy(&sc, grp, 1);"),
+    "kv_bias_added": ("x[e] = bias ? v - bias[b * 32 + e] : v;", "x[e] = bias ? v + bias[b * 32 + e] : v;"),
+    "kv_cell_offset_ignored": ("uint8_t *blk = cache + ((cell0 + i) * nb + b) * bb;",
+                               "uint8_t *blk = cache + (i * nb + b) * bb;"),
     "gemv_drops_last_element": ("for (int64_t k = 0; k < K; ++k) s += w[k] * (double)x[k];",
                                 "for (int64_t k = 0; k + 1 < K; ++k) s += w[k] * (double)x[k];"),
     "gemm_transposed_store": ("Y[n * M + m] = s;", "Y[(m * N + n) % (M * N)] = s;"),
