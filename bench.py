@@ -64,9 +64,14 @@ GEMV_SRC = os.path.join(ROOT, "block_quantized_weight_qmat_amd", "csrc", "gemv.h
 ALL_OPS = ["quantize_q4_0", "quantize_q8_0", "quantize_q4_k", "gemv_q4_0", "gemv_q8_0",
            "gemv_q4_k", "quantize_act_q8_0", "gemm_q4_0"]
 # timed per kernel, not part of the step: the few-token decode batch
-# (qmat_gemm with N <= 48) and the Q6_K-style quantizer, GEMV and GEMM
+# (qmat_gemm with N <= 48), the Q6_K-style quantizer, GEMV and GEMM, and
+# the KV-cache write of a 512-token prefill (dim 1024: 8 KV heads of 128)
+# into a 16384-cell cache, Q4_0 with the per-channel bias and Q8_0 without
+KV_DIM, KV_CELLS, KV_N = 1024, 16384, 512
 DECODE_NS = (4, 16)
-EXTRA_OPS = [f"decode_q4_0_n{n}" for n in DECODE_NS] + ["quantize_q6_k", "gemv_q6_k", "gemm_q6_k"]
+EXTRA_OPS = [f"decode_q4_0_n{n}" for n in DECODE_NS] + ["quantize_q6_k", "gemv_q6_k", "gemm_q8_0",
+                                                         "gemm_q4_k", "gemm_q6_k",
+                                                         "kv_write_q4_0", "kv_write_q8_0"]
 
 
 def parse():
@@ -254,7 +259,20 @@ def main():
             i, cold[f][s % len(cold[f])], x, M, K, out=y[f])
     table["quantize_act_q8_0"] = lambda s: binding.quantize(1, X_rot[s % len(X_rot)], out=Xq)
     table["gemm_q4_0"] = lambda s: binding.gemm(0, packed["q4_0"], Xq, M, K, N, out=Y)
-    table["gemm_q6_k"] = lambda s: binding.gemm(3, packed["q6_k"], Xq, M, K, N, out=Y)
+    # the other formats write elsewhere: the Q4_0 parity check below reads Y
+    Yx = torch.empty_like(Y) if any(need(f"gemm_{f}") for f in ("q8_0", "q4_k", "q6_k")) else Y
+    for f, i in (("q8_0", 1), ("q4_k", 2), ("q6_k", 3)):
+        table[f"gemm_{f}"] = lambda s, f=f, i=i: binding.gemm(i, packed[f], Xq, M, K, N, out=Yx)
+    kv_rows = X_rot[0][:KV_N, :KV_DIM].contiguous()
+    kv_bias = X_rot[0][0, KV_DIM:2 * KV_DIM].contiguous()
+    kv_cache = {f: torch.empty((KV_CELLS, binding.row_bytes(i, KV_DIM)), dtype=torch.uint8,
+                               device=dev) for f, i in (("q4_0", 0), ("q8_0", 1))}
+    kv_bytes = {f: 4 * KV_N * KV_DIM + (4 * KV_DIM if f == "q4_0" else 0)
+                + KV_N * binding.row_bytes(i, KV_DIM) for f, i in (("q4_0", 0), ("q8_0", 1))}
+    table["kv_write_q4_0"] = lambda s: binding.kv_write(
+        0, kv_rows, kv_cache["q4_0"], (s * KV_N) % (KV_CELLS - KV_N), bias=kv_bias)
+    table["kv_write_q8_0"] = lambda s: binding.kv_write(
+        1, kv_rows, kv_cache["q8_0"], (s * KV_N) % (KV_CELLS - KV_N))
     for n in DECODE_NS:
         table[f"decode_q4_0_n{n}"] = lambda s, n=n: binding.gemm(
             0, cold["q4_0"][s % len(cold["q4_0"])], Xq_dec[n], M, K, n, out=Y_dec[n])
@@ -284,6 +302,11 @@ def main():
             f = name[5:]
             gbs = gemv_bytes[f] / us / 1e3
             kernels[name] = {"us": us, "bytes": gemv_bytes[f], "GB/s": gbs, "bound": "hbm",
+                             "frac": gbs / HBM_PEAK_GBS}
+        elif name.startswith("kv_write_"):
+            f = name[9:]
+            gbs = kv_bytes[f] / us / 1e3
+            kernels[name] = {"us": us, "bytes": kv_bytes[f], "GB/s": gbs, "bound": "hbm",
                              "frac": gbs / HBM_PEAK_GBS}
         elif name.startswith("quantize_act"):
             gbs = actq_bytes / us / 1e3

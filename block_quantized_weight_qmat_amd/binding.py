@@ -57,6 +57,8 @@ def load_library():
     lib.qmat_gemv.restype = i32
     lib.qmat_gemm.argtypes = [i32, p, p, p, i64, i64, i64, p]
     lib.qmat_gemm.restype = i32
+    lib.qmat_kv_write.argtypes = [i32, p, p, p, i64, i64, i64, i64, p]
+    lib.qmat_kv_write.restype = i32
     _lib = lib
     return lib
 
@@ -154,3 +156,27 @@ def gemm(fmt, blocks: torch.Tensor, Xq: torch.Tensor, M: int, K: int, N: int,
     _check("qmat_gemm", load_library().qmat_gemm(
         f, blocks.data_ptr(), Xq.data_ptr(), out.data_ptr(), M, K, N, _stream(Xq)))
     return out
+
+
+def kv_write(fmt, rows: torch.Tensor, cache: torch.Tensor, cell0: int,
+             bias: torch.Tensor | None = None) -> torch.Tensor:
+    """Quantize rows [n, dim] (minus bias [dim] if given) into cache rows
+    cell0 .. cell0 + n - 1 (cache: uint8 [cells, row_bytes(fmt, dim)])."""
+    f = _fmt(fmt)
+    _gpu(rows, "rows", torch.float32)
+    _gpu(cache, "cache", torch.uint8)
+    if rows.dim() != 2 or cache.dim() != 2:
+        raise ValueError("rows and cache must be 2-D")
+    n, dim = rows.shape
+    if cache.shape[1] != row_bytes(f, dim):
+        raise ValueError("cache rows do not match fmt and dim")
+    bp = 0
+    if bias is not None:
+        _gpu(bias, "bias", torch.float32)
+        if bias.numel() != dim:
+            raise ValueError("bias must hold dim values")
+        bp = bias.data_ptr()
+    _check("qmat_kv_write", load_library().qmat_kv_write(
+        f, rows.data_ptr(), bp or None, cache.data_ptr(), int(cell0), n, cache.shape[0], dim,
+        _stream(rows)))
+    return cache

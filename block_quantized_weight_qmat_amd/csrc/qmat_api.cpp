@@ -126,4 +126,20 @@ int qmat_gemm(int fmt, const void* blocks, const void* X_q8, float* Y, int64_t M
       qmat::launch_gemm(fmt, blocks, X_q8, Y, M, K, N, static_cast<hipStream_t>(stream)));
 }
 
+int qmat_kv_write(int fmt, const float* rows, const float* bias, void* cache, int64_t cell0,
+                  int64_t n, int64_t cells, int64_t dim, void* stream) {
+  if (fmt != QMAT_Q4_0 && fmt != QMAT_Q8_0) return QMAT_E_FMT;
+  int rc = check_shape(fmt, cells, dim);
+  if (rc != QMAT_OK) return rc;
+  if (n < 0 || cell0 < 0 || n > cells || cell0 > cells - n) return QMAT_E_SHAPE;
+  if (n == 0 || dim == 0) return QMAT_OK;  // nothing to read or write
+  if ((rc = check_buf(rows, true)) != QMAT_OK) return rc;
+  if (cache == nullptr) return QMAT_E_NULL;
+  void* dst = static_cast<uint8_t*>(cache) + cell0 * qmat_row_bytes(fmt, dim);
+  if ((rc = check_buf(dst, true)) != QMAT_OK) return rc;
+  if (bias != nullptr && (rc = check_buf(bias, true)) != QMAT_OK) return rc;
+  return hip_status(
+      qmat::launch_kv_write(fmt, rows, bias, dst, n, dim, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -15,6 +15,11 @@ constexpr int kFmtQ6_K = 3;
 hipError_t launch_quantize(int fmt, const float* W, void* blocks, int64_t rows, int64_t K,
                            hipStream_t stream);
 
+// KV-cache write: n rows of dim elements, minus bias when non-null, as Q4_0
+// or Q8_0 rows at dst (16-byte aligned).
+hipError_t launch_kv_write(int fmt, const float* rows, const float* bias, void* dst, int64_t n,
+                           int64_t dim, hipStream_t stream);
+
 hipError_t launch_gemv(int fmt, const void* blocks, const float* x, float* y, int64_t M,
                        int64_t K, hipStream_t stream);
 

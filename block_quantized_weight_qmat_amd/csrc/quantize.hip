@@ -77,13 +77,18 @@ __device__ __forceinline__ float div_shared(float a, float b, float y) {
 
 // Q4_0 (kQ4 = true) or Q8_0 (false): one lane per 32-element block, 64
 // blocks per wave. The packed blocks of a wave are assembled in LDS and
-// written out with 16-byte stores.
-template <bool kQ4>
-__global__ __launch_bounds__(kQThreads) void quantize_b32_kernel(
-    const float* __restrict__ W, uint8_t* __restrict__ out, int64_t nblocks) {
+// written out with 16-byte stores. With a bias (the KV-cache write), element
+// e of block g is x - bias[32 (g % nb_row) + e] (fp32) before quantizing.
+// Waves share nothing, so the workgroup size (kThreads) only sets how the
+// blocks spread over the CUs. kBias compiles the bias in (the KV-cache
+// write); the weight quantizer keeps its registers free of it.
+template <bool kQ4, int kThreads, bool kBias>
+__global__ __launch_bounds__(kThreads) void quantize_b32_kernel(
+    const float* __restrict__ W, uint8_t* __restrict__ out, int64_t nblocks,
+    const float* __restrict__ bias, int64_t nb_row) {
   constexpr int kBB = kQ4 ? 18 : 34;
   constexpr float kQmax = kQ4 ? 7.0f : 127.0f;
-  constexpr int kWaves = kQThreads / kWave;
+  constexpr int kWaves = kThreads / kWave;
   __shared__ __attribute__((aligned(16))) float xs[kWaves][kWave * 32];
   __shared__ __attribute__((aligned(16))) uint8_t ob[kWaves][kWave * kBB];
 
@@ -96,10 +101,31 @@ __global__ __launch_bounds__(kQThreads) void quantize_b32_kernel(
     const int64_t g0 = chunk * kPerWG + (int64_t)wv * kWave;  // first block of this wave
     const int64_t left = nblocks - g0;
     const int nblk = left <= 0 ? 0 : (left < kWave ? (int)left : kWave);
-    stage_blocks(W + g0 * 32, nblk, xs[wv], lane);
     const bool valid = lane < nblk;
+    // the bias loads go out before the staging wait, so both overlap
+    f32x4 bb[8];
+    const bool biased = kBias && valid;
+    if (biased) {
+      // block index within its row; 32-bit division whenever the counts fit
+      const int64_t g = g0 + lane;
+      const int64_t c = nblocks <= 0xFFFFFFFFLL ? (int64_t)((uint32_t)g % (uint32_t)nb_row)
+                                                : g % nb_row;
+      const f32x4* bp = reinterpret_cast<const f32x4*>(bias + c * 32);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) bb[k] = bp[k];
+    }
+    stage_blocks(W + g0 * 32, nblk, xs[wv], lane);
     float v[32];
     read_block(xs[wv], lane, valid, v);
+    if (biased) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        v[4 * k + 0] -= bb[k].x;
+        v[4 * k + 1] -= bb[k].y;
+        v[4 * k + 2] -= bb[k].z;
+        v[4 * k + 3] -= bb[k].w;
+      }
+    }
 
     // amax over the block (|x| >= +0, so the max order does not matter)
     float a = 0.0f;
@@ -362,6 +388,31 @@ constexpr int64_t kMaxGrid = 1 << 24;
 
 int64_t grid_for(int64_t chunks) { return chunks < kMaxGrid ? chunks : kMaxGrid; }
 
+// nb Q4_0 / Q8_0 blocks, one per lane. Below 1024 waves of work a launch of
+// 256-thread workgroups leaves most CUs idle (a 512-token K or V write of
+// dim 1024 is 256 waves), so small jobs go out one wave per workgroup.
+template <bool kQ4, bool kBias>
+void launch_b32_with(const float* src, uint8_t* out, int64_t nb, const float* bias, int64_t nb_row,
+                hipStream_t stream) {
+  const int64_t waves = (nb + kWave - 1) / kWave;
+  if (waves < 1024)
+    hipLaunchKernelGGL((quantize_b32_kernel<kQ4, kWave, kBias>), dim3((unsigned)waves),
+                       dim3(kWave), 0, stream, src, out, nb, bias, nb_row);
+  else
+    hipLaunchKernelGGL((quantize_b32_kernel<kQ4, kQThreads, kBias>),
+                       dim3((unsigned)grid_for((nb + kQThreads - 1) / kQThreads)),
+                       dim3(kQThreads), 0, stream, src, out, nb, bias, nb_row);
+}
+
+template <bool kQ4>
+void launch_b32(const float* src, uint8_t* out, int64_t nb, const float* bias, int64_t nb_row,
+                hipStream_t stream) {
+  if (bias != nullptr)
+    launch_b32_with<kQ4, true>(src, out, nb, bias, nb_row, stream);
+  else
+    launch_b32_with<kQ4, false>(src, out, nb, nullptr, nb_row, stream);
+}
+
 }  // namespace
 
 hipError_t launch_quantize(int fmt, const float* W, void* blocks, int64_t rows, int64_t K,
@@ -379,15 +430,24 @@ hipError_t launch_quantize(int fmt, const float* W, void* blocks, int64_t rows, 
                          0, stream, W, out, nsuper);
   } else {
     const int64_t nb = rows * (K / 32);
-    const int64_t chunks = (nb + kQThreads - 1) / kQThreads;  // one block per thread
-    if (chunks == 0) return hipSuccess;
+    if (nb == 0) return hipSuccess;
     if (fmt == kFmtQ4_0)
-      hipLaunchKernelGGL(quantize_b32_kernel<true>, dim3((unsigned)grid_for(chunks)),
-                         dim3(kQThreads), 0, stream, W, out, nb);
+      launch_b32<true>(W, out, nb, nullptr, 1, stream);
     else
-      hipLaunchKernelGGL(quantize_b32_kernel<false>, dim3((unsigned)grid_for(chunks)),
-                         dim3(kQThreads), 0, stream, W, out, nb);
+      launch_b32<false>(W, out, nb, nullptr, 1, stream);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_write(int fmt, const float* rows, const float* bias, void* dst, int64_t n,
+                           int64_t dim, hipStream_t stream) {
+  const int64_t nb = n * (dim / 32);
+  if (nb == 0) return hipSuccess;
+  uint8_t* out = static_cast<uint8_t*>(dst);
+  if (fmt == kFmtQ4_0)
+    launch_b32<true>(rows, out, nb, bias, dim / 32, stream);
+  else
+    launch_b32<false>(rows, out, nb, bias, dim / 32, stream);
   return hipGetLastError();
 }
 

@@ -1,11 +1,12 @@
 /*
  * qmat.h — C ABI of the block-quantized weight matmul for MI355X (gfx950).
  *
- * Three operations, all enqueued asynchronously on a caller-supplied HIP
+ * Four operations, all enqueued asynchronously on a caller-supplied HIP
  * stream:
  *   qmat_quantize  fp32 matrix  -> packed weight (or activation) blocks
  *   qmat_gemv      packed W × fp32 x        -> fp32 y        (decode)
  *   qmat_gemm      packed W × Q8_0 X blocks -> fp32 Y        (prefill)
+ *   qmat_kv_write  fp32 K or V rows -> Q4_0 / Q8_0 rows of a KV cache
  *
  * Sources. Citations name the web page and the section or table of it
  * that fixes the fact:
@@ -16,7 +17,10 @@
  *          "量化：内存真正去哪了" (Q4_0: 32 weights, one fp16 scale,
  *          18 bytes, 4.5 bits per weight).
  *   [KVQ]  lpnh.cn KV-cache article; section "kv-mean-center 进阶技巧",
- *          paragraph "问题" (Q4_0 is symmetric: value ≈ scale × q).
+ *          paragraph "问题" (Q4_0 is symmetric: value ≈ scale × q), and
+ *          the same section's bias subtracted from K before Q4_0
+ *          quantization; section "量化 KV Cache 的一键配置方法" (K and V
+ *          caches stored as q8_0 or q4_0).
  *   [BARE] xdnf.cn llama.cpp article; section 3.2 (dequant snippet: low
  *          nibbles are the first 16 elements of a block, high nibbles the
  *          last 16; fp16 parameters precede the nibbles).
@@ -192,6 +196,31 @@ int qmat_gemv(int fmt, const void *blocks, const float *x, float *y,
  */
 int qmat_gemm(int fmt, const void *blocks, const void *X_q8, float *Y,
               int64_t M, int64_t K, int64_t N, void *stream);
+
+/*
+ * qmat_kv_write — quantize new key or value rows into a KV cache.
+ *   [KVQ] "量化 KV Cache 的一键配置方法": K and V rows are stored as q8_0 or
+ *   q4_0 blocks. [KVQ] "kv-mean-center 进阶技巧": a fixed per-channel bias may
+ *   be subtracted from K first; attention is unchanged (a query's scores all
+ *   move by the same q·bias, and softmax ignores a constant per row) while
+ *   the centred values quantize with less error.
+ *   fmt:   QMAT_Q4_0 or QMAT_Q8_0 (others: QMAT_E_FMT).
+ *   rows:  fp32 [n][dim], one new vector per token (dim = KV heads × head
+ *          dimension), a multiple of 32.
+ *   bias:  fp32 [dim] subtracted from every row (fp32, correctly rounded)
+ *          before quantizing, or NULL.
+ *   cache: cells rows of qmat_row_bytes(fmt, dim) bytes in the block layout
+ *          above; rows cell0 .. cell0+n-1 are overwritten, every other byte is
+ *          left as it was. Each written row holds exactly the bytes
+ *          qmat_quantize(fmt, rows[i] - bias, ...) would write.
+ *   Shapes: 0 <= n, cell0 and cell0 + n <= cells (QMAT_E_SHAPE otherwise).
+ *   rows, bias (if given) and cache + cell0 * row_bytes must be 16-byte
+ *   aligned (QMAT_E_ALIGN); any cell0 qualifies when dim is a multiple of 256.
+ *   n == 0 or dim == 0 enqueues nothing.
+ */
+int qmat_kv_write(int fmt, const float *rows, const float *bias, void *cache,
+                  int64_t cell0, int64_t n, int64_t cells, int64_t dim,
+                  void *stream);
 
 #ifdef __cplusplus
 }

@@ -127,3 +127,21 @@ def test_product_path_does_not_use_the_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in text and "from oracle" not in text, f
                 assert "liboracle" not in text and "qmat_oracle" not in text, f
+
+
+def test_kv_write_arguments(lib):
+    f = lib.qmat_kv_write
+    f.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                  ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    assert f(2, A, None, A, 0, 1, 4, 256, None) == E_FMT           # Q4_K is not a cache type
+    assert f(3, A, None, A, 0, 1, 4, 256, None) == E_FMT
+    assert f(0, A, None, A, 0, 1, 4, 48, None) == E_SHAPE          # dim % 32
+    assert f(0, A, None, A, 3, 2, 4, 256, None) == E_SHAPE         # past the last cell
+    assert f(0, A, None, A, -1, 1, 4, 256, None) == E_SHAPE
+    assert f(1, A, None, A, 0, -1, 4, 256, None) == E_SHAPE
+    assert f(0, None, None, A, 0, 0, 4, 256, None) == 0            # nothing to do
+    assert f(0, None, None, A, 0, 1, 4, 256, None) == E_NULL
+    assert f(0, A, None, None, 0, 1, 4, 256, None) == E_NULL
+    assert f(0, A, A + 4, A, 0, 1, 4, 256, None) == E_ALIGN        # bias
+    assert f(0, A, None, A, 1, 1, 4, 64, None) == E_ALIGN          # cell 1 of 36-byte rows

@@ -147,6 +147,33 @@ def test_quantize_bytes_identical_full_sizes(q):
         assert np.array_equal(host(q.quantize(2, dev_tensor(W))), oracle.quantize(2, W))
 
 
+def test_kv_write_bytes(q):
+    """KV-cache writes (with and without the per-channel bias) give the
+    oracle's bytes in the written cells and leave every other byte alone."""
+    import torch
+    rng = np.random.default_rng(900)
+    for fmt in (0, 1):
+        for dim, cells, cell0, n, centred in (
+                (256, 40, 0, 1, False), (256, 40, 7, 5, True), (1024, 64, 31, 33, True),
+                (4096, 12, 1, 11, False), (1024, 16, 16, 0, True), (2048, 9, 0, 9, True),
+                (32, 12, 8, 4, True), (96, 5, 0, 5, False),  # one and three blocks per row
+                (1024, 16384, 16383, 1, True),  # a decode write into the last cell
+                (1024, 16384, 512, 512, True),  # the 512-token prefill write
+                (1024, 4096, 100, 2048, fmt == 0)):  # >= 1024 waves: 256-thread workgroups
+            say(f"kv write fmt={fmt} dim={dim} cells={cells} cell0={cell0} n={n} bias={centred}")
+            rb = oracle.row_bytes(fmt, dim)
+            cache = rng.integers(0, 256, (cells, rb), dtype=np.uint8)
+            mean = rng.normal(0, 3, dim).astype(np.float32)
+            rows = (mean + rng.normal(0, 0.5, (n, dim))).astype(np.float32)
+            rows[:, ::37] = 0.0
+            bias = mean if centred else None
+            dc = dev_tensor(cache)
+            q.kv_write(fmt, dev_tensor(rows), dc, cell0, None if bias is None else dev_tensor(bias))
+            want = oracle.kv_write(fmt, rows, bias, cache, cell0)
+            assert np.array_equal(host(dc), want), (fmt, dim, cell0, n, centred)
+    torch.cuda.synchronize()
+
+
 # ------------------------------------------------------------------ GEMV --
 
 def gemv_case(q, fmt, W, x):
