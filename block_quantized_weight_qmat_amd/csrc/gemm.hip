@@ -19,11 +19,15 @@
 // 12582912 + S. Then t = fma(F, dx, -12582912 * dx) = dx * S with one
 // rounding (12582912 * dx is exact for an fp16 dx), and acc = fma(t, dw, acc).
 //
-// Tiling: a workgroup computes a 128 (m) x 64 (n) tile; each of its eight
-// compute waves owns one 32 x 32 MFMA tile of it (two compute waves per SIMD:
-// a single wave issues dependent-free fp32 FMAs at only half the rate). A stage holds 8
-// K-blocks of W and X in LDS, unpacked to int8 rows of 32 bytes plus fp32
-// scales, so every MFMA operand is one 16-byte LDS read.
+// Tiling: a workgroup computes a 128 (m) x 64 (n) tile: four 32 x 64 wave
+// tiles (two 32 x 32 MFMA tiles each). Each wave tile is shared by two
+// compute waves on the same SIMD, which take the first and the second half
+// of every stage's K-blocks and add their accumulators through LDS at the
+// end of the tile (Q4_K-style: one compute wave per wave tile, see ks_of). The scale step is fp32 VALU work and a single wave issues
+// independent fp32 FMAs at only about half the SIMD's rate, so two waves
+// per SIMD split it; every operand and scale is still read from LDS once.
+// A stage holds 8 K-blocks of W and X in LDS, unpacked to int8 rows of 32
+// bytes plus fp32 scales, so every MFMA operand is one 16-byte LDS read.
 //
 // Pipeline: a workgroup has eight compute waves and four loader waves. Loader
 // waves hold kDepth stages of raw blocks in registers (stage s+1+kDepth is
@@ -58,11 +62,20 @@ constexpr int kKB = 8;  // K-blocks per stage
 #endif
 // each compute wave owns 32 rows x (32 * kNT) columns of the tile
 constexpr int kNT = QMAT_GEMM_NT;  // 32-column MFMA tiles per compute wave
-constexpr int kThreads = kWave * kRT * kCT / kNT;  // compute threads
-#ifndef QMAT_GEMM_LOADERS
-#define QMAT_GEMM_LOADERS 4
-#endif
-constexpr int kLoadThreads = kWave * QMAT_GEMM_LOADERS;  // loader threads
+constexpr int kTileWaves = kRT * kCT / kNT;  // wave tiles per workgroup tile
+// Compute waves per wave tile (each takes kKB / ks_of(FMT) blocks of every
+// stage). Q4_K-style stays at one: its min term leaves a share no registers
+// for overlapping the LDS reads, and one wave per tile with the pipelined
+// stage below is faster.
+constexpr int ks_of(int fmt) { return fmt == kFmtQ4_K ? 1 : 2; }
+constexpr int threads_of(int fmt) { return kWave * kTileWaves * ks_of(fmt); }  // compute threads
+// Loader waves. The loaders' unpacking and LDS writes are the critical path
+// of a stage (they reach the stage barrier last), so the split formats use
+// eight: two per SIMD, each with half the items, at four waves per SIMD and
+// 128 registers. Q4_K-style's single compute wave per tile needs more
+// registers than a third wave per SIMD would leave.
+constexpr int loaders_of(int fmt) { return fmt == kFmtQ4_K ? 4 : 8; }
+constexpr int load_threads_of(int fmt) { return kWave * loaders_of(fmt); }
 constexpr int kDepth = QMAT_GEMM_DEPTH;  // stages a loader thread holds in registers
 constexpr uint32_t kMagicI = 0x4B400000u;  // 1.5 * 2^23 as fp32 bits
 constexpr float kMagicF = 12582912.0f;
@@ -469,51 +482,52 @@ struct TileLoader {
   }
 };
 
-// One K-stage of a wave's NT 32 x 32 tiles (rows 32 wm.., column tiles
-// wn0..) from LDS into the fp32 accumulators; nbs blocks of the stage exist.
+// Blocks [b0, b1) of a K-stage for a wave's NT 32 x 32 tiles (rows 32 wm..,
+// column tiles wn0..), from LDS into the fp32 accumulators.
 // Q6_K-style stage: per block, the MFMA of each 16-element half (lanes of
 // the other half give zero weight operands: the products pair operand bytes
 // of the same lane half, which hold the same elements on both sides), each
 // scaled by its own row scale.
 template <int NT>
-__device__ __forceinline__ void compute_stage_q6(const Stage& cur, int nbs, int wm, int wn0,
-                                                 int l32, int half, const i32x16& cmagic,
-                                                 float (&acc)[NT][16]) {
-  for (int bb = 0; bb < nbs; ++bb) {
+__device__ __forceinline__ void compute_range_q6(const Stage& cur, int b0, int b1, int wm,
+                                                 int wn0, int l32, int half,
+                                                 const i32x16& cmagic, float (&acc)[NT][16]) {
+  for (int bb = b0; bb < b1; ++bb) {
     Ops<NT> op;
     load_ops(cur, bb, wm, wn0, l32, half, op);
     const i32x4 z = {0, 0, 0, 0};
     const i32x4 a0 = half == 0 ? op.a : z, a1 = half == 0 ? z : op.a;
-    i32x16 d0[NT], d1[NT];
+    // one half at a time, so that a single set of MFMA results is live
+    i32x16 d[NT];
+    Scales<NT> sc;
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      d0[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, op.b[t], cmagic, 0, 0, 0);
-      d1[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, op.b[t], cmagic, 0, 0, 0);
-    }
-    Scales<NT> sc0, sc1;
-    load_scales(cur, bb, wm, wn0, l32, half, sc0);
+    for (int t = 0; t < NT; ++t)
+      d[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, op.b[t], cmagic, 0, 0, 0);
+    load_scales(cur, bb, wm, wn0, l32, half, sc);
+    apply_scales(sc, d, acc);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+      d[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, op.b[t], cmagic, 0, 0, 0);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const f32x4 t = *reinterpret_cast<const f32x4*>(&cur.wo[bb][wm * 32 + 8 * q + 4 * half]);
-      sc1.dw[4 * q + 0] = t.x;
-      sc1.dw[4 * q + 1] = t.y;
-      sc1.dw[4 * q + 2] = t.z;
-      sc1.dw[4 * q + 3] = t.w;
+      sc.dw[4 * q + 0] = t.x;
+      sc.dw[4 * q + 1] = t.y;
+      sc.dw[4 * q + 2] = t.z;
+      sc.dw[4 * q + 3] = t.w;
     }
-#pragma unroll
-    for (int t = 0; t < NT; ++t) sc1.dx[t] = sc0.dx[t];
-    apply_scales(sc0, d0, acc);
-    apply_scales(sc1, d1, acc);
+    apply_scales(sc, d, acc);
   }
 }
 
-template <int FMT, int NT>
-__device__ __forceinline__ void compute_stage(const Stage& cur, int nbs, int wm, int wn0,
-                                              int l32, int half, const i32x16& cmagic,
+template <int FMT, int NT, int PER>
+__device__ __forceinline__ void compute_range(const Stage& cur, int b0, int b1, int wm,
+                                              int wn0, int l32, int half, const i32x16& cmagic,
                                               float (&acc)[NT][16]) {
   if (FMT == kFmtQ6_K) {
-    compute_stage_q6<NT>(cur, nbs, wm, wn0, l32, half, cmagic, acc);
-  } else if (nbs == kKB) {
+    compute_range_q6<NT>(cur, b0, b1, wm, wn0, l32, half, cmagic, acc);
+  } else if (PER == kKB && b1 - b0 == kKB) {
     // Full stage, software-pipelined: the column scales of all 8 blocks are
     // read up front; in step bb the MFMAs of block bb+1 are issued
     // (operands read one step earlier), the operands of block bb+2 and the
@@ -553,16 +567,33 @@ __device__ __forceinline__ void compute_stage(const Stage& cur, int nbs, int wm,
       apply_block(dw[bb & 1], dxs[bb], c1s[bb], d[bb & 1], acc);
       if (FMT == kFmtQ4_K && (bb & 1)) min_term(cur, bb - 1, kKB, wm, wn0, l32, half, acc);
     }
+  } else if (b1 - b0 == PER) {
+    // A full share, unrolled. The other compute wave of the SIMD covers
+    // this wave's waits for the LDS and the matrix core (reading block j+1's
+    // operands ahead of block j's scaling measured slower).
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      Ops<NT> op;
+      Scales<NT> sc;
+      load_ops(cur, b0 + j, wm, wn0, l32, half, op);
+      i32x16 d[NT];
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        d[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(op.a, op.b[t], cmagic, 0, 0, 0);
+      load_scales(cur, b0 + j, wm, wn0, l32, half, sc);
+      apply_scales(sc, d, acc);
+      if (FMT == kFmtQ4_K && (j & 1)) min_term(cur, b0 + j - 1, b1, wm, wn0, l32, half, acc);
+    }
   } else {
-    for (int bb = 0; bb < nbs; ++bb) {
+    for (int bb = b0; bb < b1; ++bb) {
       i32x16 d[NT];
       Scales<NT> sc;
 #pragma unroll
       for (int t = 0; t < NT; ++t) mfma_block(cur, bb, wm, wn0 + t, l32, half, cmagic, d[t]);
       load_scales(cur, bb, wm, wn0, l32, half, sc);
       apply_scales(sc, d, acc);
-      if (FMT == kFmtQ4_K && ((bb & 1) || bb + 1 == nbs))
-        min_term(cur, bb & ~1, nbs, wm, wn0, l32, half, acc);
+      if (FMT == kFmtQ4_K && (((bb - b0) & 1) || bb + 1 == b1))
+        min_term(cur, bb - ((bb - b0) & 1), b1, wm, wn0, l32, half, acc);
     }
   }
 }
@@ -610,14 +641,19 @@ __device__ __forceinline__ i32x16 magic_vec() {
   return c;
 }
 
-// Warp-specialized kernel: kLoadThreads loader threads fill the LDS stages,
-// kThreads compute threads own 32 x (32 kNT) tiles each.
+// Warp-specialized kernel: load_threads_of(FMT) loader threads fill the LDS stages,
+// threads_of(FMT) compute threads share 32 x (32 kNT) wave tiles ks_of(FMT)
+// to a tile.
 template <int FMT>
-__global__ __launch_bounds__(kThreads + kLoadThreads) void gemm_kernel(
+__global__ __launch_bounds__(threads_of(FMT) + load_threads_of(FMT)) void gemm_kernel(
     const uint8_t* __restrict__ Wb, const uint8_t* __restrict__ Xb, float* __restrict__ Y,
     int64_t M, int K, int64_t N, int64_t tiles_n, int64_t ntiles) {
   __shared__ __attribute__((aligned(16))) Stage st[2];
-  typedef TileLoader<FMT, kLoadThreads> TL;
+  typedef TileLoader<FMT, load_threads_of(FMT)> TL;
+  constexpr int kKS = ks_of(FMT), kPer = kKB / kKS, kThreads = threads_of(FMT);
+  static_assert((kKS - 1) * kTileWaves * kNT * 16 * kWave * 4 <= 2 * (int)sizeof(Stage),
+                "reduction buffer exceeds the LDS stages");
+  static_assert(kKB % kKS == 0 && (kPer % 2 == 0 || kKS == 1), "K split must keep block pairs");
   // role per wave, in a scalar register so that the branch is uniform
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const bool loader = wave >= kThreads / kWave;
@@ -672,12 +708,17 @@ __global__ __launch_bounds__(kThreads + kLoadThreads) void gemm_kernel(
 #pragma unroll
       for (int k = 0; k + 1 < kDepth; ++k)
         if (s + k < nstage) step(s + k, regs[(k + 1) % kDepth]);
+      if (kKS > 1) __syncthreads();  // the compute waves' reduction
       // the next tile reuses both LDS stages
       __syncthreads();
     }
   } else {
     const i32x16 cmagic = magic_vec();
-    const int wm = wv % kRT, wn0 = (wv / kRT) * kNT;  // rows 32wm.., column tiles wn0..
+    // waves tw and tw + kTileWaves share a SIMD and wave tile tw: rows
+    // 32 wm.., column tiles wn0..; share ks takes blocks [ks kPer, (ks+1) kPer)
+    // of every stage
+    const int ks = wv / kTileWaves, tw = wv % kTileWaves;
+    const int wm = tw % kRT, wn0 = (tw / kRT) * kNT;
     for (int64_t tile = lin; tile < ntiles; tile += gridDim.x) {
       const int64_t tm = tile / tiles_n, tn = tile - tm * tiles_n;
       const int64_t m0 = tm * kBM, n0 = tn * kBN;
@@ -688,11 +729,42 @@ __global__ __launch_bounds__(kThreads + kLoadThreads) void gemm_kernel(
         for (int i = 0; i < 16; ++i) acc[t][i] = 0.0f;
       __syncthreads();  // stage 0 is in LDS
       for (int s = 0; s < nstage; ++s) {
-        compute_stage<FMT, kNT>(st[s & 1], min(kKB, nb - s * kKB), wm, wn0, l32, half, cmagic,
-                                acc);
+        const int nbs = min(kKB, nb - s * kKB);
+        compute_range<FMT, kNT, kPer>(st[s & 1], min(nbs, ks * kPer), min(nbs, (ks + 1) * kPer), wm,
+                                wn0, l32, half, cmagic, acc);
         __syncthreads();
       }
-      store_tile<kNT>(Y, M, N, m0, n0, wm, wn0, l32, half, acc);
+      if (kKS > 1) {
+        // both LDS stages are free until the end-of-tile barrier: the other
+        // shares park their sums there, and share 0 adds them in share order
+        float* red = reinterpret_cast<float*>(&st[0]);
+        // an opaque copy of the base, so that the 32 addresses below are
+        // formed here and not hoisted out of the tile loop into registers
+        int rbase = ((ks > 0 ? ks - 1 : 0) * kTileWaves + tw) * kNT * 16 * kWave + lane;
+        asm volatile("" : "+v"(rbase));
+        constexpr int kVals = kNT * 16;
+        if (ks > 0) {
+          float* p = red + rbase;
+#pragma unroll
+          for (int t = 0; t < kNT; ++t)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) p[(t * 16 + i) * kWave] = acc[t][i];
+        }
+        __syncthreads();
+        if (ks == 0) {
+#pragma unroll
+          for (int k = 1; k < kKS; ++k) {
+            const float* p = red + rbase + (k - 1) * kTileWaves * kVals * kWave;
+#pragma unroll
+            for (int t = 0; t < kNT; ++t)
+#pragma unroll
+              for (int i = 0; i < 16; ++i) acc[t][i] += p[(t * 16 + i) * kWave];
+          }
+          store_tile<kNT>(Y, M, N, m0, n0, wm, wn0, l32, half, acc);
+        }
+      } else {
+        store_tile<kNT>(Y, M, N, m0, n0, wm, wn0, l32, half, acc);
+      }
       __syncthreads();
     }
   }
@@ -718,7 +790,7 @@ hipError_t launch_gemm(int fmt, const void* blocks, const void* Xq8, float* Y, i
   const uint8_t* W = static_cast<const uint8_t*>(blocks);
   const uint8_t* X = static_cast<const uint8_t*>(Xq8);
 #define QMAT_GEMM_LAUNCH(F)                                                                \
-  hipLaunchKernelGGL(gemm_kernel<F>, dim3(grid), dim3(kThreads + kLoadThreads), 0, stream, W, \
+  hipLaunchKernelGGL(gemm_kernel<F>, dim3(grid), dim3(threads_of(F) + load_threads_of(F)), 0, stream, W, \
                      X, Y, M, (int)K, N, tiles_n, ntiles)
   switch (fmt) {
     case kFmtQ4_0:
