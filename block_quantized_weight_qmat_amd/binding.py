@@ -57,6 +57,8 @@ def load_library():
     lib.qmat_gemv.restype = i32
     lib.qmat_gemm.argtypes = [i32, p, p, p, i64, i64, i64, p]
     lib.qmat_gemm.restype = i32
+    lib.qmat_prefill.argtypes = [i32, p, p, p, p, i64, i64, i64, p]
+    lib.qmat_prefill.restype = i32
     lib.qmat_kv_write.argtypes = [i32, p, p, p, i64, i64, i64, i64, p]
     lib.qmat_kv_write.restype = i32
     _lib = lib
@@ -156,6 +158,34 @@ def gemm(fmt, blocks: torch.Tensor, Xq: torch.Tensor, M: int, K: int, N: int,
     _check("qmat_gemm", load_library().qmat_gemm(
         f, blocks.data_ptr(), Xq.data_ptr(), out.data_ptr(), M, K, N, _stream(Xq)))
     return out
+
+
+def prefill(fmt, blocks: torch.Tensor, X: torch.Tensor, M: int,
+            out: torch.Tensor | None = None,
+            xq: torch.Tensor | None = None) -> tuple[torch.Tensor, torch.Tensor]:
+    """Y[N, M] = dequant(Q8_0(X)) @ dequant(W)^T from fp32 X [N, K] in one
+    call; returns (Y, xq), xq being the Q8_0 activation blocks it wrote."""
+    f = _fmt(fmt)
+    _gpu(blocks, "blocks", torch.uint8)
+    _gpu(X, "X", torch.float32)
+    if X.dim() != 2:
+        raise ValueError("X must be 2-D [N, K]")
+    N, K = X.shape
+    if blocks.numel() != M * row_bytes(f, K):
+        raise ValueError("blocks do not match M, K")
+    if xq is None:
+        xq = torch.empty((N, row_bytes(Q8_0, K)), dtype=torch.uint8, device=X.device)
+    _gpu(xq, "xq", torch.uint8)
+    if xq.numel() != N * row_bytes(Q8_0, K):
+        raise ValueError("xq has the wrong size")
+    if out is None:
+        out = torch.empty((N, M), dtype=torch.float32, device=X.device)
+    _gpu(out, "out", torch.float32)
+    if out.numel() != N * M:
+        raise ValueError("out must hold N*M values")
+    _check("qmat_prefill", load_library().qmat_prefill(
+        f, blocks.data_ptr(), X.data_ptr(), xq.data_ptr(), out.data_ptr(), M, K, N, _stream(X)))
+    return out, xq
 
 
 def kv_write(fmt, rows: torch.Tensor, cache: torch.Tensor, cell0: int,

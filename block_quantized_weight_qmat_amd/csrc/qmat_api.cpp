@@ -126,6 +126,24 @@ int qmat_gemm(int fmt, const void* blocks, const void* X_q8, float* Y, int64_t M
       qmat::launch_gemm(fmt, blocks, X_q8, Y, M, K, N, static_cast<hipStream_t>(stream)));
 }
 
+int qmat_prefill(int fmt, const void* blocks, const float* X, void* xq, float* Y, int64_t M,
+                 int64_t K, int64_t N, void* stream) {
+  if (!fmt_ok(fmt)) return QMAT_E_FMT;
+  int rc = check_shape(fmt, M, K);
+  if (rc != QMAT_OK) return rc;
+  if ((rc = check_shape(QMAT_Q8_0, N, K)) != QMAT_OK) return rc;
+  if (K > kMaxGemmK) return QMAT_E_SHAPE;
+  if (M == 0 || N == 0) return QMAT_OK;  // nothing to read or write
+  if ((rc = check_buf(blocks, K > 0)) != QMAT_OK) return rc;
+  if ((rc = check_buf(X, K > 0)) != QMAT_OK) return rc;
+  if ((rc = check_buf(xq, K > 0)) != QMAT_OK) return rc;
+  if ((rc = check_buf(Y, true)) != QMAT_OK) return rc;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (K > 0 && (rc = hip_status(qmat::launch_quantize(QMAT_Q8_0, X, xq, N, K, st))) != QMAT_OK)
+    return rc;
+  return hip_status(qmat::launch_gemm(fmt, blocks, xq, Y, M, K, N, st));
+}
+
 int qmat_kv_write(int fmt, const float* rows, const float* bias, void* cache, int64_t cell0,
                   int64_t n, int64_t cells, int64_t dim, void* stream) {
   if (fmt != QMAT_Q4_0 && fmt != QMAT_Q8_0) return QMAT_E_FMT;

@@ -1,11 +1,12 @@
 /*
  * qmat.h — C ABI of the block-quantized weight matmul for MI355X (gfx950).
  *
- * Four operations, all enqueued asynchronously on a caller-supplied HIP
+ * Five operations, all enqueued asynchronously on a caller-supplied HIP
  * stream:
  *   qmat_quantize  fp32 matrix  -> packed weight (or activation) blocks
  *   qmat_gemv      packed W × fp32 x        -> fp32 y        (decode)
  *   qmat_gemm      packed W × Q8_0 X blocks -> fp32 Y        (prefill)
+ *   qmat_prefill   packed W × fp32 X        -> fp32 Y        (prefill, one call)
  *   qmat_kv_write  fp32 K or V rows -> Q4_0 / Q8_0 rows of a KV cache
  *
  * Sources. Citations name the web page and the section or table of it
@@ -184,9 +185,9 @@ int qmat_gemv(int fmt, const void *blocks, const float *x, float *y,
  *   Y: fp32 [N][M] (token-major), overwritten.
  *   K is at most 2^24 here (QMAT_E_SHAPE above that): the kernel addresses
  *   a 128-row tile with 32-bit byte offsets.
- *   Up to 48 tokens (a decode batch), and for Q6_K weights at any N, the
- *   weights are instead streamed once per 16 tokens and each weight block
- *   is applied to every token's block with int8 dot products; the
+ *   Up to 48 tokens (a decode batch) the weights are instead streamed once
+ *   per 16 tokens and each weight block is applied to every token's block
+ *   with int8 dot products; the
  *   arithmetic (exact block sums, the fp16 block scales applied in fp32;
  *   Q6_K: per 16-weight half) and the accuracy bound are the same.
  *   Accuracy: relative L2 error against the exact (fp64) product of the
@@ -196,6 +197,28 @@ int qmat_gemv(int fmt, const void *blocks, const float *x, float *y,
  */
 int qmat_gemm(int fmt, const void *blocks, const void *X_q8, float *Y,
               int64_t M, int64_t K, int64_t N, void *stream);
+
+/*
+ * qmat_prefill — the prefill product from fp32 activations in one call:
+ *   the activations are quantized to Q8_0 into the caller's workspace, then
+ *   multiplied as by qmat_gemm. [LC05 "算力决定 Prefill"] as for qmat_gemm;
+ *   the activation rule is qmat_quantize's Q8_0 rule.
+ *   blocks: W in fmt (Q4_0, Q8_0, Q4_K or Q6_K), M rows of K.
+ *   X: fp32 [N][K] activations.
+ *   xq: workspace of N * qmat_row_bytes(QMAT_Q8_0, K) bytes, owned by the
+ *       caller; afterwards it holds exactly what
+ *       qmat_quantize(QMAT_Q8_0, X, xq, N, K, stream) writes, so the same
+ *       activations can be multiplied by further weight matrices with
+ *       qmat_gemm.
+ *   Y: fp32 [N][M] (token-major), overwritten.
+ *   The two kernels are enqueued on stream in that order; Y is exactly
+ *   qmat_gemm(fmt, blocks, xq, Y, M, K, N, stream)'s result. Shapes, the K
+ *   limit and errors are qmat_gemm's; X and xq follow the same rules as
+ *   the other buffers (non-NULL and 16-byte aligned when K > 0). X, xq and Y
+ *   must not overlap. M == 0 or N == 0 enqueues nothing.
+ */
+int qmat_prefill(int fmt, const void *blocks, const float *X, void *xq, float *Y,
+                 int64_t M, int64_t K, int64_t N, void *stream);
 
 /*
  * qmat_kv_write — quantize new key or value rows into a KV cache.

@@ -145,3 +145,19 @@ def test_kv_write_arguments(lib):
     assert f(0, A, None, None, 0, 1, 4, 256, None) == E_NULL
     assert f(0, A, A + 4, A, 0, 1, 4, 256, None) == E_ALIGN        # bias
     assert f(0, A, None, A, 1, 1, 4, 64, None) == E_ALIGN          # cell 1 of 36-byte rows
+
+
+def test_prefill_arguments(lib):
+    f = lib.qmat_prefill
+    assert f(7, A, A, A, A, 1, 32, 1, None) == E_FMT
+    assert f(0, A, A, A, A, 1, 48, 1, None) == E_SHAPE             # K % 32
+    assert f(2, A, A, A, A, 1, 32, 1, None) == E_SHAPE             # Q4_K needs K % 256
+    assert f(0, A, A, A, A, 1, 32, -1, None) == E_SHAPE
+    assert f(0, A, A, A, A, 1, 2 ** 24 + 32, 1, None) == E_SHAPE   # GEMM K limit
+    assert f(0, A, None, A, A, 1, 32, 1, None) == E_NULL           # X
+    assert f(0, A, A, None, A, 1, 32, 1, None) == E_NULL           # workspace
+    assert f(0, A, A, A, None, 1, 32, 1, None) == E_NULL           # Y
+    assert f(0, A, A + 4, A, A, 1, 32, 1, None) == E_ALIGN
+    assert f(0, A, A, A + 2, A, 1, 32, 1, None) == E_ALIGN
+    assert f(0, None, None, None, None, 0, 64, 3, None) == OK      # nothing to do
+    assert f(0, None, None, None, None, 3, 64, 0, None) == OK

@@ -427,6 +427,27 @@ def test_gemm_k_zero(q):
     assert np.array_equal(host(Y), np.zeros((7, 33), np.float32))
 
 
+@pytest.mark.parametrize("fmt", [0, 1, 2, 3])
+def test_prefill_one_call(q, fmt):
+    """qmat_prefill: its workspace holds the oracle's Q8_0 activation bytes,
+    and its product is qmat_gemm's on them (same bits) and within the GEMM
+    bound of the oracle; a decode batch, an MFMA-sized batch and a ragged one."""
+    import torch
+    rng = np.random.default_rng(800 + fmt)
+    for M, K, N in ((97, 256 * 9, 4), (130, 2048, 70), (64, 256 * 3, 1)):
+        say(f"prefill one call fmt={fmt} M={M} K={K} N={N}")
+        W = mixed_matrix(rng, M, K)
+        X = rng.normal(0, 1, (N, K)).astype(np.float32)
+        dB = dev_tensor(oracle.quantize(fmt, W))
+        Y, xq = q.prefill(fmt, dB, dev_tensor(X), M)
+        Xq = oracle.quantize(1, X)
+        assert np.array_equal(host(xq), Xq)
+        assert np.array_equal(host(Y), host(q.gemm(fmt, dB, xq, M, K, N)))
+        ref = oracle.gemm(fmt, oracle.quantize(fmt, W), Xq, M, K, N)
+        assert rel_l2(host(Y), ref) <= GEMM_TOL
+    torch.cuda.synchronize()
+
+
 def test_prefill_full_size_sampled(q):
     """The prefill workload at full size, quantized on the GPU (bytes checked
     against the oracle), GEMM checked on sampled rows and tokens."""
