@@ -363,6 +363,10 @@ def test_gemm_small_and_ragged(q, fmt):
               (200, 256 * 9, 130)]
     if fmt < 2:
         shapes += [(1, 32, 1), (33, 32 * 37, 5), (65, 32 * 5, 66)]
+        # last stages of 3, 4 and 7 blocks: the two compute waves of a tile
+        # split a stage's 8 blocks 4 + 4, so these leave the second share
+        # short or empty and the first one full or short
+        shapes += [(130, 32 * 11, 64), (129, 32 * 12, 65), (128, 32 * 23, 70)]
     for M, K, N in shapes:
         say(f"gemm fmt={fmt} M={M} K={K} N={N}")
         W = mixed_matrix(rng, M, K) if M > 2 else rng.normal(0, 0.02, (M, K)).astype(np.float32)
