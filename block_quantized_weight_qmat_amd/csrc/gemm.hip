@@ -23,18 +23,19 @@
 // tiles (two 32 x 32 MFMA tiles each). Each wave tile is shared by two
 // compute waves on the same SIMD, which take the first and the second half
 // of every stage's K-blocks and add their accumulators through LDS at the
-// end of the tile (Q4_K-style: one compute wave per wave tile, see ks_of). The scale step is fp32 VALU work and a single wave issues
-// independent fp32 FMAs at only about half the SIMD's rate, so two waves
-// per SIMD split it; every operand and scale is still read from LDS once.
-// A stage holds 8 K-blocks of W and X in LDS, unpacked to int8 rows of 32
-// bytes plus fp32 scales, so every MFMA operand is one 16-byte LDS read.
+// end of the tile (Q4_K-style: one compute wave per wave tile, see ks_of).
+// The scale step is fp32 VALU work and a single wave issues independent
+// fp32 FMAs at only about half the SIMD's rate, so two waves per SIMD split
+// it; every operand and scale is still read from LDS once. A stage holds 8
+// K-blocks of W and X in LDS, unpacked to int8 rows of 32 bytes plus fp32
+// scales, so every MFMA operand is one 16-byte LDS read.
 //
-// Pipeline: a workgroup has eight compute waves and four loader waves. Loader
-// waves hold kDepth stages of raw blocks in registers (stage s+1+kDepth is
-// requested while stage s is computed), unpack stage s+1 into the free half of a
-// two-stage LDS buffer, and meet the compute waves at one barrier per stage.
-// Keeping several stages in flight per CU is what the memory latency needs;
-// compute waves keep only accumulators and operands.
+// Pipeline: a workgroup has eight compute waves and eight loader waves
+// (Q4_K-style: four and four). Loader waves hold kDepth stages of raw blocks
+// in registers (stage s+1+kDepth is requested while stage s is computed),
+// unpack stage s+1 into the free half of a two-stage LDS buffer, and meet the
+// compute waves at one barrier per stage. Compute waves keep only
+// accumulators and operands.
 //
 // Tile order: consecutive workgroup ids land on different XCDs (round
 // robin), so ids are remapped to give each XCD a contiguous band of m-tiles
@@ -64,9 +65,8 @@ constexpr int kKB = 8;  // K-blocks per stage
 constexpr int kNT = QMAT_GEMM_NT;  // 32-column MFMA tiles per compute wave
 constexpr int kTileWaves = kRT * kCT / kNT;  // wave tiles per workgroup tile
 // Compute waves per wave tile (each takes kKB / ks_of(FMT) blocks of every
-// stage). Q4_K-style stays at one: its min term leaves a share no registers
-// for overlapping the LDS reads, and one wave per tile with the pipelined
-// stage below is faster.
+// stage). Q4_K-style stays at one, with the pipelined stage below: its min
+// term needs registers that a split leaves it without (measured: it spills).
 constexpr int ks_of(int fmt) { return fmt == kFmtQ4_K ? 1 : 2; }
 constexpr int threads_of(int fmt) { return kWave * kTileWaves * ks_of(fmt); }  // compute threads
 // Loader waves. The loaders' unpacking and LDS writes are the critical path
