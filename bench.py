@@ -87,7 +87,69 @@ def parse():
     p.add_argument("--batch", type=int, default=0,
                    help="launches per kernel-timing batch (default max(steps, 50))")
     p.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    p.add_argument("--no-peaks", action="store_true",
+                   help="skip the measured-peak kernels (libqmat_micro.so)")
     return p.parse_args()
+
+
+def measured_peaks(torch) -> dict:
+    """This GPU's own peaks, for the rooflines beside the nominal ones: HBM
+    read bandwidth over a 2 GiB buffer (beyond the 256 MB Infinity Cache),
+    the dense int8 MFMA rate, the plain (non-packed) fp32 FMA rate, and the
+    FMA rate of waves that share their SIMDs with int8 MFMA waves. Each is
+    the best of five event-timed launches."""
+    import ctypes
+    from block_quantized_weight_qmat_amd import binding
+    path = os.path.join(os.path.dirname(binding.library_path()), "libqmat_micro.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
+                           "`python -m block_quantized_weight_qmat_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, i32, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+    lib.qmat_micro_read.argtypes = [P, i64, P, i32, P]
+    for f in (lib.qmat_micro_mfma_i8, lib.qmat_micro_fma_f32, lib.qmat_micro_mix):
+        f.argtypes = [i32, P, i32, P]
+    dev = torch.device("cuda")
+    stream = torch.cuda.current_stream()
+    sp = P(stream.cuda_stream)
+
+    def best_ms(launch):
+        ts = []
+        for _ in range(6):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            rc = launch()
+            b.record(stream)
+            torch.cuda.synchronize()
+            if rc != 0:
+                raise RuntimeError(f"measured-peak kernel failed to launch ({rc})")
+            ts.append(a.elapsed_time(b))
+        return min(ts[1:])  # the first launch warms up
+
+    read_bytes, read_grids = 2 << 30, (1024, 2048, 4096, 8192)
+    buf = torch.empty(read_bytes, dtype=torch.uint8, device=dev)
+    out = torch.empty(max(read_grids) * 512, dtype=torch.int32, device=dev)
+    ms = min(best_ms(lambda g=g: lib.qmat_micro_read(P(buf.data_ptr()), read_bytes,
+                                                     P(out.data_ptr()), g, sp))
+             for g in read_grids)
+    hbm = read_bytes / ms / 1e6
+    del buf
+    grid, iters = 2048, 2000
+    ms = best_ms(lambda: lib.qmat_micro_mfma_i8(iters, P(out.data_ptr()), grid, sp))
+    mfma = grid * 4 * iters * 4 * 2 * 32 * 32 * 32 / ms / 1e9
+    iters = 20000
+    ms = best_ms(lambda: lib.qmat_micro_fma_f32(iters, P(out.data_ptr()), grid, sp))
+    fma = grid * 256 * iters * 8 * 2 / ms / 1e9
+    mix_grid = 1024
+    ms = best_ms(lambda: lib.qmat_micro_mix(iters, P(out.data_ptr()), mix_grid, sp))
+    fma_mix = mix_grid * 256 * iters * 8 * 2 / ms / 1e9
+    return {"hbm_read_GBs": round(hbm, 1), "int8_mfma_TOPS": round(mfma, 1),
+            "fp32_fma_TFLOPs": round(fma, 2), "fp32_fma_TFLOPs_beside_mfma": round(fma_mix, 2),
+            "kernels": "libqmat_micro.so: 2 GiB coalesced read (best of 1024-8192 "
+                       "workgroups); 4 chains of "
+                       "v_mfma_i32_32x32x32_i8 per wave; 8 chains of v_fma_f32 per lane; "
+                       "half MFMA, half FMA waves per SIMD"}
 
 
 def rel_l2(a, ref):
@@ -359,6 +421,7 @@ def main():
                "sample": f"{reps} full Q4_0 GEMVs 4096x11008 (dequantize to fp64, fp64 dot, "
                          f"OpenMP over rows) in {t_cpu:.1f} s; same algorithmic bytes as value"}
 
+    peaks = None if args.no_peaks else measured_peaks(torch)
     headline = kernels.get("gemv_q4_0")
     gemm = kernels.get("gemm_q4_0")
     traffic = traffic_for_current_kernel() if headline else None
@@ -383,9 +446,14 @@ def main():
             "unit": "GB/s", "frac": round(headline["frac"], 4),
             "traffic": None if traffic is None else round(traffic),
             "kernel": "gemv_q4_0", "bytes_per_launch": gemv_bytes["q4_0"],
-            "us_per_launch": round(headline["us"], 3)},
+            "us_per_launch": round(headline["us"], 3),
+            "frac_of_measured": None if not peaks else round(
+                headline["GB/s"] / peaks["hbm_read_GBs"], 4)},
         "gemm_int8_tops": None if not gemm else round(gemm["TOPS"], 1),
         "gemm_frac_of_int8_peak": None if not gemm else round(gemm["frac"], 4),
+        "gemm_frac_of_measured_int8": None if not (gemm and peaks) else round(
+            gemm["TOPS"] / peaks["int8_mfma_TOPS"], 4),
+        "measured_peaks": peaks,
         "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                     for k, v in kernels.items()},
         "parity": parity,

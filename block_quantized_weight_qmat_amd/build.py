@@ -1,4 +1,5 @@
-"""Build libqmat.so (gfx950) from csrc/ with hipcc, in-tree.
+"""Build libqmat.so (gfx950) from csrc/ with hipcc, in-tree, and beside it
+libqmat_micro.so, the measured-peak kernels that only the benchmark loads.
 
     python -m block_quantized_weight_qmat_amd.build
 
@@ -19,10 +20,12 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libqmat.so")
+MICRO_LIB = os.path.join(PKG, "libqmat_micro.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["quantize.hip", "gemv.hip", "gemm.hip", "qmat_api.cpp"]
+MICRO_SOURCES = ["micro.hip"]
 
 CFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
@@ -45,16 +48,22 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build() -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs: list, lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build() -> str:
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs = SOURCES + MICRO_SOURCES
+    with ThreadPoolExecutor(max_workers=len(srcs)) as ex:
+        objs = list(ex.map(_compile, srcs))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], MICRO_LIB)
     return LIB
 
 

@@ -161,3 +161,22 @@ def test_prefill_arguments(lib):
     assert f(0, A, A, A + 2, A, 1, 32, 1, None) == E_ALIGN
     assert f(0, None, None, None, None, 0, 64, 3, None) == OK      # nothing to do
     assert f(0, None, None, None, None, 3, 64, 0, None) == OK
+
+
+def test_measured_peak_library():
+    """libqmat_micro.so (the benchmark's measured-peak kernels) exports its
+    four entry points, and each refuses bad arguments before any HIP call."""
+    path = os.path.join(os.path.dirname(binding.library_path()), "libqmat_micro.so")
+    if not os.path.exists(path):
+        pytest.skip("libqmat_micro.so not built")
+    m = ctypes.CDLL(path)
+    P, i32, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+    m.qmat_micro_read.argtypes = [P, i64, P, i32, P]
+    for f in (m.qmat_micro_mfma_i8, m.qmat_micro_fma_f32, m.qmat_micro_mix):
+        f.argtypes = [i32, P, i32, P]
+    assert m.qmat_micro_read(None, 64, A, 1, None) == 1
+    assert m.qmat_micro_read(A, 40, A, 1, None) == 1       # not a multiple of 16 bytes
+    assert m.qmat_micro_read(A, 64, A, 0, None) == 1
+    assert m.qmat_micro_mfma_i8(0, A, 1, None) == 1
+    assert m.qmat_micro_fma_f32(1, None, 1, None) == 1
+    assert m.qmat_micro_mix(8, A, 1, None) == 1            # fewer than 16 iterations
