@@ -1,0 +1,123 @@
+"""A second, independent implementation of the Q4_0, Q8_0 and Q6_K-style
+quantizers in vectorised numpy, written from the rules in include/qmat.h,
+that must agree byte for byte with the oracle. It shares the oracle's
+reading of the pages (so it is a cross-check of the C code's indexing,
+rounding and packing, not a pin of the reading); the pins are in
+test_oracle_pins.py.
+
+Sources of the rules: "05. llama.cpp：从 GGUF 文件到本地推理服务", table in
+section "量化类型：Q4_K_M 到底是什么"; "llama.cpp 原理：如何在普通硬件跑本地大模型",
+section "量化：内存真正去哪了" (18-byte Q4_0 blocks); lpnh.cn KV-cache article,
+section "kv-mean-center 进阶技巧", paragraph "问题" (Q4_0 symmetric).
+"""
+import numpy as np
+import pytest
+
+import oracle
+
+
+def f16_bits(v32):
+    """fp32 -> fp16 bits, round to nearest even, subnormals kept."""
+    return np.asarray(v32, np.float32).astype(np.float16).view(np.uint16)
+
+
+def f16_value(bits):
+    return bits.view(np.float16).astype(np.float32)
+
+
+def round_away(q32):
+    """Round half away from zero of fp32 values, exactly (in float64)."""
+    q = np.asarray(q32, np.float64)
+    return np.sign(q) * np.floor(np.abs(q) + 0.5)
+
+
+def np_quant_b32(W, qmax):
+    """Q4_0 (qmax 7) or Q8_0 (qmax 127): per 32 elements d = amax / qmax
+    stored as fp16, codes round(x / D) clamped, D the stored scale."""
+    rows, K = W.shape
+    x = W.reshape(rows, K // 32, 32).astype(np.float32)
+    amax = np.max(np.abs(x), axis=2)
+    d = (amax / np.float32(qmax)).astype(np.float32)
+    h = f16_bits(d)
+    D = f16_value(h)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = round_away((x / D[..., None]).astype(np.float32))
+    q = np.where(D[..., None] == 0, 0, np.clip(q, -qmax - (1 if qmax == 7 else 0), qmax))
+    q = q.astype(np.int64)
+    out = np.zeros((rows, K // 32, 2 + (16 if qmax == 7 else 32)), np.uint8)
+    out[..., 0] = h & 0xFF
+    out[..., 1] = h >> 8
+    if qmax == 7:
+        c = (q + 8).astype(np.uint8)
+        out[..., 2:] = c[..., :16] | (c[..., 16:] << 4)
+    else:
+        out[..., 2:] = (q & 0xFF).astype(np.uint8)
+    return out.reshape(rows, -1)
+
+
+def np_quant_q6k(W):
+    """Q6_K-style: per 16 elements s = amax / 31; per 256 d = max s / 127
+    (fp16); sc = clamp(round(s / D), 0, 127); codes c = clamp(round(x /
+    (D sc)), -32, 31) + 32; bytes: d, then per 32-element group g the int8
+    scales sc_2g, sc_2g+1, 16 bytes of low nibbles (byte t: code t, code
+    16 + t in the high nibble) and the words H0, H1 whose byte b holds the
+    high 2 bits of codes 4w + b (H0) and 16 + 4w + b (H1) at bits 2w, 2w+1."""
+    rows, K = W.shape
+    x = W.reshape(rows, K // 256, 16, 16).astype(np.float32)
+    amax = np.max(np.abs(x), axis=3)
+    s = (amax / np.float32(31)).astype(np.float32)
+    d = (np.max(s, axis=2) / np.float32(127)).astype(np.float32)
+    h = f16_bits(d)
+    D = f16_value(h)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        sc = round_away((s / D[..., None]).astype(np.float32))
+    sc = np.where(D[..., None] == 0, 0, np.clip(sc, 0, 127)).astype(np.int64)
+    div = (D[..., None] * sc.astype(np.float32)).astype(np.float32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = round_away((x / div[..., None]).astype(np.float32))
+    q = np.where(div[..., None] == 0, 0, np.clip(q, -32, 31)).astype(np.int64)
+    c = (q + 32).reshape(rows, K // 256, 8, 32)
+    out = np.zeros((rows, K // 256, 210), np.uint8)
+    out[..., 0] = h & 0xFF
+    out[..., 1] = h >> 8
+    scg = sc.reshape(rows, K // 256, 8, 2)
+    for g in range(8):
+        base = 2 + 26 * g
+        out[..., base] = (scg[..., g, 0] & 0xFF).astype(np.uint8)
+        out[..., base + 1] = (scg[..., g, 1] & 0xFF).astype(np.uint8)
+        cg = c[..., g, :]
+        out[..., base + 2:base + 18] = ((cg[..., :16] & 15) | ((cg[..., 16:] & 15) << 4)).astype(np.uint8)
+        for half, off in ((0, 18), (1, 22)):
+            for b in range(4):
+                v = np.zeros(cg.shape[:-1], np.int64)
+                for w in range(4):
+                    v |= ((cg[..., 16 * half + 4 * w + b] >> 4) & 3) << (2 * w)
+                out[..., base + off + b] = v.astype(np.uint8)
+    return out.reshape(rows, -1)
+
+
+def mixed(rng, rows, K):
+    W = rng.normal(0, 0.02, (rows, K)).astype(np.float32)
+    W[rows // 4] *= 1e-6                       # fp16-subnormal scales
+    W[rows // 3] = 0.0                         # zero blocks
+    W[rows // 2, ::7] = 0.5                    # outliers
+    t = rng.integers(-7, 8, (K,)).astype(np.float32)
+    W[rows - 1] = t * np.float32(0.125) + np.float32(0.0625)  # halves: rounding ties
+    return W
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_q4_0_q8_0_agree_with_oracle(seed):
+    rng = np.random.default_rng(1000 + seed)
+    for rows, K in ((37, 32 * 41), (8, 4096)):
+        W = mixed(rng, rows, K)
+        assert np.array_equal(np_quant_b32(W, 7), oracle.quantize(0, W)), (rows, K)
+        assert np.array_equal(np_quant_b32(W, 127), oracle.quantize(1, W)), (rows, K)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_q6_k_agrees_with_oracle(seed):
+    rng = np.random.default_rng(2000 + seed)
+    for rows, K in ((29, 256 * 5), (6, 4096)):
+        W = mixed(rng, rows, K)
+        assert np.array_equal(np_quant_q6k(W), oracle.quantize(3, W)), (rows, K)

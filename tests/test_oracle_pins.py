@@ -55,9 +55,10 @@ def pin_f16_encode_sweep(orc: Oracle):
     three_q = v + 3 * (nxt - v) / 4
     pos = np.concatenate([v, mids, quarter, three_q]).astype(np.float32)
     rng = np.random.default_rng(1234)
-    rand_bits = rng.integers(0, 2**32, size=2_000_000, dtype=np.uint64).astype(np.uint32)
+    # about 10^7 values in all
+    rand_bits = rng.integers(0, 2**32, size=6_500_000, dtype=np.uint64).astype(np.uint32)
     rand = rand_bits.view(np.float32)
-    near = (rng.uniform(-27, 17, size=1_000_000)).astype(np.float64)
+    near = (rng.uniform(-27, 17, size=3_000_000)).astype(np.float64)
     near = (np.exp2(near) * rng.choice([-1.0, 1.0], size=near.size)).astype(np.float32)
     allv = np.concatenate([pos, -pos, rand, near])
     got = orc.f32_to_f16_array(allv)
