@@ -239,6 +239,7 @@ int qmat_prefill(int fmt, const void *blocks, const float *X, void *xq, float *Y
  *   Shapes: 0 <= n, cell0 and cell0 + n <= cells (QMAT_E_SHAPE otherwise).
  *   rows, bias (if given) and cache + cell0 * row_bytes must be 16-byte
  *   aligned (QMAT_E_ALIGN); any cell0 qualifies when dim is a multiple of 256.
+ *   rows and bias must not overlap the cache.
  *   n == 0 or dim == 0 enqueues nothing.
  */
 int qmat_kv_write(int fmt, const float *rows, const float *bias, void *cache,
