@@ -423,12 +423,17 @@ def test_gemm_decode_full_size_sampled(q):
     torch.cuda.empty_cache()
 
 
-def test_gemm_k_zero(q):
+@pytest.mark.parametrize("fmt", [0, 1, 2, 3])
+def test_gemm_k_zero(q, fmt):
+    """Empty sums: both the decode-batch path (7 tokens) and the MFMA tiles
+    (70 tokens, ragged in M and N) write zeros over whatever Y held."""
     import torch
-    say("gemm K=0")
     e = torch.empty(0, dtype=torch.uint8, device="cuda")
-    Y = q.gemm(0, e, e, 33, 0, 7)
-    assert np.array_equal(host(Y), np.zeros((7, 33), np.float32))
+    for N in (7, 70):
+        say(f"gemm K=0 fmt={fmt} N={N}")
+        Y = torch.full((N, 133), 3.0, dtype=torch.float32, device="cuda")
+        q.gemm(fmt, e, e, 133, 0, N, out=Y)
+        assert np.array_equal(host(Y), np.zeros((N, 133), np.float32))
 
 
 @pytest.mark.parametrize("fmt", [0, 1, 2, 3])
@@ -449,6 +454,12 @@ def test_prefill_one_call(q, fmt):
         assert np.array_equal(host(Y), host(q.gemm(fmt, dB, xq, M, K, N)))
         ref = oracle.gemm(fmt, oracle.quantize(fmt, W), Xq, M, K, N)
         assert rel_l2(host(Y), ref) <= GEMM_TOL
+    # K = 0: nothing to quantize, and every output is an empty sum
+    say(f"prefill one call fmt={fmt} K=0")
+    Y0 = torch.full((5, 7), 3.0, dtype=torch.float32, device="cuda")
+    q.prefill(fmt, torch.empty((7, 0), dtype=torch.uint8, device="cuda"),
+              torch.empty((5, 0), dtype=torch.float32, device="cuda"), 7, out=Y0)
+    assert np.array_equal(host(Y0), np.zeros((5, 7), np.float32))
     torch.cuda.synchronize()
 
 
