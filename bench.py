@@ -92,12 +92,17 @@ def parse():
     return p.parse_args()
 
 
-def measured_peaks(torch) -> dict:
+def measured_peaks(torch, slice_bytes: int | None = None) -> dict:
     """This GPU's own peaks, for the rooflines beside the nominal ones: HBM
     read bandwidth over a 2 GiB buffer (beyond the 256 MB Infinity Cache),
     the dense int8 MFMA rate, the plain (non-packed) fp32 FMA rate, and the
     FMA rate of waves that share their SIMDs with int8 MFMA waves. Each is
-    the best of five event-timed launches."""
+    the best of five event-timed launches.
+
+    With slice_bytes, also the read rate of launches that each read only
+    that many bytes, back to back, from a different part of the 2 GiB
+    buffer every time (so from HBM): the ceiling that a kernel streaming
+    slice_bytes per launch, timed the same way, can reach."""
     import ctypes
     from block_quantized_weight_qmat_amd import binding
     path = os.path.join(os.path.dirname(binding.library_path()), "libqmat_micro.so")
@@ -134,6 +139,28 @@ def measured_peaks(torch) -> dict:
                                                      P(out.data_ptr()), g, sp))
              for g in read_grids)
     hbm = read_bytes / ms / 1e6
+    sliced = None
+    if slice_bytes:
+        n16 = slice_bytes // 16 * 16
+        stride = -(-n16 // 4096) * 4096
+        slots = read_bytes // stride
+        launches = min(64, slots)
+
+        def mean_ms(g):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for i in range(launches):
+                rc = lib.qmat_micro_read(P(buf.data_ptr() + (i % slots) * stride), n16,
+                                         P(out.data_ptr()), g, sp)
+                if rc != 0:
+                    raise RuntimeError(f"measured-peak kernel failed to launch ({rc})")
+            b.record(stream)
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) / launches
+
+        ms = min(min(mean_ms(g) for _ in range(3)) for g in (256, 512, 1024, 2048))
+        sliced = {"bytes": n16, "GBs": round(n16 / ms / 1e6, 1), "us": round(1e3 * ms, 3)}
     del buf
     grid, iters = 2048, 2000
     ms = best_ms(lambda: lib.qmat_micro_mfma_i8(iters, P(out.data_ptr()), grid, sp))
@@ -146,8 +173,11 @@ def measured_peaks(torch) -> dict:
     fma_mix = mix_grid * 256 * iters * 8 * 2 / ms / 1e9
     return {"hbm_read_GBs": round(hbm, 1), "int8_mfma_TOPS": round(mfma, 1),
             "fp32_fma_TFLOPs": round(fma, 2), "fp32_fma_TFLOPs_beside_mfma": round(fma_mix, 2),
+            "hbm_read_same_bytes": sliced,
             "kernels": "libqmat_micro.so: 2 GiB coalesced read (best of 1024-8192 "
-                       "workgroups); 4 chains of "
+                       "workgroups); the same read over the GEMV's bytes per launch, "
+                       f"{launches if slice_bytes else 0} launches back to back from "
+                       "distinct offsets (best of 256-2048 workgroups); 4 chains of "
                        "v_mfma_i32_32x32x32_i8 per wave; 8 chains of v_fma_f32 per lane; "
                        "half MFMA, half FMA waves per SIMD"}
 
@@ -421,7 +451,7 @@ def main():
                "sample": f"{reps} full Q4_0 GEMVs 4096x11008 (dequantize to fp64, fp64 dot, "
                          f"OpenMP over rows) in {t_cpu:.1f} s; same algorithmic bytes as value"}
 
-    peaks = None if args.no_peaks else measured_peaks(torch)
+    peaks = None if args.no_peaks else measured_peaks(torch, gemv_bytes.get("q4_0"))
     headline = kernels.get("gemv_q4_0")
     gemm = kernels.get("gemm_q4_0")
     traffic = traffic_for_current_kernel() if headline else None
@@ -448,7 +478,9 @@ def main():
             "kernel": "gemv_q4_0", "bytes_per_launch": gemv_bytes["q4_0"],
             "us_per_launch": round(headline["us"], 3),
             "frac_of_measured": None if not peaks else round(
-                headline["GB/s"] / peaks["hbm_read_GBs"], 4)},
+                headline["GB/s"] / peaks["hbm_read_GBs"], 4),
+            "frac_of_same_bytes_read": None if not (peaks and peaks["hbm_read_same_bytes"]) else round(
+                headline["GB/s"] / peaks["hbm_read_same_bytes"]["GBs"], 4)},
         "gemm_int8_tops": None if not gemm else round(gemm["TOPS"], 1),
         "gemm_frac_of_int8_peak": None if not gemm else round(gemm["frac"], 4),
         "gemm_frac_of_measured_int8": None if not (gemm and peaks) else round(
