@@ -92,6 +92,19 @@ def parse():
     return p.parse_args()
 
 
+def read_slices(buf_bytes: int, slice_bytes: int, max_launches: int = 64):
+    """Launch plan for reading slice_bytes at a time out of a buffer of
+    buf_bytes: (bytes per launch, a multiple of 16; stride between launch
+    starts, a multiple of 4096; number of disjoint slots; launches). Launch
+    i reads [i * stride, i * stride + bytes), inside the buffer."""
+    n16 = slice_bytes // 16 * 16
+    if n16 < 16 or n16 > buf_bytes:
+        raise ValueError(f"cannot read {slice_bytes} bytes at a time from {buf_bytes}")
+    stride = -(-n16 // 4096) * 4096
+    slots = max(1, buf_bytes // stride)
+    return n16, stride, slots, min(max_launches, slots)
+
+
 def measured_peaks(torch, slice_bytes: int | None = None) -> dict:
     """This GPU's own peaks, for the rooflines beside the nominal ones: HBM
     read bandwidth over a 2 GiB buffer (beyond the 256 MB Infinity Cache),
@@ -141,10 +154,7 @@ def measured_peaks(torch, slice_bytes: int | None = None) -> dict:
     hbm = read_bytes / ms / 1e6
     sliced = None
     if slice_bytes:
-        n16 = slice_bytes // 16 * 16
-        stride = -(-n16 // 4096) * 4096
-        slots = read_bytes // stride
-        launches = min(64, slots)
+        n16, stride, slots, launches = read_slices(read_bytes, slice_bytes)
 
         def mean_ms(g):
             a = torch.cuda.Event(enable_timing=True)

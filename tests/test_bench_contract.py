@@ -67,3 +67,25 @@ def test_counter_calibration(tmp_path, monkeypatch):
     t["gemv_src_sha256_16"] = "0" * 16
     out.write_text(json.dumps(t))
     assert bench.traffic_for_current_kernel() is None
+
+
+@pytest.mark.parametrize("slice_bytes", [16, 4095, 4096, 25422848, 25804817, 1 << 30, 2 << 30])
+def test_read_slices_stay_in_the_buffer(slice_bytes):
+    """Every launch of the same-bytes read starts 4 KiB-aligned, reads a
+    multiple of 16 bytes, and ends inside the 2 GiB buffer; distinct
+    launches read disjoint parts of it."""
+    buf = 2 << 30
+    n16, stride, slots, launches = bench.read_slices(buf, slice_bytes)
+    assert n16 % 16 == 0 and 0 <= slice_bytes - n16 < 16 and stride % 4096 == 0
+    assert stride >= n16 and 1 <= launches <= min(64, slots)
+    for i in range(launches):
+        assert i * stride + n16 <= buf
+    if slice_bytes == 25422848:
+        assert launches == 64 and launches * n16 > 256 << 20   # beyond the Infinity Cache
+
+
+def test_read_slices_refuse_what_does_not_fit():
+    with pytest.raises(ValueError):
+        bench.read_slices(1 << 20, (1 << 20) + 16)
+    with pytest.raises(ValueError):
+        bench.read_slices(1 << 20, 15)
