@@ -750,7 +750,9 @@ constexpr int kRowWaves = QMAT_GEMV_ROW_WAVES;
 constexpr int kRowSlot = 8192;  // one strip of fp32 activations
 // A wait for a ready flag gives up after this many polls (each with a short
 // sleep, some tens of milliseconds in all) instead of hanging the device if
-// a flag were never raised; the flags are raised unconditionally.
+// a flag were never raised; the flags are raised unconditionally. A wave
+// that gave up writes NaN to its rows, so the failure cannot pass as a
+// plausible result.
 constexpr int kRowSpinLimit = 1 << 20;
 
 // LDS flags as relaxed workgroup-scope atomics: read afresh on every poll
@@ -908,11 +910,13 @@ __global__ __launch_bounds__(kRowWaves * kWave) void gemv_rows_kernel(
   float part[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) part[r] = 0.0f;
+  bool lost = false;  // a flag wait gave up
   // strip st from buffer w, then (if `next`) strip st + kD into w
   auto step = [&](int st, typename F::Raw (&w)[R], bool next) {
     const int j = st * kWave + lane;
-    for (int n = 0; flag_get(&ready[st]) == 0 && n < kRowSpinLimit; ++n)
-      __builtin_amdgcn_s_sleep(1);
+    int n = 0;
+    for (; flag_get(&ready[st]) == 0 && n < kRowSpinLimit; ++n) __builtin_amdgcn_s_sleep(1);
+    lost |= n == kRowSpinLimit;
     asm volatile("" ::: "memory");
     XP xp;
     get_rec(slots + st * kRowSlot, lane, xp, F::kSum);
@@ -941,7 +945,8 @@ __global__ __launch_bounds__(kRowWaves * kWave) void gemv_rows_kernel(
   constexpr int kShift = 6 - log2i<R>();
   const int r = (lane >> kShift) & (R - 1);
   const float sum = wave_reduce_rows<R>(part, lane);
-  if ((lane & ((1 << kShift) - 1)) == 0 && m0 + r < M) y[m0 + r] = sum;
+  if ((lane & ((1 << kShift) - 1)) == 0 && m0 + r < M)
+    y[m0 + r] = lost ? __builtin_nanf("") : sum;
 }
 
 #ifndef QMAT_GEMV_CFG

@@ -169,6 +169,11 @@ int qmat_quantize(int fmt, const float *W, void *blocks, int64_t rows,
  *   20-bit integer (|X| < 2^19, relative step <= 2^-17.9 of the slice's
  *   largest element), the integer dot products with the codes are exact,
  *   and the per-block results are accumulated in fp32.
+ *   Rows of 8192 to 16384 elements are computed by waves that wait, with a
+ *   bounded number of polls, for activation records that other waves of
+ *   their workgroup publish; a wave whose wait ran out (never expected: the
+ *   records are always published) writes NaN to its rows rather than a
+ *   value computed from incomplete records.
  */
 int qmat_gemv(int fmt, const void *blocks, const float *x, float *y,
               int64_t M, int64_t K, void *stream);

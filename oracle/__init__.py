@@ -84,6 +84,8 @@ class Oracle:
         lib.oracle_kv_write.restype = ctypes.c_int
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = ctypes.c_int
+        lib.oracle_set_threads.argtypes = [ctypes.c_int]
+        lib.oracle_set_threads.restype = ctypes.c_int
         self.lib = lib
         self.path = path
 
@@ -101,6 +103,10 @@ class Oracle:
 
     def num_threads(self) -> int:
         return int(self.lib.oracle_num_threads())
+
+    def set_threads(self, n: int) -> int:
+        """OpenMP threads for later calls; returns the number in effect."""
+        return int(self.lib.oracle_set_threads(int(n)))
 
     # fp16 ------------------------------------------------------------------
     def f32_to_f16_bits(self, v: float) -> int:

@@ -533,3 +533,16 @@ int oracle_num_threads(void) {
   return 1;
 #endif
 }
+
+/* Set the number of OpenMP threads for the oracle's later parallel loops
+ * (n < 1 leaves it unchanged); returns the number now in effect. Used by the
+ * benchmark's CPU baseline to time one thread beside all of them. */
+int oracle_set_threads(int n) {
+#ifdef _OPENMP
+  if (n >= 1) omp_set_num_threads(n);
+  return omp_get_max_threads();
+#else
+  (void)n;
+  return 1;
+#endif
+}
