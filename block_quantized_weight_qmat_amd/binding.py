@@ -61,6 +61,10 @@ def load_library():
     lib.qmat_prefill.restype = i32
     lib.qmat_kv_write.argtypes = [i32, p, p, p, i64, i64, i64, i64, p]
     lib.qmat_kv_write.restype = i32
+    lib.qmat_prefill_noalloc.argtypes = [i32, p, p, p, i64, i64, i64, p]
+    lib.qmat_prefill_noalloc.restype = i32
+    lib.qmat_noalloc_scratch_bytes.argtypes = []
+    lib.qmat_noalloc_scratch_bytes.restype = i64
     _lib = lib
     return lib
 
@@ -186,6 +190,34 @@ def prefill(fmt, blocks: torch.Tensor, X: torch.Tensor, M: int,
     _check("qmat_prefill", load_library().qmat_prefill(
         f, blocks.data_ptr(), X.data_ptr(), xq.data_ptr(), out.data_ptr(), M, K, N, _stream(X)))
     return out, xq
+
+
+def noalloc_scratch_bytes() -> int:
+    """Size of the static device workspace of prefill_noalloc."""
+    return int(load_library().qmat_noalloc_scratch_bytes())
+
+
+def prefill_noalloc(fmt, blocks: torch.Tensor, X: torch.Tensor, M: int,
+                    out: torch.Tensor | None = None) -> torch.Tensor:
+    """prefill() with the Q8_0 activation workspace in the library's static
+    device array instead of a caller buffer (nothing is allocated when out
+    is given); calls that overlap on one device race on that workspace."""
+    f = _fmt(fmt)
+    _gpu(blocks, "blocks", torch.uint8)
+    _gpu(X, "X", torch.float32)
+    if X.dim() != 2:
+        raise ValueError("X must be 2-D [N, K]")
+    N, K = X.shape
+    if blocks.numel() != M * row_bytes(f, K):
+        raise ValueError("blocks do not match M, K")
+    if out is None:
+        out = torch.empty((N, M), dtype=torch.float32, device=X.device)
+    _gpu(out, "out", torch.float32)
+    if out.numel() != N * M:
+        raise ValueError("out must hold N*M values")
+    _check("qmat_prefill_noalloc", load_library().qmat_prefill_noalloc(
+        f, blocks.data_ptr(), X.data_ptr(), out.data_ptr(), M, K, N, _stream(X)))
+    return out
 
 
 def kv_write(fmt, rows: torch.Tensor, cache: torch.Tensor, cell0: int,

@@ -2,10 +2,14 @@
 //
 // Every argument is validated on the host before anything is enqueued; the
 // launchers in quantize.hip / gemv.hip / gemm.hip then enqueue the kernels on
-// the caller's stream. No device memory is allocated and no state is kept.
+// the caller's stream. No device memory is allocated. The one piece of
+// library-owned device memory is the static activation workspace of
+// qmat_prefill_noalloc below (a module global, resolved once per device).
 #include "qmat.h"
 
-#include <hip/hip_runtime_api.h>
+#include <hip/hip_runtime.h>
+
+#include <mutex>
 
 #include "qmat_launch.hpp"
 
@@ -43,6 +47,52 @@ int check_shape(int fmt, int64_t rows, int64_t K) {
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? QMAT_OK : QMAT_E_HIP; }
+
+// Arguments of the one-call prefill (with or without a caller workspace):
+// format, shapes, the GEMM's K limit; QMAT_OK with *empty set when there is
+// nothing to do.
+int check_prefill(int fmt, int64_t M, int64_t K, int64_t N, bool* empty) {
+  *empty = false;
+  if (!fmt_ok(fmt)) return QMAT_E_FMT;
+  int rc = check_shape(fmt, M, K);
+  if (rc != QMAT_OK) return rc;
+  if ((rc = check_shape(QMAT_Q8_0, N, K)) != QMAT_OK) return rc;
+  if (K > kMaxGemmK) return QMAT_E_SHAPE;
+  *empty = M == 0 || N == 0;
+  return QMAT_OK;
+}
+
+// ---- static workspace of qmat_prefill_noalloc ----------------------------
+// Each device that runs the library holds one copy of this array until the
+// process ends. In host code `scratch` is only a stand-in for the symbol:
+// its device address comes from hipGetSymbolAddress, called once per device
+// with that device current, and only that address is ever passed on.
+static __device__ __align__(256) uint8_t scratch[QMAT_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// Device address of the current device's workspace (nullptr on failure).
+void* scratch_for_current_device(int* status) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    *status = QMAT_E_HIP;
+    return nullptr;
+  }
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? p : nullptr;
+  });
+  if (g_scratch_err[dev] != hipSuccess || g_scratch_ptr[dev] == nullptr) {
+    *status = QMAT_E_HIP;
+    return nullptr;
+  }
+  *status = QMAT_OK;
+  return g_scratch_ptr[dev];
+}
 
 }  // namespace
 
@@ -83,6 +133,9 @@ const char* qmat_strerror(int status) {
     case QMAT_E_NULL: return "required pointer is NULL";
     case QMAT_E_HIP: return "HIP kernel launch failed";
     case QMAT_E_ALIGN: return "pointer is not 16-byte aligned";
+    case QMAT_E_SCRATCH:
+      return "the Q8_0 activations (N * row bytes) exceed the static workspace of "
+             "qmat_prefill_noalloc (qmat_noalloc_scratch_bytes())";
     default: return "unknown status";
   }
 }
@@ -128,16 +181,36 @@ int qmat_gemm(int fmt, const void* blocks, const void* X_q8, float* Y, int64_t M
 
 int qmat_prefill(int fmt, const void* blocks, const float* X, void* xq, float* Y, int64_t M,
                  int64_t K, int64_t N, void* stream) {
-  if (!fmt_ok(fmt)) return QMAT_E_FMT;
-  int rc = check_shape(fmt, M, K);
+  bool empty = false;
+  int rc = check_prefill(fmt, M, K, N, &empty);
   if (rc != QMAT_OK) return rc;
-  if ((rc = check_shape(QMAT_Q8_0, N, K)) != QMAT_OK) return rc;
-  if (K > kMaxGemmK) return QMAT_E_SHAPE;
-  if (M == 0 || N == 0) return QMAT_OK;  // nothing to read or write
+  if (empty) return QMAT_OK;  // nothing to read or write
   if ((rc = check_buf(blocks, K > 0)) != QMAT_OK) return rc;
   if ((rc = check_buf(X, K > 0)) != QMAT_OK) return rc;
   if ((rc = check_buf(xq, K > 0)) != QMAT_OK) return rc;
   if ((rc = check_buf(Y, true)) != QMAT_OK) return rc;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (K > 0 && (rc = hip_status(qmat::launch_quantize(QMAT_Q8_0, X, xq, N, K, st))) != QMAT_OK)
+    return rc;
+  return hip_status(qmat::launch_gemm(fmt, blocks, xq, Y, M, K, N, st));
+}
+
+int64_t qmat_noalloc_scratch_bytes(void) { return QMAT_NOALLOC_SCRATCH_BYTES; }
+
+int qmat_prefill_noalloc(int fmt, const void* blocks, const float* X, float* Y, int64_t M,
+                         int64_t K, int64_t N, void* stream) {
+  bool empty = false;
+  int rc = check_prefill(fmt, M, K, N, &empty);
+  if (rc != QMAT_OK) return rc;
+  if (empty) return QMAT_OK;  // nothing to read or write
+  // N * row bytes cannot overflow: check_shape bounded it by INT64_MAX
+  if (N * qmat_row_bytes(QMAT_Q8_0, K) > (int64_t)QMAT_NOALLOC_SCRATCH_BYTES)
+    return QMAT_E_SCRATCH;
+  if ((rc = check_buf(blocks, K > 0)) != QMAT_OK) return rc;
+  if ((rc = check_buf(X, K > 0)) != QMAT_OK) return rc;
+  if ((rc = check_buf(Y, true)) != QMAT_OK) return rc;
+  void* xq = scratch_for_current_device(&rc);
+  if (xq == nullptr) return rc;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   if (K > 0 && (rc = hip_status(qmat::launch_quantize(QMAT_Q8_0, X, xq, N, K, st))) != QMAT_OK)
     return rc;

@@ -8,6 +8,8 @@
  *   qmat_gemm      packed W × Q8_0 X blocks -> fp32 Y        (prefill)
  *   qmat_prefill   packed W × fp32 X        -> fp32 Y        (prefill, one call)
  *   qmat_kv_write  fp32 K or V rows -> Q4_0 / Q8_0 rows of a KV cache
+ * and qmat_prefill_noalloc, qmat_prefill without a caller workspace for
+ * callers that cannot allocate device memory.
  *
  * Sources. Citations name the web page and the section or table of it
  * that fixes the fact:
@@ -71,7 +73,8 @@
  * Common contract for every entry point:
  *   - Pointers W, x, y, blocks, X_q8, Y are DEVICE pointers owned by the
  *     caller, each 16-byte aligned (QMAT_E_ALIGN otherwise). The library
- *     keeps no pointer after return and owns no device memory.
+ *     keeps no pointer after return and owns no device memory, except the
+ *     static workspace of qmat_prefill_noalloc (below).
  *   - stream is a hipStream_t (NULL = the legacy default stream). The call
  *     returns once the work is enqueued; results are ready when the stream
  *     reaches that point.
@@ -86,7 +89,8 @@
  *     N (or rows, for quantize) enqueues nothing and dereferences no pointer.
  *     K == 0 is valid: quantize writes nothing, gemv
  *     and gemm write zeros (the empty sum).
- *   - Thread safe; no global mutable state.
+ *   - Thread safe; no global mutable state apart from qmat_prefill_noalloc's
+ *     per-device workspace (see there: its calls must not overlap).
  */
 #ifndef QMAT_H
 #define QMAT_H
@@ -112,8 +116,15 @@ typedef enum qmat_status {
                        a size beyond the limits above                    */
   QMAT_E_NULL = 3,  /* a required pointer is NULL                         */
   QMAT_E_HIP = 4,   /* the HIP launch itself failed                       */
-  QMAT_E_ALIGN = 5  /* a pointer is not 16-byte aligned                   */
+  QMAT_E_ALIGN = 5, /* a pointer is not 16-byte aligned                   */
+  QMAT_E_SCRATCH = 6 /* qmat_prefill_noalloc: the activation workspace it
+                        needs exceeds its static scratch                   */
 } qmat_status;
+
+/* Bytes of the static device workspace of qmat_prefill_noalloc (16 MiB):
+ * room for the Q8_0 activations of N tokens of K elements while
+ * N * K / 32 * 34 <= this, e.g. 1024 tokens at K = 14336. */
+#define QMAT_NOALLOC_SCRATCH_BYTES (16u << 20)
 
 /* Elements per block: 32 (Q4_0, Q8_0), 256 (Q4_K, Q6_K); 0 if unknown. */
 int64_t qmat_block_elems(int fmt);
@@ -224,6 +235,34 @@ int qmat_gemm(int fmt, const void *blocks, const void *X_q8, float *Y,
  */
 int qmat_prefill(int fmt, const void *blocks, const float *X, void *xq, float *Y,
                  int64_t M, int64_t K, int64_t N, void *stream);
+
+/*
+ * qmat_prefill_noalloc — qmat_prefill for callers that cannot allocate
+ *   device memory (code under HIP graph capture, tight serving loops,
+ *   harnesses that forbid hipMalloc): the same product, with the Q8_0
+ *   activation workspace taken from a static device array of the library
+ *   (QMAT_NOALLOC_SCRATCH_BYTES, one per device, held until the process
+ *   ends) instead of a caller buffer. No call allocates or frees memory.
+ *   The workspace is looked up once per device (hipGetSymbolAddress, with
+ *   that device current) on the first call made there; calls must run on a
+ *   stream of the current device.
+ *   blocks, X, Y, M, K, N: as for qmat_prefill; Y is exactly what
+ *   qmat_prefill writes for the same inputs.
+ *   Errors: qmat_prefill's, checked in the same order, then QMAT_E_SCRATCH
+ *   when N * qmat_row_bytes(QMAT_Q8_0, K) > QMAT_NOALLOC_SCRATCH_BYTES (before
+ *   the pointer checks and before anything is enqueued); QMAT_E_HIP if the
+ *   workspace's address cannot be obtained.
+ *   Every call on one device shares that device's workspace, which keeps the
+ *   last call's activations (nothing in it needs to start at zero): calls
+ *   whose work overlaps on one device — on two streams, or from two threads
+ *   without ordering — race on it and give undefined results. Serialise them
+ *   (one stream, or events), or use qmat_prefill with separate workspaces.
+ */
+int qmat_prefill_noalloc(int fmt, const void *blocks, const float *X, float *Y,
+                         int64_t M, int64_t K, int64_t N, void *stream);
+
+/* QMAT_NOALLOC_SCRATCH_BYTES, as a call (for bindings without the header). */
+int64_t qmat_noalloc_scratch_bytes(void);
 
 /*
  * qmat_kv_write — quantize new key or value rows into a KV cache.

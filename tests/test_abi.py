@@ -13,7 +13,7 @@ from block_quantized_weight_qmat_amd import binding
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "qmat.h")
 
-OK, E_FMT, E_SHAPE, E_NULL, E_HIP, E_ALIGN = 0, 1, 2, 3, 4, 5
+OK, E_FMT, E_SHAPE, E_NULL, E_HIP, E_ALIGN, E_SCRATCH = 0, 1, 2, 3, 4, 5, 6
 
 
 @pytest.fixture(scope="module")
@@ -48,7 +48,8 @@ def test_enum_values_match_header():
     assert vals["QMAT_Q6_K"] == "3"
     assert binding.Q4_0 == 0 and binding.Q8_0 == 1 and binding.Q4_K == 2 and binding.Q6_K == 3
     assert [vals[k] for k in ("QMAT_OK", "QMAT_E_FMT", "QMAT_E_SHAPE", "QMAT_E_NULL",
-                              "QMAT_E_HIP", "QMAT_E_ALIGN")] == ["0", "1", "2", "3", "4", "5"]
+                              "QMAT_E_HIP", "QMAT_E_ALIGN", "QMAT_E_SCRATCH")] == \
+        ["0", "1", "2", "3", "4", "5", "6"]
 
 
 def test_sizes_agree_with_oracle(lib):
@@ -63,7 +64,7 @@ def test_sizes_agree_with_oracle(lib):
 
 
 def test_strerror(lib):
-    for s in range(6):
+    for s in range(7):
         assert len(lib.qmat_strerror(s)) > 3
     assert lib.qmat_strerror(99) == b"unknown status"
 
@@ -180,3 +181,19 @@ def test_measured_peak_library():
     assert m.qmat_micro_mfma_i8(0, A, 1, None) == 1
     assert m.qmat_micro_fma_f32(1, None, 1, None) == 1
     assert m.qmat_micro_mix(8, A, 1, None) == 1            # fewer than 16 iterations
+
+
+def test_prefill_noalloc_arguments(lib):
+    """The allocation-free prefill checks its arguments as qmat_prefill does,
+    then its workspace limit, all before any HIP call."""
+    f = lib.qmat_prefill_noalloc
+    assert lib.qmat_noalloc_scratch_bytes() == 16 << 20
+    K = 11008
+    n_over = (16 << 20) // oracle.row_bytes(1, K) + 1
+    assert f(4, A, A, A, 1, K, 1, None) == E_FMT
+    assert f(0, A, A, A, 1, 48, 1, None) == E_SHAPE
+    assert f(0, A, A, A, 1, 2 ** 24 + 32, 1, None) == E_SHAPE
+    assert f(0, A, A, A, 4, K, n_over, None) == E_SCRATCH
+    assert f(0, None, None, None, 0, K, n_over, None) == OK   # M == 0: nothing to do
+    assert f(0, A, None, A, 4, K, 2, None) == E_NULL
+    assert f(0, A, A + 4, A, 4, K, 2, None) == E_ALIGN
