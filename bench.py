@@ -25,6 +25,15 @@ Timing, two passes:
     so the events see the GPU's own time per launch, which agrees with
     rocprofv3's kernel durations.
 
+Beside the step, every other workload of the measurement plan is timed per
+kernel (``kernels``): the 1024x1024 Q4_0 GEMV (latency); the 196-matrix
+Qwen3-0.6B-like decode set as one pass of 196 GEMV launches, Q4_0 and Q8_0,
+rotating over copies of the whole set; the 11008x4096 orientation of the 7B
+layer (the strip kernel); the Q4_K-style GEMV at 4096x4096 and 4096x11008
+with per-row scale spread; the decode batch, the Q6_K-style kernels, the
+other GEMM formats and the KV-cache write. The prefill GEMM reads a different
+copy of W at every launch as the GEMVs do.
+
 Output: one JSON line. ``value`` is the Q4_0 GEMV's algorithmic bytes
 (packed weights + x + y) divided by its mean time per launch, the headline of
 the metric; the GEMM's int8 TOPS and every other kernel's rate and roofline
@@ -69,9 +78,15 @@ ALL_OPS = ["quantize_q4_0", "quantize_q8_0", "quantize_q4_k", "gemv_q4_0", "gemv
 # into a 16384-cell cache, Q4_0 with the per-channel bias and Q8_0 without
 KV_DIM, KV_CELLS, KV_N = 1024, 16384, 512
 DECODE_NS = (4, 16)
-EXTRA_OPS = [f"decode_q4_0_n{n}" for n in DECODE_NS] + ["quantize_q6_k", "gemv_q6_k", "gemm_q8_0",
-                                                         "gemm_q4_k", "gemm_q6_k",
-                                                         "kv_write_q4_0", "kv_write_q8_0"]
+# the other decode workloads: (name, format id, workload)
+GEMV_EXTRA = [("gemv_q4_0_1024x1024", 0, "gemv_1024"),
+              ("gemv_q4_0_11008x4096", 0, "llama7b_1"), ("gemv_q8_0_11008x4096", 1, "llama7b_1"),
+              ("gemv_q4_k_4096x4096_spread", 2, "q4k_0"),
+              ("gemv_q4_k_4096x11008_spread", 2, "q4k_1")]
+QWEN3_OPS = ["qwen3_pass_q4_0", "qwen3_pass_q8_0"]
+EXTRA_OPS = ([f"decode_q4_0_n{n}" for n in DECODE_NS] + [g[0] for g in GEMV_EXTRA] + QWEN3_OPS
+             + ["quantize_q6_k", "gemv_q6_k", "gemm_q8_0", "gemm_q4_k", "gemm_q6_k",
+                "kv_write_q4_0", "kv_write_q8_0"])
 
 
 def parse():
@@ -115,7 +130,10 @@ def measured_peaks(torch, slice_bytes: int | None = None) -> dict:
     With slice_bytes, also the read rate of launches that each read only
     that many bytes, back to back, from a different part of the 2 GiB
     buffer every time (so from HBM): the ceiling that a kernel streaming
-    slice_bytes per launch, timed the same way, can reach."""
+    slice_bytes per launch, timed the same way (timed_batch: the launches
+    queued behind a GPU sleep, so host launch gaps do not count), can reach.
+    The best of four launch shapes, each the mean over a batch of
+    launches."""
     import ctypes
     from block_quantized_weight_qmat_amd import binding
     path = os.path.join(os.path.dirname(binding.library_path()), "libqmat_micro.so")
@@ -156,21 +174,20 @@ def measured_peaks(torch, slice_bytes: int | None = None) -> dict:
     if slice_bytes:
         n16, stride, slots, launches = read_slices(read_bytes, slice_bytes)
 
-        def mean_ms(g):
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            for i in range(launches):
-                rc = lib.qmat_micro_read(P(buf.data_ptr() + (i % slots) * stride), n16,
-                                         P(out.data_ptr()), g, sp)
-                if rc != 0:
-                    raise RuntimeError(f"measured-peak kernel failed to launch ({rc})")
-            b.record(stream)
-            torch.cuda.synchronize()
-            return a.elapsed_time(b) / launches
+        def launch_slice(g, i):
+            rc = lib.qmat_micro_read(P(buf.data_ptr() + (i % slots) * stride), n16,
+                                     P(out.data_ptr()), g, sp)
+            if rc != 0:
+                raise RuntimeError(f"measured-peak kernel failed to launch ({rc})")
 
-        ms = min(min(mean_ms(g) for _ in range(3)) for g in (256, 512, 1024, 2048))
-        sliced = {"bytes": n16, "GBs": round(n16 / ms / 1e6, 1), "us": round(1e3 * ms, 3)}
+        for g in (256, 512, 1024, 2048):  # warm up every launch shape
+            launch_slice(g, 0)
+        torch.cuda.synchronize()
+        us = {g: timed_batch(torch, lambda i, g=g: launch_slice(g, i), launches)
+              for g in (256, 512, 1024, 2048)}
+        g_best = min(us, key=us.get)
+        sliced = {"bytes": n16, "GBs": round(n16 / us[g_best] / 1e3, 1),
+                  "us": round(us[g_best], 3), "workgroups": g_best, "launches": launches}
     del buf
     grid, iters = 2048, 2000
     ms = best_ms(lambda: lib.qmat_micro_mfma_i8(iters, P(out.data_ptr()), grid, sp))
@@ -187,7 +204,8 @@ def measured_peaks(torch, slice_bytes: int | None = None) -> dict:
             "kernels": "libqmat_micro.so: 2 GiB coalesced read (best of 1024-8192 "
                        "workgroups); the same read over the GEMV's bytes per launch, "
                        f"{launches if slice_bytes else 0} launches back to back from "
-                       "distinct offsets (best of 256-2048 workgroups); 4 chains of "
+                       "distinct offsets queued behind a GPU sleep (best of 256-2048 "
+                       "workgroups); 4 chains of "
                        "v_mfma_i32_32x32x32_i8 per wave; 8 chains of v_fma_f32 per lane; "
                        "half MFMA, half FMA waves per SIMD"}
 
@@ -276,10 +294,11 @@ def traffic_for_current_kernel():
 
 
 # ------------------------------------------------------------------ timing
-def timed_batch(torch, fn, n: int) -> float:
-    """Mean GPU time per launch (us) of n back-to-back launches of fn(i)."""
+def timed_batch(torch, fn, n: int, launches_per_call: int = 1) -> float:
+    """Mean GPU time per call (us) of n back-to-back calls of fn(i), each
+    enqueueing launches_per_call kernels."""
     stream = torch.cuda.current_stream()
-    fill_us = 40.0 * n
+    fill_us = 40.0 * n * launches_per_call
     for _ in range(5):
         torch.cuda.synchronize()
         torch.cuda._sleep(int(fill_us * 2000))  # ~2 GHz shader clock
@@ -297,6 +316,64 @@ def timed_batch(torch, fn, n: int) -> float:
             return 1e3 * a.elapsed_time(b) / n
         fill_us *= 3
     return 1e3 * a.elapsed_time(b) / n
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(Bh, x_np, Xh, gemv_nbytes: int, seconds: float) -> dict:
+    """The oracle as it stands, timed on this host's cores: the Q4_0 GEMV at
+    4096 x 11008 with all OpenMP threads (median of 3 timed samples of about
+    seconds/4 each) and with one thread (median of 3 single products), and
+    the Q4_0 GEMM on a 256-row x 512-token sample of the prefill workload
+    (median of 3)."""
+    import oracle
+    all_threads = oracle.num_threads()
+
+    def rate_gemv(budget):
+        reps, t = 0, 0.0
+        t1 = time.perf_counter()
+        while t < budget or reps == 0:
+            oracle.gemv(0, Bh, x_np, M, K)
+            reps += 1
+            t = time.perf_counter() - t1
+        return gemv_nbytes * reps / t / 1e9, reps, t
+
+    oracle.gemv(0, Bh, x_np, M, K)  # warm up
+    samples = [rate_gemv(seconds / 4) for _ in range(3)]
+    med = sorted(samples)[1]
+    rows = 256
+    gops = []
+    for _ in range(3):
+        t1 = time.perf_counter()
+        oracle.gemm(0, Bh[:rows], Xh, rows, K, N)
+        gops.append(2.0 * rows * N * K / (time.perf_counter() - t1) / 1e9)
+    one = []
+    try:
+        oracle.set_threads(1)
+        for _ in range(3):
+            t1 = time.perf_counter()
+            oracle.gemv(0, Bh, x_np, M, K)
+            one.append(gemv_nbytes / (time.perf_counter() - t1) / 1e9)
+    finally:
+        oracle.set_threads(all_threads)
+    return {"value": round(med[0], 3), "unit": "GB/s", "cores": all_threads, "kind": "oracle",
+            "sample": f"median of 3 samples, each {med[1]} full Q4_0 GEMVs 4096x11008 "
+                      f"(dequantize to fp64, fp64 dot, OpenMP over rows, {all_threads} "
+                      f"threads) in {med[2]:.1f} s; same algorithmic bytes as value",
+            "one_thread_GBs": round(sorted(one)[1], 3),
+            "gemm_q4_0_GOPs": round(sorted(gops)[1], 3),
+            "gemm_sample": f"Q4_0 GEMM {rows} rows x {N} tokens x {K}, {all_threads} threads, "
+                           "median of 3",
+            "nproc": os.cpu_count(), "cpu_model": cpu_model()}
 
 
 def main():
@@ -333,7 +410,7 @@ def main():
 
     need = lambda prefix: any(o.startswith(prefix) for o in only)
     cold = {f: copies(packed[f], COLD_BYTES) if need("gemv_" + f) or need("decode_" + f)
-            else [packed[f]] for f in fmts}
+            or need("gemm_" + f) else [packed[f]] for f in fmts}
     W_rot = [Wf] + ([Wf.clone()] if need("quantize_q") else [])
     X_rot = [torch.from_numpy(X_np).to(dev) for _ in range(12 if need("quantize_act") else 1)]
     q_out = {f: torch.empty_like(packed[f]) for f in fmts}
@@ -344,6 +421,39 @@ def main():
     Y_dec = {n: torch.empty((n, M), dtype=torch.float32, device=dev) for n in DECODE_NS}
     src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
+    # the other decode workloads, packed on the GPU, each rotated over copies
+    # that together exceed the Infinity Cache
+    gx = {}
+    for name, fi, wl in GEMV_EXTRA:
+        if name not in only:
+            continue
+        if wl == "gemv_1024":
+            Wn, xn = inputs.gemv_1024()
+        elif wl.startswith("llama7b_"):
+            Wn, xn = inputs.llama7b_layer(int(wl[-1]))
+        else:
+            Wn, xn = inputs.q4k_rows(int(wl[-1]))
+        pk = binding.quantize(fi, torch.from_numpy(Wn).to(dev))
+        gx[name] = (fi, copies(pk, COLD_BYTES), torch.from_numpy(xn).to(dev),
+                    torch.empty(Wn.shape[0], dtype=torch.float32, device=dev), Wn.shape)
+        del pk
+    # the Qwen3-0.6B-like decode set: every matrix packed on the GPU; a pass
+    # is 196 GEMV launches, and passes rotate over copies of the whole set
+    qwen = {}
+    for name in QWEN3_OPS:
+        if name not in only:
+            continue
+        fi = fmts[name[len("qwen3_pass_"):]]
+        mats = []
+        for i in range(len(inputs.qwen3_shapes())):
+            _, Wn, xn = inputs.qwen3_matrix(i)
+            pk = binding.quantize(fi, torch.from_numpy(Wn).to(dev))
+            mats.append((pk, torch.from_numpy(xn).to(dev), Wn.shape))
+        set_bytes = sum(m[0].numel() for m in mats)
+        sets = [mats] + [[(m[0].clone(), m[1], m[2]) for m in mats]
+                         for _ in range(max(1, math.ceil(COLD_BYTES / set_bytes)) - 1)]
+        yq = torch.empty(max(m[2][0] for m in mats), dtype=torch.float32, device=dev)
+        qwen[name] = (fi, sets, yq)
     torch.cuda.synchronize()
 
     rb = {f: binding.row_bytes(i, K) for f, i in fmts.items()}
@@ -360,11 +470,23 @@ def main():
         table[f"gemv_{f}"] = lambda s, f=f, i=i: binding.gemv(
             i, cold[f][s % len(cold[f])], x, M, K, out=y[f])
     table["quantize_act_q8_0"] = lambda s: binding.quantize(1, X_rot[s % len(X_rot)], out=Xq)
-    table["gemm_q4_0"] = lambda s: binding.gemm(0, packed["q4_0"], Xq, M, K, N, out=Y)
+    # W from HBM at every launch, as in a prefill that streams each layer once
+    table["gemm_q4_0"] = lambda s: binding.gemm(0, cold["q4_0"][s % len(cold["q4_0"])], Xq,
+                                                M, K, N, out=Y)
+    for name, (fi, cps, xv, yv, shp) in gx.items():
+        table[name] = lambda s, fi=fi, cps=cps, xv=xv, yv=yv, shp=shp: binding.gemv(
+            fi, cps[s % len(cps)], xv, shp[0], shp[1], out=yv)
+
+    def qwen_pass(s, fi, sets, yq):
+        for pk, xv, (rows, kk) in sets[s % len(sets)]:
+            binding.gemv(fi, pk, xv, rows, kk, out=yq[:rows])
+    for name, (fi, sets, yq) in qwen.items():
+        table[name] = lambda s, fi=fi, sets=sets, yq=yq: qwen_pass(s, fi, sets, yq)
     # the other formats write elsewhere: the Q4_0 parity check below reads Y
     Yx = torch.empty_like(Y) if any(need(f"gemm_{f}") for f in ("q8_0", "q4_k", "q6_k")) else Y
     for f, i in (("q8_0", 1), ("q4_k", 2), ("q6_k", 3)):
-        table[f"gemm_{f}"] = lambda s, f=f, i=i: binding.gemm(i, packed[f], Xq, M, K, N, out=Yx)
+        table[f"gemm_{f}"] = lambda s, f=f, i=i: binding.gemm(
+            i, cold[f][s % len(cold[f])], Xq, M, K, N, out=Yx)
     kv_rows = X_rot[0][:KV_N, :KV_DIM].contiguous()
     kv_bias = X_rot[0][0, KV_DIM:2 * KV_DIM].contiguous()
     kv_cache = {f: torch.empty((KV_CELLS, binding.row_bytes(i, KV_DIM)), dtype=torch.uint8,
@@ -396,11 +518,27 @@ def main():
 
     # ------------------------------------------------------------ kernels
     nb = args.batch if args.batch > 0 else max(args.steps, 50)
-    mean_us = {name: timed_batch(torch, fn, nb) for name, fn in ops + extra if name != "copy"}
+    nq = len(inputs.qwen3_shapes())
+    mean_us = {name: (timed_batch(torch, fn, max(4, nb // 10), nq) if name in QWEN3_OPS
+                      else timed_batch(torch, fn, nb))
+               for name, fn in ops + extra if name != "copy"}
 
     kernels = {}
     for name, us in mean_us.items():
-        if name.startswith("gemv_"):
+        if name in gx:
+            fi, cps, _, _, (rows, kk) = gx[name]
+            nbytes = cps[0].numel() + 4 * kk + 4 * rows
+            gbs = nbytes / us / 1e3
+            kernels[name] = {"us": us, "bytes": nbytes, "GB/s": gbs, "bound": "hbm",
+                             "frac": gbs / HBM_PEAK_GBS}
+        elif name in qwen:
+            mats = qwen[name][1][0]
+            nbytes = sum(m[0].numel() + 4 * m[2][1] + 4 * m[2][0] for m in mats)
+            gbs = nbytes / us / 1e3
+            kernels[name] = {"us": us, "launches": len(mats), "bytes": nbytes, "GB/s": gbs,
+                             "bound": "hbm", "frac": gbs / HBM_PEAK_GBS,
+                             "us_per_launch": us / len(mats)}
+        elif name.startswith("gemv_"):
             f = name[5:]
             gbs = gemv_bytes[f] / us / 1e3
             kernels[name] = {"us": us, "bytes": gemv_bytes[f], "GB/s": gbs, "bound": "hbm",
@@ -440,6 +578,7 @@ def main():
             rng = np.random.default_rng(1)
             rows = np.sort(rng.choice(M, 32, replace=False))
             toks = np.sort(rng.choice(N, 16, replace=False))
+            # the last launch read copy (launches - 1) of W; all copies are equal
             Bh = packed["q4_0"].cpu().numpy()
             Xh = Xq.cpu().numpy()
             refY = oracle.gemm(0, Bh[rows], Xh[toks], len(rows), K, len(toks))
@@ -448,18 +587,8 @@ def main():
     # ------------------------------------------------------------ CPU oracle
     cpu = None
     if not args.no_cpu_baseline and "gemv_q4_0" in mean_us:
-        import oracle
-        Bh = packed["q4_0"].cpu().numpy()
-        reps, t_cpu = 0, 0.0
-        t1 = time.perf_counter()
-        while t_cpu < args.cpu_seconds:
-            oracle.gemv(0, Bh, x_np, M, K)
-            reps += 1
-            t_cpu = time.perf_counter() - t1
-        cpu = {"value": round(gemv_bytes["q4_0"] * reps / t_cpu / 1e9, 3), "unit": "GB/s",
-               "cores": oracle.num_threads(), "kind": "oracle",
-               "sample": f"{reps} full Q4_0 GEMVs 4096x11008 (dequantize to fp64, fp64 dot, "
-                         f"OpenMP over rows) in {t_cpu:.1f} s; same algorithmic bytes as value"}
+        cpu = cpu_baseline(packed["q4_0"].cpu().numpy(), x_np, Xq.cpu().numpy(),
+                           gemv_bytes["q4_0"], args.cpu_seconds)
 
     peaks = None if args.no_peaks else measured_peaks(torch, gemv_bytes.get("q4_0"))
     headline = kernels.get("gemv_q4_0")
