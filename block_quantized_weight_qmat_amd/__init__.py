@@ -1,4 +1,5 @@
-"""Block-quantized weight matmul (Q4_0, Q8_0, Q4_K-style) for MI355X.
+"""Block-quantized weight matmul (Q4_0, Q8_0, Q4_K-style, Q6_K-style) for
+MI355X.
 
 The compute lives in the HIP library ``libqmat.so`` (C ABI in
 ``include/qmat.h``); ``binding`` marshals torch device tensors into it.
@@ -6,10 +7,11 @@ The compute lives in the HIP library ``libqmat.so`` (C ABI in
 """
 from __future__ import annotations
 
-__all__ = ["quantize", "gemv", "gemm", "block_elems", "block_bytes", "row_bytes",
-           "Q4_0", "Q8_0", "Q4_K", "QmatError", "library_path"]
+__all__ = ["quantize", "gemv", "gemm", "prefill", "prefill_noalloc", "kv_write",
+           "block_elems", "block_bytes", "row_bytes", "noalloc_scratch_bytes",
+           "Q4_0", "Q8_0", "Q4_K", "Q6_K", "FORMATS", "QmatError", "library_path"]
 
-Q4_0, Q8_0, Q4_K = 0, 1, 2
+Q4_0, Q8_0, Q4_K, Q6_K = 0, 1, 2, 3
 
 
 def __getattr__(name):

@@ -120,9 +120,9 @@ int64_t qmat_block_bytes(int fmt) {
 
 int64_t qmat_row_bytes(int fmt, int64_t K) {
   if (!fmt_ok(fmt) || K < 0) return -1;
-  const int64_t be = qmat_block_elems(fmt);
-  if (K % be != 0) return -1;
-  return K / be * qmat_block_bytes(fmt);
+  const int64_t be = qmat_block_elems(fmt), bb = qmat_block_bytes(fmt);
+  if (K % be != 0 || K / be > INT64_MAX / bb) return -1;
+  return K / be * bb;
 }
 
 const char* qmat_strerror(int status) {

@@ -134,7 +134,7 @@ int64_t qmat_block_elems(int fmt);
 int64_t qmat_block_bytes(int fmt);
 
 /* Bytes of one packed row of K elements; -1 for an unknown fmt, a negative
- * K or a K that is not a multiple of the block. */
+ * K, a K that is not a multiple of the block, or a byte count beyond int64. */
 int64_t qmat_row_bytes(int fmt, int64_t K);
 
 /* Static English text for a status code (never NULL). */

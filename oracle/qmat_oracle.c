@@ -363,7 +363,8 @@ int oracle_quantize(int fmt, const float *W, uint8_t *out, int64_t rows,
 int oracle_kv_write(int fmt, const float *rows, const float *bias, uint8_t *cache,
                     int64_t cell0, int64_t n, int64_t cells, int64_t dim) {
   if (fmt != ORC_Q4_0 && fmt != ORC_Q8_0) return -1;
-  if (dim < 0 || dim % 32 != 0 || n < 0 || cell0 < 0 || cell0 + n > cells) return -1;
+  if (dim < 0 || dim % 32 != 0 || n < 0 || cell0 < 0 || n > cells || cell0 > cells - n)
+    return -1;
   int64_t nb = dim / 32, bb = oracle_block_bytes(fmt);
   float x[32];
   for (int64_t i = 0; i < n; ++i) {

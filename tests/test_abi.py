@@ -197,3 +197,23 @@ def test_prefill_noalloc_arguments(lib):
     assert f(0, None, None, None, 0, K, n_over, None) == OK   # M == 0: nothing to do
     assert f(0, A, None, A, 4, K, 2, None) == E_NULL
     assert f(0, A, A + 4, A, 4, K, 2, None) == E_ALIGN
+
+
+def test_documented_departures_from_the_planned_header(lib):
+    """The boundary's documented departures, each as documented: an int
+    format (out-of-range values are ordinary arguments), signed size helpers
+    that report errors, the 16-byte alignment rule, the GEMM's K limit, and
+    Python calls that take the shape."""
+    import inspect
+    assert lib.qmat_block_elems(2 ** 31 - 1) == 0 and lib.qmat_row_bytes(-7, 32) == -1
+    assert lib.qmat_gemv(2 ** 31 - 1, A, A, A, 1, 32, None) == E_FMT
+    assert lib.qmat_row_bytes(0, 31) == -1 and lib.qmat_row_bytes(0, 2 ** 40) == 2 ** 35 * 18
+    for off in (1, 2, 4, 8):
+        assert lib.qmat_gemv(0, A, A, A + off, 1, 32, None) == E_ALIGN
+    assert lib.qmat_gemm(0, A, A, A, 1, 2 ** 24 + 32, 1, None) == E_SHAPE
+    assert lib.qmat_prefill(0, A, A, A, A, 1, 2 ** 24 + 32, 1, None) == E_SHAPE
+    assert list(inspect.signature(binding.gemv).parameters)[:5] == ["fmt", "blocks", "x", "M", "K"]
+    assert list(inspect.signature(binding.gemm).parameters)[:6] == ["fmt", "blocks", "Xq", "M", "K", "N"]
+    import block_quantized_weight_qmat_amd as pkg
+    for name in pkg.__all__:
+        assert getattr(pkg, name) is not None, name

@@ -1,5 +1,5 @@
-"""A second, independent implementation of the Q4_0, Q8_0 and Q6_K-style
-quantizers in vectorised numpy, written from the rules in include/qmat.h,
+"""A second, independent implementation of the Q4_0, Q8_0, Q4_K-style and
+Q6_K-style quantizers in vectorised numpy, written from the rules in include/qmat.h,
 that must agree byte for byte with the oracle. It shares the oracle's
 reading of the pages (so it is a cross-check of the C code's indexing,
 rounding and packing, not a pin of the reading); the pins are in
@@ -96,6 +96,47 @@ def np_quant_q6k(W):
     return out.reshape(rows, -1)
 
 
+def np_quant_q4k(W):
+    """Q4_K-style, from the rule and layout stated for qmat_quantize: per
+    32-element sub-block j, lo = min(0, min w), hi = max w, scale = (hi - lo)
+    / 15, off = -lo (fp32); per 256, d = max scale / 63 and dmin = max off /
+    63, stored as fp16; sc = clamp(round(scale / D), 0, 63), mn =
+    clamp(round(off / Dmin), 0, 63) (0 when the stored value is 0); codes q =
+    clamp(round((w + Dmin mn) / (D sc)), 0, 15) (0 when D sc = 0). Bytes: d,
+    dmin, the 16 six-bit fields (sc_0..7 then mn_0..7) as a 96-bit
+    little-endian integer, then 16 code bytes per sub-block in Q4_0 nibble
+    order."""
+    rows, K = W.shape
+    x = W.reshape(rows, K // 256, 8, 32).astype(np.float32)
+    mn = np.min(x, axis=3)
+    lo = np.where(mn < 0, mn, np.float32(0)).astype(np.float32)
+    hi = np.max(x, axis=3)
+    scale = ((hi - lo).astype(np.float32) / np.float32(15)).astype(np.float32)
+    off = (-lo).astype(np.float32)
+    d = (np.maximum(np.max(scale, axis=2), 0) / np.float32(63)).astype(np.float32)
+    dm = (np.maximum(np.max(off, axis=2), 0) / np.float32(63)).astype(np.float32)
+    hd, hm = f16_bits(d), f16_bits(dm)
+    D, Dm = f16_value(hd)[..., None], f16_value(hm)[..., None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        sc = np.where(D == 0, 0, np.clip(round_away((scale / D).astype(np.float32)), 0, 63))
+        mq = np.where(Dm == 0, 0, np.clip(round_away((off / Dm).astype(np.float32)), 0, 63))
+    sc, mq = sc.astype(np.int64), mq.astype(np.int64)
+    S = (D * sc.astype(np.float32)).astype(np.float32)[..., None]
+    O = (Dm * mq.astype(np.float32)).astype(np.float32)[..., None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = round_away(((x + O).astype(np.float32) / S).astype(np.float32))
+    q = np.where(S == 0, 0, np.clip(q, 0, 15)).astype(np.uint8)
+    out = np.zeros((rows, K // 256, 144), np.uint8)
+    out[..., 0], out[..., 1] = hd & 0xFF, hd >> 8
+    out[..., 2], out[..., 3] = hm & 0xFF, hm >> 8
+    fields = np.concatenate([sc, mq], axis=2)                       # [.., 16]
+    bits = (fields[..., :, None] >> np.arange(6)) & 1               # [.., 16, 6]
+    out[..., 4:16] = np.packbits(bits.reshape(rows, K // 256, 96).astype(np.uint8),
+                                 axis=-1, bitorder="little")
+    out[..., 16:] = (q[..., :16] | (q[..., 16:] << 4)).reshape(rows, K // 256, 128)
+    return out.reshape(rows, -1)
+
+
 def mixed(rng, rows, K):
     W = rng.normal(0, 0.02, (rows, K)).astype(np.float32)
     W[rows // 4] *= 1e-6                       # fp16-subnormal scales
@@ -121,3 +162,19 @@ def test_q6_k_agrees_with_oracle(seed):
     for rows, K in ((29, 256 * 5), (6, 4096)):
         W = mixed(rng, rows, K)
         assert np.array_equal(np_quant_q6k(W), oracle.quantize(3, W)), (rows, K)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_q4_k_agrees_with_oracle(seed):
+    rng = np.random.default_rng(3000 + seed)
+    for rows, K in ((29, 256 * 5), (6, 4096)):
+        W = mixed(rng, rows, K)
+        W[1] = np.abs(W[1])           # one-signed rows: lo = 0, no offset
+        W[2] = -np.abs(W[2]) - 0.01   # all negative: hi < 0
+        W[3, :256] = -0.0             # a superblock of negative zeros
+        assert np.array_equal(np_quant_q4k(W), oracle.quantize(2, W)), (rows, K)
+    # the C4 workload's rows with a per-row scale spread
+    from block_quantized_weight_qmat_amd import inputs
+    W, _ = inputs.q4k_rows(0)
+    W = W[:64]
+    assert np.array_equal(np_quant_q4k(W), oracle.quantize(2, W))
