@@ -8,8 +8,9 @@
 // Per K-block b (32 elements) and output (m, n):
 //   S[m,n,b] = sum_{i<32} wq[m,32b+i] * xq[n,32b+i]        (exact int32, MFMA)
 //   Y[n][m] += dw[m,b] * dx[n,b] * S[m,n,b]                 (fp32, VALU)
-// wq is the signed code (c - 8) for Q4_0, q for Q8_0, and the unsigned code q
-// for Q4_K-style, whose per-sub-block offset adds -O[m,b] * dx[n,b] * sum(xq).
+// wq is 16 (c - 8) for Q4_0 (its dw is stored divided by 16, exactly), q for
+// Q8_0, and the unsigned code q for Q4_K-style, whose per-sub-block offset
+// adds -O[m,b] * dx[n,b] * sum(xq).
 // Q6_K-style blocks (wq = c - 32) have a scale per 16-element half: each half
 // is its own MFMA (the other half's operand lanes zeroed) and scaled alone.
 //
@@ -104,13 +105,13 @@ struct Stage {
   }
 };
 
-// Nibbles of 4 code bytes -> 4 signed bytes (c - 8), for the low or high
-// nibble: per byte, c + 0x78 stays below 0x88 (no carry between bytes) and
-// flipping its top bit gives c - 8 as a signed byte.
-__device__ __forceinline__ uint32_t nib_signed(uint32_t w, int shift) {
-  const uint32_t c = (w >> shift) & 0x0F0F0F0Fu;
-  return (c + 0x78787878u) ^ 0x80808080u;
-}
+// Nibbles of 4 Q4_0 code bytes -> 4 signed bytes 16 (c - 8), given
+// x = codes ^ 0x88888888: a nibble c ^ 8 in the top half of a byte is, read
+// as a signed byte, 16 (c - 8). The high nibbles are x & 0xF0F0F0F0, the low
+// ones (x << 4) & 0xF0F0F0F0: two or one operations per word after the
+// shared XOR (the unscaled c - 8 takes four per nibble set).
+__device__ __forceinline__ uint32_t nib16_hi(uint32_t x) { return x & 0xF0F0F0F0u; }
+__device__ __forceinline__ uint32_t nib16_lo(uint32_t x) { return (x << 4) & 0xF0F0F0F0u; }
 
 __device__ __forceinline__ uint32_t nib_unsigned(uint32_t w, int shift) {
   return (w >> shift) & 0x0F0F0F0Fu;
@@ -408,11 +409,11 @@ struct TileLoader {
         if (FMT == kFmtQ4_0) {
           uint32_t h, c[8];
           realign_lane(wl[it], 18, r.wa[it], r.wb[it], r.ws[it], h, c);
-          store16(dst.w(bb, 0, rr), nib_signed(c[0], 0), nib_signed(c[1], 0),
-                  nib_signed(c[2], 0), nib_signed(c[3], 0));
-          store16(dst.w(bb, 1, rr), nib_signed(c[0], 4), nib_signed(c[1], 4),
-                  nib_signed(c[2], 4), nib_signed(c[3], 4));
-          dst.wd[bb][rr] = f16_bits_to_f32(h);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) c[k] ^= 0x88888888u;
+          store16(dst.w(bb, 0, rr), nib16_lo(c[0]), nib16_lo(c[1]), nib16_lo(c[2]), nib16_lo(c[3]));
+          store16(dst.w(bb, 1, rr), nib16_hi(c[0]), nib16_hi(c[1]), nib16_hi(c[2]), nib16_hi(c[3]));
+          dst.wd[bb][rr] = f16_bits_to_f32(h) * 0.0625f;  // the codes carry a factor 16
         } else if (FMT == kFmtQ8_0) {
           uint32_t h, c[8];
           realign_lane(wl[it], 34, r.wa[it], r.wb[it], r.ws[it], h, c);

@@ -30,4 +30,5 @@ hipError_t launch_gemm_small(int fmt, const void* blocks, const void* Xq8, float
 hipError_t launch_gemm(int fmt, const void* blocks, const void* Xq8, float* Y, int64_t M,
                        int64_t K, int64_t N, hipStream_t stream);
 
+
 }  // namespace qmat
