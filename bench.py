@@ -27,8 +27,9 @@ Timing, two passes:
 
 Beside the step, every other workload of the measurement plan is timed per
 kernel (``kernels``): the 1024x1024 Q4_0 GEMV (latency); the 196-matrix
-Qwen3-0.6B-like decode set as one pass of 196 GEMV launches, Q4_0 and Q8_0,
-rotating over copies of the whole set; the 11008x4096 orientation of the 7B
+Qwen3-0.6B-like decode set, Q4_0 and Q8_0, as one pass: one qmat_gemv_batch
+call (a few launches), and beside it the same 196 products as 196 qmat_gemv
+launches, each rotating over copies of the whole set; the 11008x4096 orientation of the 7B
 layer (the strip kernel); the Q4_K-style GEMV at 4096x4096 and 4096x11008
 with per-row scale spread; the decode batch, the Q6_K-style kernels, the
 other GEMM formats and the KV-cache write. The prefill GEMM reads a different
@@ -83,7 +84,8 @@ GEMV_EXTRA = [("gemv_q4_0_1024x1024", 0, "gemv_1024"),
               ("gemv_q4_0_11008x4096", 0, "llama7b_1"), ("gemv_q8_0_11008x4096", 1, "llama7b_1"),
               ("gemv_q4_k_4096x4096_spread", 2, "q4k_0"),
               ("gemv_q4_k_4096x11008_spread", 2, "q4k_1")]
-QWEN3_OPS = ["qwen3_pass_q4_0", "qwen3_pass_q8_0"]
+# the Qwen3-like set as one qmat_gemv_batch call, and as 196 qmat_gemv calls
+QWEN3_OPS = ["qwen3_pass_q4_0", "qwen3_pass_q8_0", "qwen3_launches_q4_0", "qwen3_launches_q8_0"]
 EXTRA_OPS = ([f"decode_q4_0_n{n}" for n in DECODE_NS] + [g[0] for g in GEMV_EXTRA] + QWEN3_OPS
              + ["quantize_q6_k", "gemv_q6_k", "gemm_q8_0", "gemm_q4_k", "gemm_q6_k",
                 "kv_write_q4_0", "kv_write_q8_0"])
@@ -438,12 +440,13 @@ def main():
                     torch.empty(Wn.shape[0], dtype=torch.float32, device=dev), Wn.shape)
         del pk
     # the Qwen3-0.6B-like decode set: every matrix packed on the GPU; a pass
-    # is 196 GEMV launches, and passes rotate over copies of the whole set
+    # is one batch call (or 196 GEMV launches), and passes rotate over copies
+    # of the whole set
     qwen = {}
     for name in QWEN3_OPS:
         if name not in only:
             continue
-        fi = fmts[name[len("qwen3_pass_"):]]
+        fi = fmts[name.split("_", 2)[2]]
         mats = []
         for i in range(len(inputs.qwen3_shapes())):
             _, Wn, xn = inputs.qwen3_matrix(i)
@@ -453,7 +456,11 @@ def main():
         sets = [mats] + [[(m[0].clone(), m[1], m[2]) for m in mats]
                          for _ in range(max(1, math.ceil(COLD_BYTES / set_bytes)) - 1)]
         yq = torch.empty(max(m[2][0] for m in mats), dtype=torch.float32, device=dev)
-        qwen[name] = (fi, sets, yq)
+        # the batch writes every product at once: one output per matrix
+        ys = [torch.empty(m[2][0], dtype=torch.float32, device=dev) for m in mats]
+        jobs = [binding.gemv_jobs(fi, [(pk, xv, yv, shp[0], shp[1])
+                                       for (pk, xv, shp), yv in zip(st, ys)]) for st in sets]
+        qwen[name] = (fi, sets, yq, ys, jobs)
     torch.cuda.synchronize()
 
     rb = {f: binding.row_bytes(i, K) for f, i in fmts.items()}
@@ -477,11 +484,14 @@ def main():
         table[name] = lambda s, fi=fi, cps=cps, xv=xv, yv=yv, shp=shp: binding.gemv(
             fi, cps[s % len(cps)], xv, shp[0], shp[1], out=yv)
 
-    def qwen_pass(s, fi, sets, yq):
+    def qwen_launches(s, fi, sets, yq):
         for pk, xv, (rows, kk) in sets[s % len(sets)]:
             binding.gemv(fi, pk, xv, rows, kk, out=yq[:rows])
-    for name, (fi, sets, yq) in qwen.items():
-        table[name] = lambda s, fi=fi, sets=sets, yq=yq: qwen_pass(s, fi, sets, yq)
+    for name, (fi, sets, yq, _, jobs) in qwen.items():
+        if name.startswith("qwen3_launches"):
+            table[name] = lambda s, fi=fi, sets=sets, yq=yq: qwen_launches(s, fi, sets, yq)
+        else:
+            table[name] = lambda s, fi=fi, jobs=jobs: binding.gemv_batch(fi, jobs[s % len(jobs)])
     # the other formats write elsewhere: the Q4_0 parity check below reads Y
     Yx = torch.empty_like(Y) if any(need(f"gemm_{f}") for f in ("q8_0", "q4_k", "q6_k")) else Y
     for f, i in (("q8_0", 1), ("q4_k", 2), ("q6_k", 3)):
@@ -519,8 +529,9 @@ def main():
     # ------------------------------------------------------------ kernels
     nb = args.batch if args.batch > 0 else max(args.steps, 50)
     nq = len(inputs.qwen3_shapes())
-    mean_us = {name: (timed_batch(torch, fn, max(4, nb // 10), nq) if name in QWEN3_OPS
-                      else timed_batch(torch, fn, nb))
+    mean_us = {name: (timed_batch(torch, fn, max(4, nb // 10),
+                                  nq if name.startswith("qwen3_launches") else 8)
+                      if name in QWEN3_OPS else timed_batch(torch, fn, nb))
                for name, fn in ops + extra if name != "copy"}
 
     kernels = {}
@@ -535,9 +546,9 @@ def main():
             mats = qwen[name][1][0]
             nbytes = sum(m[0].numel() + 4 * m[2][1] + 4 * m[2][0] for m in mats)
             gbs = nbytes / us / 1e3
-            kernels[name] = {"us": us, "launches": len(mats), "bytes": nbytes, "GB/s": gbs,
+            kernels[name] = {"us": us, "matrices": len(mats), "bytes": nbytes, "GB/s": gbs,
                              "bound": "hbm", "frac": gbs / HBM_PEAK_GBS,
-                             "us_per_launch": us / len(mats)}
+                             "calls": len(mats) if name.startswith("qwen3_launches") else 1}
         elif name.startswith("gemv_"):
             f = name[5:]
             gbs = gemv_bytes[f] / us / 1e3

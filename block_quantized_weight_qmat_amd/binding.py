@@ -61,6 +61,8 @@ def load_library():
     lib.qmat_prefill.restype = i32
     lib.qmat_kv_write.argtypes = [i32, p, p, p, i64, i64, i64, i64, p]
     lib.qmat_kv_write.restype = i32
+    lib.qmat_gemv_batch.argtypes = [i32, p, i64, p]
+    lib.qmat_gemv_batch.restype = i32
     lib.qmat_prefill_noalloc.argtypes = [i32, p, p, p, i64, i64, i64, p]
     lib.qmat_prefill_noalloc.restype = i32
     lib.qmat_noalloc_scratch_bytes.argtypes = []
@@ -144,6 +146,38 @@ def gemv(fmt, blocks: torch.Tensor, x: torch.Tensor, M: int, K: int,
     _check("qmat_gemv", load_library().qmat_gemv(
         f, blocks.data_ptr(), x.data_ptr(), out.data_ptr(), M, K, _stream(x)))
     return out
+
+
+class GemvJob(ctypes.Structure):
+    """One job of gemv_batch (the C struct qmat_gemv_job)."""
+    _fields_ = [("blocks", ctypes.c_void_p), ("x", ctypes.c_void_p), ("y", ctypes.c_void_p),
+                ("M", ctypes.c_int64), ("K", ctypes.c_int64)]
+
+
+def gemv_jobs(fmt, items) -> ctypes.Array:
+    """A job array for gemv_batch from (blocks, x, y, M, K) tuples of GPU
+    tensors; it keeps raw pointers, so the tensors must outlive its use."""
+    f = _fmt(fmt)
+    arr = (GemvJob * len(items))()
+    for i, (blocks, x, y, M, K) in enumerate(items):
+        _gpu(blocks, "blocks", torch.uint8)
+        _gpu(x, "x", torch.float32)
+        _gpu(y, "y", torch.float32)
+        if blocks.numel() != M * row_bytes(f, K) or x.numel() != K or y.numel() != M:
+            raise ValueError(f"job {i}: blocks, x or y does not match M, K")
+        arr[i] = GemvJob(blocks.data_ptr(), x.data_ptr(), y.data_ptr(), M, K)
+    return arr
+
+
+def gemv_batch(fmt, jobs, stream_of: torch.Tensor | None = None):
+    """Run many GEMVs (a gemv_jobs array, or (blocks, x, y, M, K) tuples) in
+    as few launches as possible, on torch's current stream."""
+    f = _fmt(fmt)
+    arr = jobs if isinstance(jobs, ctypes.Array) else gemv_jobs(f, jobs)
+    dev = stream_of.device if stream_of is not None else torch.device("cuda")
+    st = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    _check("qmat_gemv_batch", load_library().qmat_gemv_batch(
+        f, ctypes.cast(arr, ctypes.c_void_p), len(arr), st))
 
 
 def gemm(fmt, blocks: torch.Tensor, Xq: torch.Tensor, M: int, K: int, N: int,

@@ -632,22 +632,36 @@ __device__ __forceinline__ void x_from_lds(const uint8_t* strip, int lane, f32x4
 // (K/32 odd for Q4_0/Q8_0), so even and odd rows have different block
 // alignments; row m0 + r has parity r & 1 since m0 and the group size are
 // even.
-template <class F, int R, int G, int D, bool kOdd>
-__global__ __launch_bounds__(kMaxStrips * kWave) void gemv_kernel(const uint8_t* __restrict__ B,
-                                                                  const float* __restrict__ x,
-                                                                  float* __restrict__ y,
-                                                                  int64_t M, int K) {
+// kPair (rows of at most 32 slices, one strip): each half of the wave takes
+// its own G x R rows, lane l working on slice l & 31, so that no lane idles;
+// the workgroup then owns 2 x G x R rows.
+// The body of the strip kernel for workgroup `wg` of one matrix (rows
+// wg * kRows ..); the workgroup's waves split K into strips. Waves past the
+// matrix's strips add nothing.
+template <int R, int G, bool kPair>
+constexpr int strip_rows() {
+  return kPair ? 2 * R * G : R * G;
+}
+
+template <class F, int R, int G, int D, bool kOdd, bool kPair>
+__device__ __forceinline__ void gemv_strips(const uint8_t* __restrict__ B,
+                                            const float* __restrict__ x, float* __restrict__ y,
+                                            int64_t M, int K, int64_t wg, uint8_t* xlds,
+                                            float (*red)[strip_rows<R, G, kPair>()]) {
   constexpr int RG = R * G;
-  static_assert(RG <= kWave && (RG & (RG - 1)) == 0, "rows per workgroup");
+  constexpr int kRows = strip_rows<R, G, kPair>();
+  static_assert(kRows <= kWave && (RG & (RG - 1)) == 0, "rows per workgroup");
   static_assert(D >= 1 && D <= G, "groups in flight");
-  extern __shared__ __attribute__((aligned(16))) uint8_t xlds[];
-  __shared__ float red[kMaxStrips][RG];
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
   const int nw = blockDim.x >> 6;
   const int ns = K >> 5;
   const int64_t rb = F::row_bytes(K);
-  const int64_t m0 = (int64_t)blockIdx.x * RG;
+  const int64_t m0 = wg * kRows;
+  // the slice lane and the first row of this lane's half (RG is even, so
+  // row parity is still r & 1)
+  const int sl = kPair ? (lane & 31) : lane;
+  const int64_t mh = kPair ? m0 + (lane >> 5) * RG : m0;
   uint8_t* strip = xlds + wv * kXStripBytes;
 
   float part[RG];
@@ -655,7 +669,7 @@ __global__ __launch_bounds__(kMaxStrips * kWave) void gemv_kernel(const uint8_t*
   for (int r = 0; r < RG; ++r) part[r] = 0.0f;
 
   for (int base = wv * kWave; base < ns; base += nw * kWave) {
-    const int j = base + lane;
+    const int j = base + sl;
     x_to_lds(x + (int64_t)base * 32, ns - base, strip, lane);
     if (j < ns) {
       BlockLane L[2];
@@ -667,7 +681,7 @@ __global__ __launch_bounds__(kMaxStrips * kWave) void gemv_kernel(const uint8_t*
         for (int r = 0; r < R; ++r) {
           // rows past M re-read the last row of the same parity (their
           // sums are discarded); with an odd stride M >= 2 here
-          int64_t m = m0 + g * R + r;
+          int64_t m = mh + g * R + r;
           if (m >= M) m = kOdd ? M - 1 - ((M - 1 - r) & 1) : M - 1;
           F::load(B + m * rb, L[kOdd ? (r & 1) : 0], dst[r]);
         }
@@ -685,7 +699,7 @@ __global__ __launch_bounds__(kMaxStrips * kWave) void gemv_kernel(const uint8_t*
       __builtin_amdgcn_s_waitcnt(vmcnt_imm<D * R * F::kLoads>());
       __builtin_amdgcn_sched_barrier(0);
       f32x4 xv[8];
-      x_from_lds(strip, lane, xv);
+      x_from_lds(strip, sl, xv);
       typename F::XP xp;
       F::prep(xv, xp);
       typename F::Acc ac = {};
@@ -703,16 +717,59 @@ __global__ __launch_bounds__(kMaxStrips * kWave) void gemv_kernel(const uint8_t*
     }
   }
 
-  constexpr int kShift = 6 - log2i<RG>();
-  const int row = (lane >> kShift) & (RG - 1);
-  const float sum = wave_reduce_rows<RG>(part, lane);
-  if ((lane & ((1 << kShift) - 1)) == 0) red[wv][row] = sum;
+  if constexpr (kPair) {
+    // each half reduces its own rows (exchanges within 32 lanes)
+    static_assert(RG <= 32, "rows per half");
+    constexpr int kShift = 5 - log2i<RG>();
+    reduce_level<16, RG / 2, RG>(part, lane);
+    const int row = (lane >> 5) * RG + ((lane >> kShift) & (RG - 1));
+    if ((lane & ((1 << kShift) - 1)) == 0) red[wv][row] = part[0];
+  } else {
+    constexpr int kShift = 6 - log2i<RG>();
+    const int row = (lane >> kShift) & (RG - 1);
+    const float sum = wave_reduce_rows<RG>(part, lane);
+    if ((lane & ((1 << kShift) - 1)) == 0) red[wv][row] = sum;
+  }
   __syncthreads();
-  if ((int)threadIdx.x < RG) {
+  if ((int)threadIdx.x < kRows) {
     float t = 0.0f;
     for (int w = 0; w < nw; ++w) t += red[w][threadIdx.x];
     if (m0 + threadIdx.x < M) y[m0 + threadIdx.x] = t;
   }
+}
+
+template <class F, int R, int G, int D, bool kOdd, bool kPair>
+__global__ __launch_bounds__(kMaxStrips * kWave) void gemv_kernel(const uint8_t* __restrict__ B,
+                                                                  const float* __restrict__ x,
+                                                                  float* __restrict__ y,
+                                                                  int64_t M, int K) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t xlds[];
+  __shared__ float red[kPair ? 1 : kMaxStrips][strip_rows<R, G, kPair>()];
+  gemv_strips<F, R, G, D, kOdd, kPair>(B, x, y, M, K, blockIdx.x, xlds, red);
+}
+
+// Many independent GEMVs in one launch: job blockIdx.y, its workgroup
+// blockIdx.x. Each job's pointers and sizes travel in the kernel arguments;
+// workgroups past a job's rows end at once. The jobs of one launch share the
+// row-stride parity, the pair mode and the number of strips.
+constexpr int kBatchJobs = 64;
+struct GemvBatchArgs {
+  const uint8_t* B[kBatchJobs];
+  const float* x[kBatchJobs];
+  float* y[kBatchJobs];
+  int64_t M[kBatchJobs];
+  int K[kBatchJobs];
+};
+
+template <class F, int R, int G, int D, bool kOdd, bool kPair>
+__global__ __launch_bounds__(kMaxStrips * kWave) void gemv_batch_kernel(GemvBatchArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t xlds[];
+  constexpr int kRows = strip_rows<R, G, kPair>();
+  __shared__ float red[kPair ? 1 : kMaxStrips][kRows];
+  const int j = blockIdx.y;
+  const int64_t M = a.M[j];
+  if ((int64_t)blockIdx.x * kRows >= M) return;  // the whole workgroup
+  gemv_strips<F, R, G, D, kOdd, kPair>(a.B[j], a.x[j], a.y[j], M, a.K[j], blockIdx.x, xlds, red);
 }
 
 // -------------------------------------------------- GEMV, a row per wave --
@@ -975,6 +1032,26 @@ __global__ __launch_bounds__(kRowWaves * kWave) void gemv_rows_kernel(
 #define QMAT_GEMV_ROWS_MIN_SLICES 256
 #endif
 
+// How the strip kernel covers a matrix: strips (waves) per workgroup, the
+// row-stride parity and the pair mode.
+struct StripShape {
+  int waves;
+  bool odd, pair;
+  constexpr int64_t rows(int rg) const { return pair ? 2 * rg : rg; }
+};
+
+template <class F>
+StripShape strip_shape(int64_t M, int64_t K) {
+  const int64_t ns = K / 32;
+  int waves = (int)((ns + kWave - 1) / kWave);
+  if (waves < 1) waves = 1;
+  if (waves > kMaxStrips) waves = kMaxStrips;
+  // a single row has only the even parity: the aligned variant covers it
+  const bool odd = (F::row_bytes(K) & 2) != 0 && M > 1;  // rows start 2 mod 4
+  // rows of at most half a strip: both halves of the wave take rows
+  return {waves, odd, ns <= kWave / 2 && M > 1};
+}
+
 template <class F, int R, int G, int D, int RD>
 hipError_t launch_fmt(const void* blocks, const float* x, float* y, int64_t M, int64_t K,
                       hipStream_t stream) {
@@ -994,22 +1071,116 @@ hipError_t launch_fmt(const void* blocks, const float* x, float* y, int64_t M, i
                          static_cast<const uint8_t*>(blocks), x, y, M, (int)K);
     return hipGetLastError();
   }
-  int waves = (int)((ns + kWave - 1) / kWave);
-  if (waves < 1) waves = 1;
-  if (waves > kMaxStrips) waves = kMaxStrips;
-  const int64_t grid = (M + R * G - 1) / (R * G);
-  const size_t lds = (size_t)waves * kXStripBytes;
-  // a single row has only the even parity: the aligned variant covers it
-  const bool odd = (F::row_bytes(K) & 2) != 0 && M > 1;  // rows start 2 mod 4
-  if (odd)
-    hipLaunchKernelGGL((gemv_kernel<F, R, G, D, true>), dim3((unsigned)grid),
-                       dim3(waves * kWave), lds, stream, static_cast<const uint8_t*>(blocks), x,
-                       y, M, (int)K);
+  const StripShape sh = strip_shape<F>(M, K);
+  const int64_t grid = (M + sh.rows(R * G) - 1) / sh.rows(R * G);
+  const dim3 block(sh.waves * kWave);
+  const size_t lds = (size_t)sh.waves * kXStripBytes;
+  const uint8_t* B = static_cast<const uint8_t*>(blocks);
+  if (sh.odd && sh.pair)
+    hipLaunchKernelGGL((gemv_kernel<F, R, G, D, true, true>), dim3((unsigned)grid), block, lds,
+                       stream, B, x, y, M, (int)K);
+  else if (sh.odd)
+    hipLaunchKernelGGL((gemv_kernel<F, R, G, D, true, false>), dim3((unsigned)grid), block, lds,
+                       stream, B, x, y, M, (int)K);
+  else if (sh.pair)
+    hipLaunchKernelGGL((gemv_kernel<F, R, G, D, false, true>), dim3((unsigned)grid), block, lds,
+                       stream, B, x, y, M, (int)K);
   else
-    hipLaunchKernelGGL((gemv_kernel<F, R, G, D, false>), dim3((unsigned)grid),
-                       dim3(waves * kWave), lds, stream, static_cast<const uint8_t*>(blocks), x,
-                       y, M, (int)K);
+    hipLaunchKernelGGL((gemv_kernel<F, R, G, D, false, false>), dim3((unsigned)grid), block, lds,
+                       stream, B, x, y, M, (int)K);
   return hipGetLastError();
+}
+
+// rows per group, groups per workgroup and groups in flight of the strip
+// kernel inside a batch launch
+#ifndef QMAT_BATCH_CFG
+#define QMAT_BATCH_R_Q4_0 QMAT_GEMV_R_Q4_0
+#define QMAT_BATCH_G_Q4_0 QMAT_GEMV_G_Q4_0
+#define QMAT_BATCH_D_Q4_0 QMAT_GEMV_D_Q4_0
+#define QMAT_BATCH_R_Q8_0 QMAT_GEMV_R_Q8_0
+#define QMAT_BATCH_G_Q8_0 QMAT_GEMV_G_Q8_0
+#define QMAT_BATCH_D_Q8_0 QMAT_GEMV_D_Q8_0
+#define QMAT_BATCH_R_Q4_K QMAT_GEMV_R_Q4_K
+#define QMAT_BATCH_G_Q4_K QMAT_GEMV_G_Q4_K
+#define QMAT_BATCH_D_Q4_K QMAT_GEMV_D_Q4_K
+#define QMAT_BATCH_R_Q6_K QMAT_GEMV_R_Q6_K
+#define QMAT_BATCH_G_Q6_K QMAT_GEMV_G_Q6_K
+#define QMAT_BATCH_D_Q6_K QMAT_GEMV_D_Q6_K
+#endif
+
+// A batch of GEMVs of one format: jobs whose rows take the row-per-wave
+// kernel are launched one by one; the others go through the strip kernel in
+// launches of up to kBatchJobs jobs, grouped by row-stride parity and by
+// strip shape (pair mode, or the number of strips), so that every workgroup
+// is sized for its own job.
+template <class F, int R, int G, int D, int RD>
+hipError_t launch_batch_fmt(const GemvJob* jobs, int64_t count, hipStream_t stream) {
+  constexpr int RG = R * G;
+  constexpr int kShapes = kMaxStrips + 1;  // 0: pair mode, w: w strips
+  struct Group {
+    GemvBatchArgs a;
+    int n;
+    int64_t tiles;
+  };
+  static_assert(sizeof(Group) < 4096, "batch group");
+  Group grp[2][kShapes];
+  for (auto& go : grp)
+    for (auto& g : go) g.n = 0, g.tiles = 0;
+  auto flush = [&](int o, int w) -> hipError_t {
+    Group& g = grp[o][w];
+    if (g.n == 0) return hipSuccess;
+    const dim3 grid((unsigned)g.tiles, (unsigned)g.n);
+    const int waves = w == 0 ? 1 : w;
+    const dim3 block(waves * kWave);
+    const size_t lds = (size_t)waves * kXStripBytes;
+    if (o && w == 0)
+      hipLaunchKernelGGL((gemv_batch_kernel<F, R, G, D, true, true>), grid, block, lds, stream,
+                         g.a);
+    else if (o)
+      hipLaunchKernelGGL((gemv_batch_kernel<F, R, G, D, true, false>), grid, block, lds, stream,
+                         g.a);
+    else if (w == 0)
+      hipLaunchKernelGGL((gemv_batch_kernel<F, R, G, D, false, true>), grid, block, lds, stream,
+                         g.a);
+    else
+      hipLaunchKernelGGL((gemv_batch_kernel<F, R, G, D, false, false>), grid, block, lds, stream,
+                         g.a);
+    g.n = 0;
+    g.tiles = 0;
+    return hipGetLastError();
+  };
+  for (int64_t i = 0; i < count; ++i) {
+    const GemvJob& jb = jobs[i];
+    if (jb.M == 0) continue;
+    const int64_t ns = jb.K / 32;
+    if (QMAT_GEMV_ROWS && ns >= QMAT_GEMV_ROWS_MIN_SLICES && ns <= kRowMaxSlices) {
+      const hipError_t e = launch_fmt<F, R, G, D, RD>(jb.blocks, jb.x, jb.y, jb.M, jb.K, stream);
+      if (e != hipSuccess) return e;
+      continue;
+    }
+    const StripShape sh = strip_shape<F>(jb.M, jb.K);
+    const int o = sh.odd ? 1 : 0;
+    const int w = sh.pair ? 0 : sh.waves;
+    Group& g = grp[o][w];
+    const int k = g.n++;
+    g.a.B[k] = static_cast<const uint8_t*>(jb.blocks);
+    g.a.x[k] = jb.x;
+    g.a.y[k] = jb.y;
+    g.a.M[k] = jb.M;
+    g.a.K[k] = (int)jb.K;
+    const int64_t t = (jb.M + sh.rows(RG) - 1) / sh.rows(RG);
+    g.tiles = t > g.tiles ? t : g.tiles;
+    if (g.n == kBatchJobs) {
+      const hipError_t e = flush(o, w);
+      if (e != hipSuccess) return e;
+    }
+  }
+  for (int o = 0; o < 2; ++o)
+    for (int w = 0; w < kShapes; ++w) {
+      const hipError_t e = flush(o, w);
+      if (e != hipSuccess) return e;
+    }
+  return hipSuccess;
 }
 
 // ------------------------------------------------ small-N decode GEMM --
@@ -1335,6 +1506,23 @@ hipError_t launch_small_chunk(const void* blocks, const void* Xq8, float* Y, int
 }
 
 }  // namespace
+
+hipError_t launch_gemv_batch(int fmt, const GemvJob* jobs, int64_t count, hipStream_t stream) {
+  switch (fmt) {
+    case kFmtQ4_0:
+      return launch_batch_fmt<FmtQ4_0, QMAT_BATCH_R_Q4_0, QMAT_BATCH_G_Q4_0, QMAT_BATCH_D_Q4_0,
+                              QMAT_GEMV_ROW_DEPTH_Q4_0>(jobs, count, stream);
+    case kFmtQ8_0:
+      return launch_batch_fmt<FmtQ8_0, QMAT_BATCH_R_Q8_0, QMAT_BATCH_G_Q8_0, QMAT_BATCH_D_Q8_0,
+                              QMAT_GEMV_ROW_DEPTH_Q8_0>(jobs, count, stream);
+    case kFmtQ4_K:
+      return launch_batch_fmt<FmtQ4_K, QMAT_BATCH_R_Q4_K, QMAT_BATCH_G_Q4_K, QMAT_BATCH_D_Q4_K,
+                              QMAT_GEMV_ROW_DEPTH_Q4_K>(jobs, count, stream);
+    default:
+      return launch_batch_fmt<FmtQ6_K, QMAT_BATCH_R_Q6_K, QMAT_BATCH_G_Q6_K, QMAT_BATCH_D_Q6_K,
+                              QMAT_GEMV_ROW_DEPTH_Q6_K>(jobs, count, stream);
+  }
+}
 
 hipError_t launch_gemv(int fmt, const void* blocks, const float* x, float* y, int64_t M,
                        int64_t K, hipStream_t stream) {

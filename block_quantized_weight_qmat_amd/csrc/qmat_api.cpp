@@ -9,6 +9,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cstddef>
 #include <mutex>
 
 #include "qmat_launch.hpp"
@@ -162,6 +163,29 @@ int qmat_gemv(int fmt, const void* blocks, const float* x, float* y, int64_t M, 
   if ((rc = check_buf(x, K > 0)) != QMAT_OK) return rc;
   if ((rc = check_buf(y, true)) != QMAT_OK) return rc;
   return hip_status(qmat::launch_gemv(fmt, blocks, x, y, M, K, static_cast<hipStream_t>(stream)));
+}
+
+static_assert(sizeof(qmat_gemv_job) == sizeof(qmat::GemvJob) &&
+                  offsetof(qmat_gemv_job, M) == offsetof(qmat::GemvJob, M) &&
+                  offsetof(qmat_gemv_job, K) == offsetof(qmat::GemvJob, K),
+              "job layouts");
+
+int qmat_gemv_batch(int fmt, const qmat_gemv_job* jobs, int64_t count, void* stream) {
+  if (!fmt_ok(fmt)) return QMAT_E_FMT;
+  if (count < 0) return QMAT_E_SHAPE;
+  if (count == 0) return QMAT_OK;
+  if (jobs == nullptr) return QMAT_E_NULL;
+  for (int64_t i = 0; i < count; ++i) {
+    const qmat_gemv_job& j = jobs[i];
+    int rc = check_shape(fmt, j.M, j.K);
+    if (rc != QMAT_OK) return rc;
+    if (j.M == 0) continue;
+    if ((rc = check_buf(j.blocks, j.K > 0)) != QMAT_OK) return rc;
+    if ((rc = check_buf(j.x, j.K > 0)) != QMAT_OK) return rc;
+    if ((rc = check_buf(j.y, true)) != QMAT_OK) return rc;
+  }
+  return hip_status(qmat::launch_gemv_batch(fmt, reinterpret_cast<const qmat::GemvJob*>(jobs),
+                                            count, static_cast<hipStream_t>(stream)));
 }
 
 int qmat_gemm(int fmt, const void* blocks, const void* X_q8, float* Y, int64_t M, int64_t K,

@@ -23,6 +23,15 @@ hipError_t launch_kv_write(int fmt, const float* rows, const float* bias, void* 
 hipError_t launch_gemv(int fmt, const void* blocks, const float* x, float* y, int64_t M,
                        int64_t K, hipStream_t stream);
 
+// One GEMV of a batch (the layout of qmat_gemv_job).
+struct GemvJob {
+  const void* blocks;
+  const float* x;
+  float* y;
+  int64_t M, K;
+};
+hipError_t launch_gemv_batch(int fmt, const GemvJob* jobs, int64_t count, hipStream_t stream);
+
 // Few-token product (the decode batch): W streamed once per 16 tokens.
 hipError_t launch_gemm_small(int fmt, const void* blocks, const void* Xq8, float* Y, int64_t M,
                              int64_t K, int64_t N, hipStream_t stream);

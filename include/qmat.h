@@ -1,10 +1,11 @@
 /*
  * qmat.h — C ABI of the block-quantized weight matmul for MI355X (gfx950).
  *
- * Five operations, all enqueued asynchronously on a caller-supplied HIP
+ * Six operations, all enqueued asynchronously on a caller-supplied HIP
  * stream:
  *   qmat_quantize  fp32 matrix  -> packed weight (or activation) blocks
  *   qmat_gemv      packed W × fp32 x        -> fp32 y        (decode)
+ *   qmat_gemv_batch many independent GEMVs, few launches     (decode)
  *   qmat_gemm      packed W × Q8_0 X blocks -> fp32 Y        (prefill)
  *   qmat_prefill   packed W × fp32 X        -> fp32 Y        (prefill, one call)
  *   qmat_kv_write  fp32 K or V rows -> Q4_0 / Q8_0 rows of a KV cache
@@ -188,6 +189,37 @@ int qmat_quantize(int fmt, const float *W, void *blocks, int64_t rows,
  */
 int qmat_gemv(int fmt, const void *blocks, const float *x, float *y,
               int64_t M, int64_t K, void *stream);
+
+/*
+ * qmat_gemv_batch — many independent decode GEMVs in as few launches as
+ *   possible: job i computes jobs[i].y = dequant(W_i) x_i exactly as
+ *   qmat_gemv(fmt, jobs[i].blocks, jobs[i].x, jobs[i].y, jobs[i].M,
+ *   jobs[i].K, stream) would (same kernels, same bits). [LC05 "带宽决定
+ *   Decode"]: each weight byte is read once per token; a decode step runs
+ *   many small GEMVs (a 0.6B model's layers are 1024 to 3072 wide), whose
+ *   cost at one launch each is mostly the launch.
+ *   jobs: HOST array of count descriptors, read during the call only.
+ *   fmt applies to every job. Every job is checked as qmat_gemv checks its
+ *   arguments, all of them before anything is enqueued; the first failure
+ *   is returned. Jobs with M == 0 are skipped. Outputs must not overlap each
+ *   other or any input.
+ *   Jobs whose rows hold 8192 to 16384 elements take one launch each; the
+ *   others are grouped, up to 64 jobs per launch, by the parity of their row
+ *   stride (rows starting at 2 mod 4 or not) and by the shape of their
+ *   workgroups (rows of at most 1024 elements, or the number of 2048-element
+ *   strips a row spans), so a call makes at most a few launches per shape
+ *   present plus one per long-row job. The launches are enqueued in order
+ *   on stream; the host returns once they are enqueued.
+ */
+typedef struct qmat_gemv_job {
+  const void *blocks; /* W: M rows of K in fmt */
+  const float *x;     /* fp32 [K] */
+  float *y;           /* fp32 [M], overwritten */
+  int64_t M;
+  int64_t K;
+} qmat_gemv_job;
+
+int qmat_gemv_batch(int fmt, const qmat_gemv_job *jobs, int64_t count, void *stream);
 
 /*
  * qmat_gemm — prefill matrix product over N tokens:

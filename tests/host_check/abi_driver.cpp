@@ -83,6 +83,26 @@ int main() {
   EXPECT(qmat_gemv(1, NULL, NULL, NULL, 0, 64, NULL), QMAT_OK, 0);
   EXPECT(qmat_gemm(0, NULL, NULL, NULL, 3, 64, 0, NULL), QMAT_OK, 0);
   EXPECT(qmat_kv_write(0, NULL, NULL, NULL, 0, 0, 4, 256, NULL), QMAT_OK, 0);
+  // batched GEMVs: every job checked before anything is enqueued
+  {
+    qmat_gemv_job good = {A, F, F, 64, 1024};
+    qmat_gemv_job jobs[3] = {good, good, good};
+    EXPECT(qmat_gemv_batch(7, jobs, 3, NULL), QMAT_E_FMT, 0);
+    EXPECT(qmat_gemv_batch(0, jobs, -1, NULL), QMAT_E_SHAPE, 0);
+    EXPECT(qmat_gemv_batch(0, NULL, 2, NULL), QMAT_E_NULL, 0);
+    EXPECT(qmat_gemv_batch(0, NULL, 0, NULL), QMAT_OK, 0);
+    jobs[2].K = 48;
+    EXPECT(qmat_gemv_batch(0, jobs, 3, NULL), QMAT_E_SHAPE, 0);
+    jobs[2].K = 1024;
+    jobs[1].y = (float*)(Ab + 4);
+    EXPECT(qmat_gemv_batch(0, jobs, 3, NULL), QMAT_E_ALIGN, 0);
+    jobs[1].y = NULL;
+    EXPECT(qmat_gemv_batch(0, jobs, 3, NULL), QMAT_E_NULL, 0);
+    jobs[1].M = 0;  // skipped: no pointer needed
+    EXPECT(qmat_gemv_batch(0, jobs, 3, NULL), QMAT_OK, 1);
+    jobs[0].M = INT64_MAX;
+    EXPECT(qmat_gemv_batch(0, jobs, 3, NULL), QMAT_E_SHAPE, 0);
+  }
   // accepted calls reach the launchers (quantize + gemm for the prefills)
   EXPECT(qmat_quantize(3, F, A, 7, 512, NULL), QMAT_OK, 1);
   EXPECT(qmat_gemv(0, A, F, F, 4096, 11008, NULL), QMAT_OK, 1);

@@ -30,6 +30,10 @@ hipError_t launch_gemv(int, const void*, const float*, float*, int64_t, int64_t,
   ++g_launches;
   return hipSuccess;
 }
+hipError_t launch_gemv_batch(int, const GemvJob*, int64_t, hipStream_t) {
+  ++g_launches;
+  return hipSuccess;
+}
 hipError_t launch_gemm_small(int, const void*, const void*, float*, int64_t, int64_t, int64_t,
                              hipStream_t) {
   ++g_launches;

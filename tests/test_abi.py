@@ -217,3 +217,24 @@ def test_documented_departures_from_the_planned_header(lib):
     import block_quantized_weight_qmat_amd as pkg
     for name in pkg.__all__:
         assert getattr(pkg, name) is not None, name
+
+
+def test_gemv_batch_arguments(lib):
+    """Every job is checked before anything is enqueued; a bad one anywhere
+    fails the whole call with its status."""
+    J = binding.GemvJob
+    good = J(A, A, A, 64, 1024)
+    arr = (J * 3)(good, good, good)
+    f = lib.qmat_gemv_batch
+    p = ctypes.cast(arr, ctypes.c_void_p)
+    assert f(9, p, 3, None) == E_FMT
+    assert f(0, p, -1, None) == E_SHAPE
+    assert f(0, None, 2, None) == E_NULL
+    assert f(0, None, 0, None) == OK
+    arr[2] = J(A, A, A, 64, 48)
+    assert f(0, p, 3, None) == E_SHAPE
+    arr[2] = J(A, A, A + 8, 64, 1024)
+    assert f(0, p, 3, None) == E_ALIGN
+    arr[2] = J(A, None, A, 64, 1024)
+    assert f(0, p, 3, None) == E_NULL
+    assert ctypes.sizeof(J) == 40

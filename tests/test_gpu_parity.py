@@ -275,11 +275,16 @@ def test_gemv_small_and_ragged(q, fmt):
               (129, 1024), (9, 256 * 40), (6, 256 * 72), (64, 256 * 9), (200, 256 * 43),
               # rows of 256..512 slices take the row-per-wave kernel: its first
               # and last sizes, an odd strip count, and just past its limit
-              (33, 8192), (20, 16384), (18, 256 * 33), (7, 256 * 65)]
+              (33, 8192), (20, 16384), (18, 256 * 33), (7, 256 * 65),
+              # rows of at most 32 slices: both halves of a wave take rows
+              (40, 256), (33, 768), (16, 1024), (2, 1024), (100, 512)]
     if fmt < 2:
         shapes += [(1, 32), (5, 32 * 37), (2, 64), (40, 32 * 1001), (100, 32 * 345),
                    (65, 32 * 1001), (130, 32 * 65), (19, 32 * 257), (21, 32 * 511),
-                   (7, 32 * 513)]
+                   (7, 32 * 513),
+                   # pair mode with odd row strides (an odd slice count)
+                   (17, 32), (2, 32), (3, 32 * 3), (37, 32 * 31), (50, 32 * 17), (33, 32 * 5),
+                   (16, 32 * 33)]
     for M, K in shapes:
         say(f"gemv fmt={fmt} M={M} K={K}")
         W = mixed_matrix(rng, M, K) if M > 2 else rng.normal(0, 0.02, (M, K)).astype(np.float32)
@@ -292,6 +297,8 @@ def test_gemv_small_and_ragged(q, fmt):
 def test_gemv_one_hot_gives_the_column(q, fmt):
     rng = np.random.default_rng(300)
     for M, K, k in [(40, 2048, k) for k in (0, 15, 16, 31, 32, 1000, 2047)] + \
+                   [(40, 1024, k) for k in (0, 31, 32, 1023)] + \
+                   ([(9, 32 * 31, k) for k in (0, 500, 991)] if fmt < 2 else []) + \
                    [(70, 4096, k) for k in (0, 2047, 2048, 4095)] + \
                    [(35, 11008, k) for k in (0, 4100, 11007)]:
         W = rng.normal(0, 0.02, (M, K)).astype(np.float32)
@@ -317,8 +324,8 @@ def test_gemv_activation_range(q, fmt):
     """Per-32 power-of-two prescaling keeps any finite x in fp16 range."""
     rng = np.random.default_rng(400)
     # K = 4096 and K = 11008 take the two GEMV kernels (rows of fewer or more
-    # than 256 slices)
-    cases = [(M, K, name, scale) for M, K in ((24, 4096), (70, 4096), (37, 11008))
+    # than 256 slices), K = 1024 the strip kernel's pair mode
+    cases = [(M, K, name, scale) for M, K in ((24, 4096), (70, 4096), (37, 11008), (40, 1024))
              for name, scale in (("tiny", 1e-30), ("huge", 1e30), ("subnormal", 1e-40),
                                  ("mixed", None), ("binade-top", "top"))]
     for M, K, name, scale in cases:
@@ -384,6 +391,72 @@ def test_gemv_qwen3_decode_set(q):
             worst[fmt] = max(worst[fmt], e)
             assert e <= GEMV_TOL, (name, fmt, e)
     say(f"gemv qwen3 worst rel_l2 {worst}")
+
+
+def test_gemv_batch_qwen3_set(q):
+    """The 196-matrix Qwen3-0.6B-like set as one batch (four launches of up to
+    64 jobs): every output bit-identical to the one-matrix call and within the
+    GEMV bound of the oracle."""
+    import torch
+    for fmt in (0, 1):
+        say(f"gemv batch qwen3 set fmt={fmt}")
+        jobs, refs, guards, dev = [], [], [], []
+        for i in range(len(inputs.qwen3_shapes())):
+            _, W, x = inputs.qwen3_matrix(i)
+            M, K = W.shape
+            B = oracle.quantize(fmt, W)
+            dB, dx = dev_tensor(B), dev_tensor(x)
+            g = Guarded((M,))
+            jobs.append((dB, dx, g.out, M, K))
+            guards.append(g)
+            dev.append((dB, dx))
+            if i % 7 == 0:
+                refs.append((i, oracle.gemv(fmt, B, x, M, K)))
+        q.gemv_batch(fmt, jobs)
+        torch.cuda.synchronize()
+        for i, ref in refs:
+            y = guards[i].get()
+            assert rel_l2(y, ref) <= GEMV_TOL, (fmt, i)
+        for i, (dB, dx) in enumerate(dev):
+            M, K = jobs[i][3], jobs[i][4]
+            one = gpu_gemv(q, fmt, dB, dx, M, K)
+            assert np.array_equal(guards[i].get().view(np.uint32), one.view(np.uint32)), (fmt, i)
+
+
+@pytest.mark.parametrize("fmt", [0, 1, 2, 3])
+def test_gemv_batch_mixed(q, fmt):
+    """Jobs of every kind in one call: rows for the row-per-wave kernel, odd
+    row strides, a single row, M = 0 and K = 0 jobs, and more than 64 jobs
+    (several launches); each output equals the one-matrix call's bits."""
+    import torch
+    rng = np.random.default_rng(1300 + fmt)
+    if fmt < 2:
+        shapes = [(70, 11008), (33, 32 * 37), (1, 32 * 37), (0, 1024), (19, 0), (129, 4096),
+                  (200, 32 * 345)] + [(int(rng.integers(1, 90)), 32 * int(rng.integers(1, 200)))
+                                      for _ in range(70)]
+    else:
+        shapes = [(70, 11008), (9, 256 * 9), (1, 256 * 9), (0, 1024), (19, 0), (129, 4096)] + \
+                 [(int(rng.integers(1, 90)), 256 * int(rng.integers(1, 40))) for _ in range(70)]
+    say(f"gemv batch mixed fmt={fmt}: {len(shapes)} jobs")
+    jobs, guards, dev = [], [], []
+    for M, K in shapes:
+        W = rng.normal(0, 0.02, (M, K)).astype(np.float32)
+        x = rng.normal(0, 1, K).astype(np.float32)
+        dB = dev_tensor(oracle.quantize(fmt, W)) if M * K else torch.empty(
+            M * oracle.row_bytes(fmt, K), dtype=torch.uint8, device="cuda")
+        dx = dev_tensor(x) if K else torch.empty(0, dtype=torch.float32, device="cuda")
+        g = Guarded((M,))
+        jobs.append((dB, dx, g.out, M, K))
+        guards.append(g)
+        dev.append((dB, dx))
+    q.gemv_batch(fmt, jobs)
+    torch.cuda.synchronize()
+    for i, (M, K) in enumerate(shapes):
+        if M == 0:
+            continue
+        got = guards[i].get()
+        one = gpu_gemv(q, fmt, dev[i][0], dev[i][1], M, K)
+        assert np.array_equal(got.view(np.uint32), one.view(np.uint32)), (fmt, i, M, K)
 
 
 @pytest.mark.parametrize("orient", [0, 1])
