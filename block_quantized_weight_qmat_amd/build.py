@@ -24,7 +24,7 @@ MICRO_LIB = os.path.join(PKG, "libqmat_micro.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["quantize.hip", "gemv.hip", "gemm.hip", "qmat_api.cpp"]
+SOURCES = ["quantize.hip", "gemv.hip", "decode.hip", "gemm.hip", "qmat_api.cpp"]
 MICRO_SOURCES = ["micro.hip"]
 
 CFLAGS = [
@@ -50,7 +50,9 @@ def _compile(src: str) -> str:
 
 def _link(objs: list, lib: str) -> None:
     tmp = lib + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    # -z defs: a kernel whose host stub was not emitted (an instantiation the
+    # host pass dropped) is an error here, not a library that fails to load
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,-z,defs", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")

@@ -1,0 +1,338 @@
+// decode.hip — the decode batch on the int8 matrix cores: Y = W X^T for 5 to
+// 16 tokens per launch, W in Q4_0 or Q8_0 blocks, X in Q8_0 blocks.
+//
+// Source: "05. llama.cpp：从 GGUF 文件到本地推理服务", sections "槽位、连续批处理与
+// 上下文切分" (several requests decoded at once) and "性能直觉：带宽决定 Decode，
+// 算力决定 Prefill" (decode is bound by reading the weights): a batch of tokens
+// shares one read of W, so the weight stream stays the bound as long as the
+// per-token arithmetic stays off the critical path.
+//
+// Work split. A workgroup owns 16 rows of W and all of K; its waves (16, 12
+// or 8, as LDS allows) take contiguous shares of the rows' stages. A stage
+// is 8 blocks of every row (144 or 272 bytes per row) and of every token
+// (272 bytes): both are whole 16-byte pieces, so the copies go from memory
+// straight into LDS (global_load_lds, 64 pieces per instruction). Each wave keeps its own ring
+// of D stages and issues a stage's weight and token copies together, D - 1
+// stages ahead; it waits for a stage by counting its outstanding copies
+// (they complete in issue order), so the waves never synchronise until the
+// final sum, and each stage is used as soon as it has landed.
+//
+// Arithmetic per block, exact in integers: one v_mfma_i32_16x16x32_i8 takes
+// the 16 rows' 32 codes (A) and the 16 tokens' 32 codes (B). Lane l supplies
+// row/token l % 16 and the elements 4q..4q+3 and 16+4q..16+4q+3 (q = l / 16)
+// of the block: for Q4_0 these are the two nibbles of code bytes 4q..4q+3,
+// read as one dword and turned into 16 (c - 8) with an XOR and two masks;
+// for Q8_0 (and X) two dwords of codes, realigned when the block starts at
+// 0 mod 4 (codes at 2 mod 4). The MFMA accumulates onto 1.5 * 2^23, so each
+// integer sum C comes out as the float 1.5 * 2^23 + C (|C| < 2^22) and
+// fma(F, dx, -1.5 * 2^23 * dx) is C * dx rounded once (1.5 dx is exact for
+// an fp16 dx); a second fma adds C * dx * dw to the lane's fp32 sums of rows
+// 4q..4q+3 for token l % 16. Lane 16q + r reads the scale of row 4q + (r & 3),
+// and a DPP row broadcast hands each lane the scales of its four rows.
+// A wave reads every LDS word of a stage's 8 blocks before it uses any, so
+// the reads overlap each other and the previous blocks' arithmetic.
+// The waves' sums meet in LDS and are added in wave order (deterministic).
+//
+// What bounds it: the copies. Every workgroup copies all of X next to its
+// 16 rows of W (at 16 tokens 187 KB of X per 99 KB of Q4_0 weights at
+// K = 11008), and the copies alone take about as long as the whole kernel
+// minus the arithmetic of its last stages.
+#include "qmat_device.hpp"
+#include "qmat_launch.hpp"
+
+namespace qmat {
+namespace {
+
+constexpr uint32_t kDecMagicI = 0x4B400000u;  // 1.5 * 2^23 as fp32 bits
+constexpr float kDecMagicF = 12582912.0f;
+constexpr int kDecRows = 16;   // rows of W per workgroup: the MFMA's A rows
+constexpr int kGroup = 8;      // blocks per stage
+constexpr int kXRowBytes = kGroup * 34;
+
+template <bool kQ4>
+struct DecW {
+  static constexpr int kBytes = kQ4 ? 18 : 34;
+  static constexpr int kRowBytes = kGroup * kBytes;  // one row's share of a stage
+  static constexpr int kPiecesPerRow = kRowBytes / 16;
+  static constexpr int kPieces = kDecRows * kPiecesPerRow;
+  static constexpr int kLoads = (kPieces + kWave - 1) / kWave;
+  static constexpr int kStage = kDecRows * kRowBytes;
+  static_assert(kRowBytes % 16 == 0, "whole pieces");
+};
+
+template <int NT>
+struct DecX {
+  static constexpr int kPiecesPerRow = kXRowBytes / 16;
+  static constexpr int kPieces = NT * kPiecesPerRow;
+  static constexpr int kLoads = (kPieces + kWave - 1) / kWave;
+  static constexpr int kStage = NT * kXRowBytes;
+};
+
+// Per wave: a ring of kDepth stages (weights and tokens). As many waves as 160 KB of LDS allows with a ring of
+// at least two stages (16, 12 or 8: the waves hide each other's LDS and
+// matrix-core latency), each with the deepest ring that then fits.
+template <bool kQ4, int NT>
+struct DecRing {
+  static constexpr int kStage = DecW<kQ4>::kStage + DecX<NT>::kStage;
+  static constexpr int depth_for(int waves) { return 163840 / waves / kStage; }
+  static constexpr int kWaves = depth_for(16) >= 2 ? 16 : depth_for(12) >= 2 ? 12 : 8;
+  static constexpr int kDepth0 = depth_for(kWaves);
+  static constexpr int kDepth = kDepth0 > 6 ? 6 : kDepth0;
+  static constexpr int kLoads = DecW<kQ4>::kLoads + DecX<NT>::kLoads;
+  static constexpr int kWaveLds = kDepth * kStage;
+  static_assert(kDepth >= 2 && (kDepth - 1) * kLoads < 64, "ring");
+  static_assert(kWaves * 4 * kWave * 4 <= kWaves * kWaveLds, "final sums fit");
+};
+
+// Wait until at most N copies are outstanding. The copies land in LDS behind
+// the compiler's back, so no LDS access may move across the wait.
+template <int N>
+__device__ __forceinline__ void wait_copies() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm<N>());
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+}
+
+// Wait until at most n * kPer copies are outstanding, 0 <= n < kMax (n is
+// wave-uniform; the immediate must be a constant).
+template <int kPer, int kMax>
+__device__ __forceinline__ void wait_stages(int n) {
+  if constexpr (kMax > 1) {
+    if (n >= kMax - 1) {
+      wait_copies<(kMax - 1) * kPer>();
+      return;
+    }
+    wait_stages<kPer, kMax - 1>(n);
+  } else {
+    wait_copies<0>();
+  }
+}
+
+// The LDS words a lane needs from one block: codes of elements 4q..4q+3
+// and 16+4q..16+4q+3 of its weight row and of its token, and the fp16 scales
+// of its token and of the row it broadcasts. A block at 0 mod 4 has its
+// codes at 2 mod 4, so each 4-byte run spans two words (w[0..1], w[2..3]);
+// a block at 2 mod 4 has them aligned (w[0], w[1]). Q4_0 codes hold both
+// element runs in the nibbles of one 4-byte run.
+struct BlockWords {
+  uint32_t w[4], x[4];
+  uint32_t dxb, swb;
+};
+
+template <bool kQ4>
+__device__ __forceinline__ void fetch_words(const uint8_t* wb, const uint8_t* xb, bool odd, int q,
+                                            BlockWords& o) {
+  if (!odd) {
+    const uint32_t* pw = reinterpret_cast<const uint32_t*>(wb + 4 * q);
+    o.w[0] = pw[0];
+    o.w[1] = pw[1];
+    if (!kQ4) {
+      o.w[2] = pw[4];
+      o.w[3] = pw[5];
+    }
+    const uint32_t* px = reinterpret_cast<const uint32_t*>(xb + 4 * q);
+    o.x[0] = px[0];
+    o.x[1] = px[1];
+    o.x[2] = px[4];
+    o.x[3] = px[5];
+  } else {
+    const uint32_t* pw = reinterpret_cast<const uint32_t*>(wb + 2 + 4 * q);
+    o.w[0] = pw[0];
+    if (!kQ4) o.w[1] = pw[4];
+    const uint32_t* px = reinterpret_cast<const uint32_t*>(xb + 2 + 4 * q);
+    o.x[0] = px[0];
+    o.x[1] = px[4];
+  }
+  o.dxb = *reinterpret_cast<const uint16_t*>(xb);
+}
+
+// Q8_0 codes of the lane's 8 elements as the MFMA operand (low dword:
+// elements 4q..4q+3, high dword: 16+4q..16+4q+3).
+__device__ __forceinline__ uint64_t q8_operand(const uint32_t (&w)[4], bool odd) {
+  const uint32_t lo = odd ? w[0] : __builtin_amdgcn_alignbyte(w[1], w[0], 2);
+  const uint32_t hi = odd ? w[1] : __builtin_amdgcn_alignbyte(w[3], w[2], 2);
+  return (uint64_t)hi << 32 | lo;
+}
+
+// The same elements of a Q4_0 block as 16 (c - 8): code byte t holds element
+// t in its low nibble and element t + 16 in its high nibble, and c ^ 8 read
+// as the top nibble of a byte is 16 (c - 8).
+__device__ __forceinline__ uint64_t q4_operand(const uint32_t (&w)[4], bool odd) {
+  const uint32_t c = odd ? w[0] : __builtin_amdgcn_alignbyte(w[1], w[0], 2);
+  const uint32_t v = c ^ 0x88888888u;
+  const uint32_t lo = (v << 4) & 0xF0F0F0F0u;
+  const uint32_t hi = v & 0xF0F0F0F0u;
+  return (uint64_t)hi << 32 | lo;
+}
+
+// The value of s held by lane v of this lane's 16-lane row (DPP
+// row_newbcast:v).
+template <int v>
+__device__ __forceinline__ float row_bcast(float s) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, s),
+                                                               0x150 + v, 0xF, 0xF, false));
+}
+
+template <bool kQ4, int NT>
+__global__ __launch_bounds__((DecRing<kQ4, NT>::kWaves * kWave)) void decode_mfma_kernel(
+    const uint8_t* __restrict__ Wb, const uint8_t* __restrict__ Xq, float* __restrict__ Y,
+    int64_t M, int K, int64_t N, int64_t n0) {
+  using WS = DecW<kQ4>;
+  using XS = DecX<NT>;
+  using RG = DecRing<kQ4, NT>;
+  constexpr int kWaves = RG::kWaves;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kWaves * RG::kWaveLds];
+  const int lane = (int)(threadIdx.x & 63);
+  const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  uint8_t* ring = lds + wv * RG::kWaveLds;  // slot: weights, then tokens
+  const int ns = K >> 5;
+  const int ngroups = ns / kGroup;
+  const int ga = (int)((int64_t)wv * ngroups / kWaves);
+  const int gb = (int)((int64_t)(wv + 1) * ngroups / kWaves);
+  const int64_t m0 = (int64_t)blockIdx.x * kDecRows;
+  const int64_t rb = (int64_t)ns * WS::kBytes, xrb = (int64_t)ns * 34;
+
+  // Copy sources: piece p = lane + 64 d of a stage is 16 bytes of row (or
+  // token) p / pieces-per-row. Rows past M and tokens past N copy the last
+  // valid one; their results are not stored.
+  const uint8_t* wsrc[WS::kLoads];
+#pragma unroll
+  for (int d = 0; d < WS::kLoads; ++d) {
+    const int p = lane + kWave * d;
+    const int r = p / WS::kPiecesPerRow, u = p - r * WS::kPiecesPerRow;
+    int64_t m = m0 + (r < kDecRows ? r : kDecRows - 1);
+    if (m >= M) m = M - 1;
+    wsrc[d] = Wb + m * rb + 16 * u;
+  }
+  const uint8_t* xsrc[XS::kLoads];
+#pragma unroll
+  for (int d = 0; d < XS::kLoads; ++d) {
+    const int p = lane + kWave * d;
+    const int t = p / XS::kPiecesPerRow, u = p - t * XS::kPiecesPerRow;
+    int64_t n = n0 + (t < NT ? t : NT - 1);
+    if (n >= N) n = N - 1;
+    xsrc[d] = Xq + n * xrb + 16 * u;
+  }
+  // Stage g goes to ring slot g mod depth, its weight copies first. Lane 0
+  // of every copy instruction is inside the stage, so each instruction is
+  // issued and counted.
+  auto issue = [&](int g) {
+    uint8_t* dst = ring + (g % RG::kDepth) * RG::kStage;
+    const int64_t woff = (int64_t)g * WS::kRowBytes, xoff = (int64_t)g * kXRowBytes;
+#pragma unroll
+    for (int d = 0; d < WS::kLoads; ++d)
+      if (lane + kWave * d < WS::kPieces)
+        __builtin_amdgcn_global_load_lds((const void*)(wsrc[d] + woff),
+                                         (lds_ptr_t)(dst + 1024 * d), 16, 0, 0);
+#pragma unroll
+    for (int d = 0; d < XS::kLoads; ++d)
+      if (lane + kWave * d < XS::kPieces)
+        __builtin_amdgcn_global_load_lds((const void*)(xsrc[d] + xoff),
+                                         (lds_ptr_t)(dst + WS::kStage + 1024 * d), 16, 0, 0);
+  };
+
+  const int i16 = lane & 15, q = lane >> 4;
+  const int tj = i16 < NT ? i16 : NT - 1;  // the token this lane supplies to B
+  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+
+  // Lane 16 q + r also reads the scale of row 4 q + (r & 3); a row broadcast
+  // (DPP row_newbcast:v) then gives every lane of DPP row q the scale of row
+  // 4 q + v, the row of its v-th sum.
+  const int srow = 4 * q + (lane & 3);
+  const i32x4 cmagic = {(int)kDecMagicI, (int)kDecMagicI, (int)kDecMagicI, (int)kDecMagicI};
+
+  auto compute = [&](int g) {
+    const uint8_t* ws = ring + (g % RG::kDepth) * RG::kStage;
+    const uint8_t* xs = ws + WS::kStage;
+    const uint8_t* wr = ws + i16 * WS::kRowBytes;
+    const uint8_t* xr = xs + tj * kXRowBytes;
+    const uint8_t* sr = ws + srow * WS::kRowBytes;
+    // every LDS word of the stage's 8 blocks first, so the reads overlap
+    BlockWords bw[kGroup];
+#pragma unroll
+    for (int k = 0; k < kGroup; ++k) {
+      fetch_words<kQ4>(wr + k * WS::kBytes, xr + 34 * k, (k & 1) != 0, q, bw[k]);
+      bw[k].swb = *reinterpret_cast<const uint16_t*>(sr + k * WS::kBytes);
+    }
+#pragma unroll
+    for (int k = 0; k < kGroup; ++k) {
+      const bool odd = (k & 1) != 0;
+      const uint64_t a = kQ4 ? q4_operand(bw[k].w, odd) : q8_operand(bw[k].w, odd);
+      const uint64_t b = q8_operand(bw[k].x, odd);
+      const i32x4 c = __builtin_amdgcn_mfma_i32_16x16x32_i8((long)a, (long)b, cmagic, 0, 0, 0);
+      const float dx = f16_bits_to_f32(bw[k].dxb);
+      const float mdx = -kDecMagicF * dx;
+      const float S = f16_bits_to_f32(bw[k].swb);
+      const f32x4 F = __builtin_bit_cast(f32x4, c);
+      acc[0] = fmaf(fmaf(F.x, dx, mdx), row_bcast<0>(S), acc[0]);
+      acc[1] = fmaf(fmaf(F.y, dx, mdx), row_bcast<1>(S), acc[1]);
+      acc[2] = fmaf(fmaf(F.z, dx, mdx), row_bcast<2>(S), acc[2]);
+      acc[3] = fmaf(fmaf(F.w, dx, mdx), row_bcast<3>(S), acc[3]);
+    }
+  };
+
+  for (int i = 0; i < RG::kDepth - 1; ++i)
+    if (ga + i < gb) issue(ga + i);
+  for (int g = ga; g < gb; ++g) {
+    // copies issued after stage g's: stages g + 1 .. min(g + depth - 2, gb - 1)
+    const int after = gb - 1 - g < RG::kDepth - 2 ? gb - 1 - g : RG::kDepth - 2;
+    wait_stages<RG::kLoads, RG::kDepth - 1>(after);
+    // stage g + depth - 1 reuses the slot of stage g - 1, read last iteration
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    if (g + RG::kDepth - 1 < gb) issue(g + RG::kDepth - 1);
+    compute(g);
+  }
+
+  // the waves' sums, added in wave order
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(lds);  // [wave][4][64]
+#pragma unroll
+  for (int v = 0; v < 4; ++v) red[(wv * 4 + v) * kWave + lane] = acc[v];
+  __syncthreads();
+  if (wv == 0) {
+    const int64_t n = n0 + i16;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      float s = 0.0f;
+      for (int w = 0; w < kWaves; ++w) s += red[(w * 4 + v) * kWave + lane];
+      const int64_t m = m0 + 4 * q + v;
+      if (m < M && n < N && i16 < NT) Y[n * M + m] = kQ4 ? s * 0.0625f : s;
+    }
+  }
+}
+
+template <bool kQ4, int NT>
+hipError_t launch_dec(const void* blocks, const void* Xq8, float* Y, int64_t M, int64_t K,
+                      int64_t N, int64_t n0, hipStream_t stream) {
+  const int64_t grid = (M + kDecRows - 1) / kDecRows;
+  hipLaunchKernelGGL((decode_mfma_kernel<kQ4, NT>), dim3((unsigned)grid),
+                     dim3(DecRing<kQ4, NT>::kWaves * kWave), 0, stream, static_cast<const uint8_t*>(blocks),
+                     static_cast<const uint8_t*>(Xq8), Y, M, (int)K, N, n0);
+  return hipGetLastError();
+}
+
+template <bool kQ4>
+hipError_t launch_dec_fmt(const void* blocks, const void* Xq8, float* Y, int64_t M, int64_t K,
+                          int64_t N, int64_t n0, hipStream_t stream) {
+  const int64_t nt = N - n0;
+  if (nt <= 8) return launch_dec<kQ4, 8>(blocks, Xq8, Y, M, K, N, n0, stream);
+  return launch_dec<kQ4, 16>(blocks, Xq8, Y, M, K, N, n0, stream);
+}
+
+}  // namespace
+
+bool decode_mfma_fits(int fmt, int64_t K) {
+  return (fmt == kFmtQ4_0 || fmt == kFmtQ8_0) && K >= 32 * kGroup && K % (32 * kGroup) == 0;
+}
+
+hipError_t launch_decode_mfma(int fmt, const void* blocks, const void* Xq8, float* Y, int64_t M,
+                              int64_t K, int64_t N, int64_t n0, hipStream_t stream) {
+  if (M == 0 || N <= n0) return hipSuccess;
+  return fmt == kFmtQ4_0 ? launch_dec_fmt<true>(blocks, Xq8, Y, M, K, N, n0, stream)
+                         : launch_dec_fmt<false>(blocks, Xq8, Y, M, K, N, n0, stream);
+}
+
+}  // namespace qmat

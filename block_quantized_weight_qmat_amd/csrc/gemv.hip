@@ -598,15 +598,6 @@ constexpr int log2i() {
 // phase read eight different columns (no bank conflicts).
 constexpr int kXStripBytes = kWave * 128;
 
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
-// s_waitcnt immediate (gfx9 encoding) that waits until at most N vector
-// memory operations are outstanding, leaving the other counters free.
-template <int N>
-constexpr int vmcnt_imm() {
-  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
-  return (N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8);
-}
 
 __device__ __forceinline__ void x_to_lds(const float* __restrict__ xs, int nsl, uint8_t* strip,
                                          int lane) {
@@ -1551,10 +1542,25 @@ hipError_t launch_gemv(int fmt, const void* blocks, const float* x, float* y, in
 
 namespace qmat {
 
+#ifndef QMAT_DECODE_MFMA
+#define QMAT_DECODE_MFMA 1
+#endif
+// Chunks of at least this many tokens go to the matrix-core kernel when it
+// takes the format and K. Measured at 4096 x 11008 (Q4_0 / Q8_0): up to 4
+// tokens this kernel is faster (9.5 / 12.4 us at 4 against 10.4 / 12.8), from
+// 5 the matrix cores are (8 tokens: 11.4 / 13.3 us against 12.8 / 13.7; 16:
+// 12.8 / 15.3 against 20.7 / 21.4).
+constexpr int64_t kDecodeMfmaMinTokens = 5;
+
 hipError_t launch_gemm_small(int fmt, const void* blocks, const void* Xq8, float* Y, int64_t M,
                              int64_t K, int64_t N, hipStream_t stream) {
   for (int64_t n0 = 0; n0 < N; n0 += 16) {
     hipError_t e;
+    if (QMAT_DECODE_MFMA && N - n0 >= kDecodeMfmaMinTokens && decode_mfma_fits(fmt, K)) {
+      e = launch_decode_mfma(fmt, blocks, Xq8, Y, M, K, N, n0, stream);
+      if (e != hipSuccess) return e;
+      continue;
+    }
     switch (fmt) {
       case kFmtQ4_0:
         e = launch_small_chunk<FmtQ4_0>(blocks, Xq8, Y, M, K, N, n0, stream);

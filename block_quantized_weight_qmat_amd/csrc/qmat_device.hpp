@@ -63,6 +63,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
                                            0x00020000);
 }
 
+// LDS pointers for the direct memory-to-LDS loads (global_load_lds).
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// s_waitcnt immediate (gfx9 encoding) that waits until at most N vector
+// memory operations are outstanding, leaving the other counters free.
+template <int N>
+constexpr int vmcnt_imm() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  return (N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8);
+}
+
 __device__ __forceinline__ float shfl_xor_f(float v, int mask) {
   return __shfl_xor(v, mask, kWave);
 }

@@ -31,7 +31,6 @@ __device__ __forceinline__ float clampf(float v, float lo, float hi) {
 // Part k (elements 4k..4k+3) of block b sits in column (k + b / 2) mod 8 of
 // row b, so the 16 lanes of an LDS access phase hit 16 different 16-byte bank
 // groups when lane b reads its block back.
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 __device__ __forceinline__ void stage_blocks(const float* __restrict__ src, int nblk, float* lds,
                                              int lane) {

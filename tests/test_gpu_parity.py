@@ -555,6 +555,11 @@ def test_gemm_decode_small_n(q, fmt):
     cases += [(1, 256, 3), (2, 512, 16), (1000, 1024, 4), (33, 2048, 12)]
     if fmt < 2:
         cases += [(5, 32, 2), (64, 32 * 37, 6)]
+        # K a multiple of 256 takes the matrix-core kernel: every chunk size,
+        # ragged rows, fewer stages than waves (K = 768), and stage rings that
+        # wrap many times (K = 16384)
+        cases += [(97, 256 * 9, n) for n in (1, 2, 3, 4, 5, 8, 9, 15, 16, 17, 33, 48)]
+        cases += [(16, 2048, 16), (40, 768, 9), (17, 16384, 16), (300, 256 * 43, 7)]
     for M, K, N in cases:
         say(f"gemm decode fmt={fmt} M={M} K={K} N={N}")
         W = mixed_matrix(rng, M, K) if M > 2 else rng.normal(0, 0.02, (M, K)).astype(np.float32)
