@@ -29,11 +29,14 @@ Beside the step, every other workload of the measurement plan is timed per
 kernel (``kernels``): the 1024x1024 Q4_0 GEMV (latency); the 196-matrix
 Qwen3-0.6B-like decode set, Q4_0 and Q8_0, as one pass: one qmat_gemv_batch
 call (a few launches), and beside it the same 196 products as 196 qmat_gemv
-launches, each rotating over copies of the whole set; the 11008x4096 orientation of the 7B
-layer (the strip kernel); the Q4_K-style GEMV at 4096x4096 and 4096x11008
-with per-row scale spread; the decode batch, the Q6_K-style kernels, the
-other GEMM formats and the KV-cache write. The prefill GEMM reads a different
-copy of W at every launch as the GEMVs do.
+launches, each rotating over copies of the whole set; the 11008x4096
+orientation of the 7B layer (the strip kernel); the Q4_K-style GEMV at
+4096x4096 and 4096x11008 with per-row scale spread; the decode batch, the
+Q6_K-style kernels, the other GEMM formats, the KV-cache write, and the
+activation quantizer on a warm X (what a GEMM prologue would repeat once per
+128-row m-tile). The prefill GEMM reads a different copy of W at every
+launch as the GEMVs do, and each GEMM entry carries its VALU ceiling: the
+fp32 FMAs of its scale step at the measured FMA rate.
 
 Output: one JSON line. ``value`` is the Q4_0 GEMV's algorithmic bytes
 (packed weights + x + y) divided by its mean time per launch, the headline of
@@ -66,6 +69,11 @@ if ROOT not in sys.path:
 METRIC = "Q4_0 GEMV achieved HBM GB/s (% of peak) at 4096×11008; Q8 GEMM int8 TOPS"
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
 INT8_PEAK_TOPS = 5000.0     # MI355X dense int8 MFMA (5.0 POPS)
+FP32_FMA_TFLOPS = 78.6      # MI355X fp32 vector FMA without packed math (157.3 packed)
+# fp32 FMAs of the GEMM's scale step per output and 32-element block: S*dx,
+# then the accumulation (Q6_K-style: per 16-element half; the Q4_K-style
+# min term runs on an fp32 MFMA)
+GEMM_VALU_FMAS = {"q4_0": 2, "q8_0": 2, "q4_k": 2, "q6_k": 4}
 M, K, N = 4096, 11008, 512
 COLD_BYTES = 1.5 * 2 ** 30  # > 256 MB Infinity Cache, several times over
 COPY_BYTES = 64 * 2 ** 20   # calibration copy for the byte counters
@@ -88,6 +96,7 @@ GEMV_EXTRA = [("gemv_q4_0_1024x1024", 0, "gemv_1024"),
 QWEN3_OPS = ["qwen3_pass_q4_0", "qwen3_pass_q8_0", "qwen3_launches_q4_0", "qwen3_launches_q8_0"]
 EXTRA_OPS = ([f"decode_q4_0_n{n}" for n in DECODE_NS] + [g[0] for g in GEMV_EXTRA] + QWEN3_OPS
              + ["quantize_q6_k", "gemv_q6_k", "gemm_q8_0", "gemm_q4_k", "gemm_q6_k",
+                "quantize_act_q8_0_warm",
                 "kv_write_q4_0", "kv_write_q8_0"])
 
 
@@ -477,6 +486,9 @@ def main():
         table[f"gemv_{f}"] = lambda s, f=f, i=i: binding.gemv(
             i, cold[f][s % len(cold[f])], x, M, K, out=y[f])
     table["quantize_act_q8_0"] = lambda s: binding.quantize(1, X_rot[s % len(X_rot)], out=Xq)
+    # the same X every launch (22.5 MB, resident in the 256 MB Infinity
+    # Cache): the work a GEMM prologue would repeat once per 128-row m-tile
+    table["quantize_act_q8_0_warm"] = lambda s: binding.quantize(1, X_rot[0], out=Xq)
     # W from HBM at every launch, as in a prefill that streams each layer once
     table["gemm_q4_0"] = lambda s: binding.gemm(0, cold["q4_0"][s % len(cold["q4_0"])], Xq,
                                                 M, K, N, out=Y)
@@ -563,6 +575,10 @@ def main():
             gbs = actq_bytes / us / 1e3
             kernels[name] = {"us": us, "bytes": actq_bytes, "GB/s": gbs, "bound": "hbm",
                              "frac": gbs / HBM_PEAK_GBS}
+            if name.endswith("_warm"):
+                # a prologue-fused GEMM repeats it once per 128-row m-tile
+                kernels[name]["m_tiles"] = M // 128
+                kernels[name]["repeated_per_m_tile_us"] = us * (M // 128)
         elif name.startswith("quantize_"):
             f = name[9:]
             gbs = quant_bytes[f] / us / 1e3
@@ -602,6 +618,16 @@ def main():
                            gemv_bytes["q4_0"], args.cpu_seconds)
 
     peaks = None if args.no_peaks else measured_peaks(torch, gemv_bytes.get("q4_0"))
+    # The GEMM's VALU ceiling: its scale step alone, at the fp32 FMA rate that
+    # waves sharing their SIMD with int8 MFMA waves reach (measured), or the
+    # nominal non-packed rate
+    fma_rate = peaks["fp32_fma_TFLOPs_beside_mfma"] if peaks else FP32_FMA_TFLOPS
+    for name, kv in kernels.items():
+        if name.startswith("gemm_"):
+            flops = 2 * GEMM_VALU_FMAS[name[5:]] * M * N * (K // 32)
+            ceil_us = flops / fma_rate / 1e6
+            kv.update({"valu_fma_flops": flops, "valu_ceiling_us": ceil_us,
+                       "valu_rate_TFLOPs": fma_rate, "frac_of_valu_ceiling": ceil_us / kv["us"]})
     headline = kernels.get("gemv_q4_0")
     gemm = kernels.get("gemm_q4_0")
     traffic = traffic_for_current_kernel() if headline else None
@@ -635,6 +661,11 @@ def main():
         "gemm_frac_of_int8_peak": None if not gemm else round(gemm["frac"], 4),
         "gemm_frac_of_measured_int8": None if not (gemm and peaks) else round(
             gemm["TOPS"] / peaks["int8_mfma_TOPS"], 4),
+        "gemm_valu_ceiling": None if not gemm else {
+            "us": round(gemm["valu_ceiling_us"], 3), "frac": round(gemm["frac_of_valu_ceiling"], 4),
+            "fmas_per_output_block": GEMM_VALU_FMAS["q4_0"], "rate_TFLOPs": gemm["valu_rate_TFLOPs"],
+            "what": "2 fp32 FMAs per (m, n, 32-block) scale step at the fp32 FMA rate measured "
+                    "beside int8 MFMA waves (nominal 78.6 TFLOP/s without peaks)"},
         "measured_peaks": peaks,
         "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                     for k, v in kernels.items()},
