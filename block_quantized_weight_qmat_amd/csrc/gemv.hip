@@ -6,11 +6,13 @@
 // is therefore built around the HBM stream of packed blocks, and its integer
 // work per block is kept small enough to hide under that stream.
 //
-// Work split. Two kernels share the arithmetic below. Rows of 256 to 512
-// slices (K = 8192 .. 16384) use gemv_rows_kernel: a workgroup of 16 waves
-// owns 16 rows, one per wave; the activations are converted once per
-// workgroup into LDS digit records shared by the 16 rows (see the kernel).
-// Other rows use gemv_kernel:
+// Work split. Two kernels share the arithmetic below. Rows of 128 to 512
+// slices (K = 4096 .. 16384), and of 32 to 127 slices in matrices of at most
+// 8192 rows, use gemv_rows_kernel: a workgroup of 16 waves owns 16 rows, one
+// per wave; the activations are converted once per workgroup into LDS digit
+// records shared by the 16 rows (see the kernel). Other rows (shorter, or
+// short rows of taller matrices, where the row kernel's per-workgroup
+// conversion repeats too often) use gemv_kernel:
 //   * A workgroup owns G groups of R consecutive rows and all of K. Its waves
 //     split K into strips of 64 slices; lane l of a strip owns one
 //     32-element slice (one Q4_0/Q8_0 block, or one sub-block of a Q4_K
@@ -1016,12 +1018,23 @@ __global__ __launch_bounds__(kRowWaves * kWave) void gemv_rows_kernel(
 #ifndef QMAT_GEMV_ROWS
 #define QMAT_GEMV_ROWS 1
 #endif
-// rows of this many slices (4 strips) up to kRowMaxSlices go to the
-// row-per-wave kernel; shorter rows have too few strips to hide its
-// conversion of the activations in front of the stream
-#ifndef QMAT_GEMV_ROWS_MIN_SLICES
-#define QMAT_GEMV_ROWS_MIN_SLICES 256
-#endif
+// Which rows go to the row-per-wave kernel (measured crossovers against the
+// strip kernel, Q4_0 / Q8_0 / Q4_K-style): from 128 slices up to
+// kRowMaxSlices always (11008 x 4096: 8.1 against 8.7 us); from 32 slices in
+// matrices of at most 8192 rows (4096 x 2048: 3.4 against 4.5 us; 1024 x
+// 1024: 3.1 against 3.7), but not in taller ones, whose several workgroups
+// per CU each repeat the activation conversion (11008 x 2048: 6.2 against
+// 5.8 us; 16384 x 2048: 7.6 against 6.4).
+constexpr int64_t kRowsMinSlices = 128;
+constexpr int64_t kRowsShortMinSlices = 32;
+constexpr int64_t kRowsShortMaxRows = 8192;
+__host__ __device__ constexpr bool rows_kernel_takes(int64_t M, int64_t ns) {
+  return QMAT_GEMV_ROWS && ns <= kRowMaxSlices &&
+         (ns >= kRowsMinSlices || (ns >= kRowsShortMinSlices && M <= kRowsShortMaxRows));
+}
+// In a batch a row-kernel job is a launch of its own, so only the longest
+// rows go there (the strip kernel takes many jobs per launch).
+constexpr int64_t kBatchRowsMinSlices = 256;
 
 // How the strip kernel covers a matrix: strips (waves) per workgroup, the
 // row-stride parity and the pair mode.
@@ -1047,7 +1060,7 @@ template <class F, int R, int G, int D, int RD>
 hipError_t launch_fmt(const void* blocks, const float* x, float* y, int64_t M, int64_t K,
                       hipStream_t stream) {
   const int64_t ns = K / 32;
-  if (QMAT_GEMV_ROWS && ns >= QMAT_GEMV_ROWS_MIN_SLICES && ns <= kRowMaxSlices) {
+  if (rows_kernel_takes(M, ns)) {
     constexpr int RR = QMAT_GEMV_ROW_R;
     const int64_t grid = (M + kRowWaves * RR - 1) / (kRowWaves * RR);
     const size_t lds = (size_t)((ns + kWave - 1) / kWave) * kRowSlot;
@@ -1099,8 +1112,8 @@ hipError_t launch_fmt(const void* blocks, const float* x, float* y, int64_t M, i
 #define QMAT_BATCH_D_Q6_K QMAT_GEMV_D_Q6_K
 #endif
 
-// A batch of GEMVs of one format: jobs whose rows take the row-per-wave
-// kernel are launched one by one; the others go through the strip kernel in
+// A batch of GEMVs of one format: jobs with rows of 256 to 512 slices take
+// the row-per-wave kernel, launched one by one; the others go through the strip kernel in
 // launches of up to kBatchJobs jobs, grouped by row-stride parity and by
 // strip shape (pair mode, or the number of strips), so that every workgroup
 // is sized for its own job.
@@ -1144,7 +1157,7 @@ hipError_t launch_batch_fmt(const GemvJob* jobs, int64_t count, hipStream_t stre
     const GemvJob& jb = jobs[i];
     if (jb.M == 0) continue;
     const int64_t ns = jb.K / 32;
-    if (QMAT_GEMV_ROWS && ns >= QMAT_GEMV_ROWS_MIN_SLICES && ns <= kRowMaxSlices) {
+    if (QMAT_GEMV_ROWS && ns >= kBatchRowsMinSlices && ns <= kRowMaxSlices) {
       const hipError_t e = launch_fmt<F, R, G, D, RD>(jb.blocks, jb.x, jb.y, jb.M, jb.K, stream);
       if (e != hipSuccess) return e;
       continue;

@@ -181,9 +181,9 @@ int qmat_quantize(int fmt, const float *W, void *blocks, int64_t rows,
  *   20-bit integer (|X| < 2^19, relative step <= 2^-17.9 of the slice's
  *   largest element), the integer dot products with the codes are exact,
  *   and the per-block results are accumulated in fp32.
- *   Rows of 8192 to 16384 elements are computed by waves that wait, with a
- *   bounded number of polls, for activation records that other waves of
- *   their workgroup publish; a wave whose wait ran out (never expected: the
+ *   Rows of 4096 to 16384 elements (and of 1024 to 4095 when M <= 8192)
+ *   are computed by waves that wait, with a bounded number of polls, for
+ *   activation records that other waves of their workgroup publish; a wave whose wait ran out (never expected: the
  *   records are always published) writes NaN to its rows rather than a
  *   value computed from incomplete records.
  */
@@ -192,9 +192,12 @@ int qmat_gemv(int fmt, const void *blocks, const float *x, float *y,
 
 /*
  * qmat_gemv_batch — many independent decode GEMVs in as few launches as
- *   possible: job i computes jobs[i].y = dequant(W_i) x_i exactly as
- *   qmat_gemv(fmt, jobs[i].blocks, jobs[i].x, jobs[i].y, jobs[i].M,
- *   jobs[i].K, stream) would (same kernels, same bits). [LC05 "带宽决定
+ *   possible: job i computes jobs[i].y = dequant(W_i) x_i with qmat_gemv's
+ *   arithmetic and accuracy bound. Rows shorter than 8192 elements may go
+ *   through a different work split than a single qmat_gemv call of the same
+ *   job, so the fp32 partial sums can be added in another order and the
+ *   last bits can differ from that call's; repeated batch calls give the
+ *   same bits. [LC05 "带宽决定
  *   Decode"]: each weight byte is read once per token; a decode step runs
  *   many small GEMVs (a 0.6B model's layers are 1024 to 3072 wide), whose
  *   cost at one launch each is mostly the launch.

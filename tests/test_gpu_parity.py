@@ -394,9 +394,10 @@ def test_gemv_qwen3_decode_set(q):
 
 
 def test_gemv_batch_qwen3_set(q):
-    """The 196-matrix Qwen3-0.6B-like set as one batch (four launches of up to
-    64 jobs): every output bit-identical to the one-matrix call and within the
-    GEMV bound of the oracle."""
+    """The 196-matrix Qwen3-0.6B-like set as one batch (a few launches of up
+    to 64 jobs): within the GEMV bound of the oracle (every 7th matrix),
+    within 1e-6 of the one-matrix calls (which may add the partial sums in
+    another order), and the same bits on a second batch call."""
     import torch
     for fmt in (0, 1):
         say(f"gemv batch qwen3 set fmt={fmt}")
@@ -414,20 +415,28 @@ def test_gemv_batch_qwen3_set(q):
                 refs.append((i, oracle.gemv(fmt, B, x, M, K)))
         q.gemv_batch(fmt, jobs)
         torch.cuda.synchronize()
+        first = [g.get() for g in guards]
         for i, ref in refs:
-            y = guards[i].get()
-            assert rel_l2(y, ref) <= GEMV_TOL, (fmt, i)
+            assert rel_l2(first[i], ref) <= GEMV_TOL, (fmt, i)
         for i, (dB, dx) in enumerate(dev):
             M, K = jobs[i][3], jobs[i][4]
             one = gpu_gemv(q, fmt, dB, dx, M, K)
-            assert np.array_equal(guards[i].get().view(np.uint32), one.view(np.uint32)), (fmt, i)
+            assert rel_l2(first[i], one) <= 1e-6, (fmt, i, rel_l2(first[i], one))
+        say(f"gemv batch qwen3 set fmt={fmt}: second call")
+        for g in guards:
+            g.out.fill_(float("nan"))
+        q.gemv_batch(fmt, jobs)
+        torch.cuda.synchronize()
+        for i, g in enumerate(guards):
+            assert np.array_equal(g.get().view(np.uint32), first[i].view(np.uint32)), (fmt, i)
 
 
 @pytest.mark.parametrize("fmt", [0, 1, 2, 3])
 def test_gemv_batch_mixed(q, fmt):
     """Jobs of every kind in one call: rows for the row-per-wave kernel, odd
     row strides, a single row, M = 0 and K = 0 jobs, and more than 64 jobs
-    (several launches); each output equals the one-matrix call's bits."""
+    (several launches); each output within 1e-6 of the one-matrix call, the
+    same bits on a second call."""
     import torch
     rng = np.random.default_rng(1300 + fmt)
     if fmt < 2:
@@ -451,12 +460,22 @@ def test_gemv_batch_mixed(q, fmt):
         dev.append((dB, dx))
     q.gemv_batch(fmt, jobs)
     torch.cuda.synchronize()
+    first = [g.get() for g in guards]
     for i, (M, K) in enumerate(shapes):
         if M == 0:
             continue
-        got = guards[i].get()
         one = gpu_gemv(q, fmt, dev[i][0], dev[i][1], M, K)
-        assert np.array_equal(got.view(np.uint32), one.view(np.uint32)), (fmt, i, M, K)
+        if K == 0:
+            assert np.array_equal(first[i], one), (fmt, i)
+        else:
+            assert rel_l2(first[i], one) <= 1e-6, (fmt, i, M, K, rel_l2(first[i], one))
+    for g in guards:
+        g.out.fill_(float("nan"))
+    q.gemv_batch(fmt, jobs)
+    torch.cuda.synchronize()
+    for i, (M, K) in enumerate(shapes):
+        if M:
+            assert np.array_equal(guards[i].get().view(np.uint32), first[i].view(np.uint32)), i
 
 
 @pytest.mark.parametrize("orient", [0, 1])
