@@ -877,12 +877,13 @@ __device__ __forceinline__ void get_rec(const uint8_t* slot, int l, XByte& xp, b
   xp.sxh[1] = sum ? reinterpret_cast<const int32_t*>(slot + 6656)[l] : 0;
 }
 
+// The body for workgroup wg of one matrix (rows from wg * kRowWaves * R).
 template <class F, int R, int kD, bool kOdd>
-__global__ __launch_bounds__(kRowWaves * kWave) void gemv_rows_kernel(
-    const uint8_t* __restrict__ B, const float* __restrict__ x, float* __restrict__ y,
-    int64_t M, int K) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t slots[];
-  __shared__ int ready[8];  // strip s's records are in slot s when ready[s] != 0
+__device__ __forceinline__ void gemv_rows(const uint8_t* __restrict__ B,
+                                          const float* __restrict__ x, float* __restrict__ y,
+                                          int64_t M, int K, int64_t wg, uint8_t* slots,
+                                          int* ready) {
+  // strip s's records are in slot s when ready[s] != 0
   typedef typename F::XP XP;
   constexpr uint32_t kOut = 0x80000000u;  // an offset past the end of any row
   const int lane = threadIdx.x & 63;
@@ -890,7 +891,7 @@ __global__ __launch_bounds__(kRowWaves * kWave) void gemv_rows_kernel(
   const int ns = K >> 5;
   const int nstrips = (ns + kWave - 1) / kWave;
   const int64_t rb = F::row_bytes(K);
-  const int64_t m0 = ((int64_t)blockIdx.x * kRowWaves + wv) * R;  // this wave's first row
+  const int64_t m0 = (wg * kRowWaves + wv) * R;  // this wave's first row
   // with an odd row stride, row m starts at 2 (m & 1) mod 4; a row past M
   // re-reads the last row of the same parity (M >= 2 then)
   __amdgpu_buffer_rsrc_t rrs[R];
@@ -999,6 +1000,29 @@ __global__ __launch_bounds__(kRowWaves * kWave) void gemv_rows_kernel(
     y[m0 + r] = lost ? __builtin_nanf("") : sum;
 }
 
+template <class F, int R, int kD, bool kOdd>
+__global__ __launch_bounds__(kRowWaves * kWave) void gemv_rows_kernel(
+    const uint8_t* __restrict__ B, const float* __restrict__ x, float* __restrict__ y,
+    int64_t M, int K) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t slots[];
+  __shared__ int ready[8];
+  gemv_rows<F, R, kD, kOdd>(B, x, y, M, K, blockIdx.x, slots, ready);
+}
+
+// Many GEMVs of the row kernel's shape in one launch: job blockIdx.y, its
+// workgroup blockIdx.x (the jobs of a launch share the row-stride parity
+// and the number of strips, which sizes the LDS); workgroups past a job's
+// rows end at once.
+template <class F, int R, int kD, bool kOdd>
+__global__ __launch_bounds__(kRowWaves * kWave) void gemv_rows_batch_kernel(GemvBatchArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t slots[];
+  __shared__ int ready[8];
+  const int j = blockIdx.y;
+  const int64_t M = a.M[j];
+  if ((int64_t)blockIdx.x * kRowWaves * R >= M) return;  // the whole workgroup
+  gemv_rows<F, R, kD, kOdd>(a.B[j], a.x[j], a.y[j], M, a.K[j], blockIdx.x, slots, ready);
+}
+
 #ifndef QMAT_GEMV_CFG
 // rows per group, groups per workgroup, groups in flight
 #define QMAT_GEMV_R_Q4_0 2
@@ -1032,8 +1056,10 @@ __host__ __device__ constexpr bool rows_kernel_takes(int64_t M, int64_t ns) {
   return QMAT_GEMV_ROWS && ns <= kRowMaxSlices &&
          (ns >= kRowsMinSlices || (ns >= kRowsShortMinSlices && M <= kRowsShortMaxRows));
 }
-// In a batch a row-kernel job is a launch of its own, so only the longest
-// rows go there (the strip kernel takes many jobs per launch).
+// In a batch the row kernel takes only rows of 256 slices and more: on the
+// Qwen3-like set (rows of 32 to 96 slices) batched row-kernel launches took
+// 137.6 us against the strip kernel's 67.6 (Q4_0), each 16-row workgroup
+// converting the activations for one or two strips of work per wave.
 constexpr int64_t kBatchRowsMinSlices = 256;
 
 // How the strip kernel covers a matrix: strips (waves) per workgroup, the
@@ -1112,15 +1138,17 @@ hipError_t launch_fmt(const void* blocks, const float* x, float* y, int64_t M, i
 #define QMAT_BATCH_D_Q6_K QMAT_GEMV_D_Q6_K
 #endif
 
-// A batch of GEMVs of one format: jobs with rows of 256 to 512 slices take
-// the row-per-wave kernel, launched one by one; the others go through the strip kernel in
-// launches of up to kBatchJobs jobs, grouped by row-stride parity and by
-// strip shape (pair mode, or the number of strips), so that every workgroup
-// is sized for its own job.
+// A batch of GEMVs of one format, in launches of up to kBatchJobs jobs
+// grouped so that every workgroup is sized for its own job: jobs with rows
+// of 256 to 512 slices go to the row kernel, grouped by row-stride parity
+// and strip count; the others to the strip kernel, grouped by parity and
+// workgroup shape (pair mode, or the number of strips).
 template <class F, int R, int G, int D, int RD>
 hipError_t launch_batch_fmt(const GemvJob* jobs, int64_t count, hipStream_t stream) {
   constexpr int RG = R * G;
-  constexpr int kShapes = kMaxStrips + 1;  // 0: pair mode, w: w strips
+  constexpr int RR = QMAT_GEMV_ROW_R;
+  constexpr int kShapes = kMaxStrips + 1;  // strip kernel: 0 pair mode, w: w strips
+  constexpr int kRowShapes = kRowMaxSlices / kWave + 1;  // row kernel: strips
   struct Group {
     GemvBatchArgs a;
     int n;
@@ -1128,7 +1156,10 @@ hipError_t launch_batch_fmt(const GemvJob* jobs, int64_t count, hipStream_t stre
   };
   static_assert(sizeof(Group) < 4096, "batch group");
   Group grp[2][kShapes];
+  Group rgrp[2][kRowShapes];
   for (auto& go : grp)
+    for (auto& g : go) g.n = 0, g.tiles = 0;
+  for (auto& go : rgrp)
     for (auto& g : go) g.n = 0, g.tiles = 0;
   auto flush = [&](int o, int w) -> hipError_t {
     Group& g = grp[o][w];
@@ -1153,37 +1184,65 @@ hipError_t launch_batch_fmt(const GemvJob* jobs, int64_t count, hipStream_t stre
     g.tiles = 0;
     return hipGetLastError();
   };
-  for (int64_t i = 0; i < count; ++i) {
-    const GemvJob& jb = jobs[i];
-    if (jb.M == 0) continue;
-    const int64_t ns = jb.K / 32;
-    if (QMAT_GEMV_ROWS && ns >= kBatchRowsMinSlices && ns <= kRowMaxSlices) {
-      const hipError_t e = launch_fmt<F, R, G, D, RD>(jb.blocks, jb.x, jb.y, jb.M, jb.K, stream);
-      if (e != hipSuccess) return e;
-      continue;
-    }
-    const StripShape sh = strip_shape<F>(jb.M, jb.K);
-    const int o = sh.odd ? 1 : 0;
-    const int w = sh.pair ? 0 : sh.waves;
-    Group& g = grp[o][w];
+  auto flush_rows = [&](int o, int st) -> hipError_t {
+    Group& g = rgrp[o][st];
+    if (g.n == 0) return hipSuccess;
+    const dim3 grid((unsigned)g.tiles, (unsigned)g.n);
+    const size_t lds = (size_t)st * kRowSlot;
+    if (o)
+      hipLaunchKernelGGL((gemv_rows_batch_kernel<F, RR, RD, true>), grid,
+                         dim3(kRowWaves * kWave), lds, stream, g.a);
+    else
+      hipLaunchKernelGGL((gemv_rows_batch_kernel<F, RR, RD, false>), grid,
+                         dim3(kRowWaves * kWave), lds, stream, g.a);
+    g.n = 0;
+    g.tiles = 0;
+    return hipGetLastError();
+  };
+  auto add = [](Group& g, const GemvJob& jb, int64_t tiles) {
     const int k = g.n++;
     g.a.B[k] = static_cast<const uint8_t*>(jb.blocks);
     g.a.x[k] = jb.x;
     g.a.y[k] = jb.y;
     g.a.M[k] = jb.M;
     g.a.K[k] = (int)jb.K;
-    const int64_t t = (jb.M + sh.rows(RG) - 1) / sh.rows(RG);
-    g.tiles = t > g.tiles ? t : g.tiles;
+    g.tiles = tiles > g.tiles ? tiles : g.tiles;
+  };
+  for (int64_t i = 0; i < count; ++i) {
+    const GemvJob& jb = jobs[i];
+    if (jb.M == 0) continue;
+    const int64_t ns = jb.K / 32;
+    if (QMAT_GEMV_ROWS && ns >= kBatchRowsMinSlices && ns <= kRowMaxSlices) {
+      const int o = ((F::row_bytes(jb.K) & 2) != 0 && jb.M > 1) ? 1 : 0;  // rows start 2 mod 4
+      const int st = (int)((ns + kWave - 1) / kWave);
+      Group& g = rgrp[o][st];
+      add(g, jb, (jb.M + kRowWaves * RR - 1) / (kRowWaves * RR));
+      if (g.n == kBatchJobs) {
+        const hipError_t e = flush_rows(o, st);
+        if (e != hipSuccess) return e;
+      }
+      continue;
+    }
+    const StripShape sh = strip_shape<F>(jb.M, jb.K);
+    const int o = sh.odd ? 1 : 0;
+    const int w = sh.pair ? 0 : sh.waves;
+    Group& g = grp[o][w];
+    add(g, jb, (jb.M + sh.rows(RG) - 1) / sh.rows(RG));
     if (g.n == kBatchJobs) {
       const hipError_t e = flush(o, w);
       if (e != hipSuccess) return e;
     }
   }
-  for (int o = 0; o < 2; ++o)
+  for (int o = 0; o < 2; ++o) {
+    for (int st = 0; st < kRowShapes; ++st) {
+      const hipError_t e = flush_rows(o, st);
+      if (e != hipSuccess) return e;
+    }
     for (int w = 0; w < kShapes; ++w) {
       const hipError_t e = flush(o, w);
       if (e != hipSuccess) return e;
     }
+  }
   return hipSuccess;
 }
 

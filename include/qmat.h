@@ -206,12 +206,11 @@ int qmat_gemv(int fmt, const void *blocks, const float *x, float *y,
  *   arguments, all of them before anything is enqueued; the first failure
  *   is returned. Jobs with M == 0 are skipped. Outputs must not overlap each
  *   other or any input.
- *   Jobs whose rows hold 8192 to 16384 elements take one launch each; the
- *   others are grouped, up to 64 jobs per launch, by the parity of their row
- *   stride (rows starting at 2 mod 4 or not) and by the shape of their
- *   workgroups (rows of at most 1024 elements, or the number of 2048-element
- *   strips a row spans), so a call makes at most a few launches per shape
- *   present plus one per long-row job. The launches are enqueued in order
+ *   Jobs are grouped, up to 64 per launch, by the parity of their row
+ *   stride (rows starting at 2 mod 4 or not), by kernel (rows of 8192 to
+ *   16384 elements, or shorter) and by the shape of their workgroups (rows
+ *   of at most 1024 elements, or the number of 2048-element strips a row
+ *   spans), so a call makes at most a few launches per shape present. The launches are enqueued in order
  *   on stream; the host returns once they are enqueued.
  */
 typedef struct qmat_gemv_job {

@@ -396,7 +396,7 @@ def test_gemv_qwen3_decode_set(q):
 def test_gemv_batch_qwen3_set(q):
     """The 196-matrix Qwen3-0.6B-like set as one batch (a few launches of up
     to 64 jobs): within the GEMV bound of the oracle (every 7th matrix),
-    within 1e-6 of the one-matrix calls (which may add the partial sums in
+    within 1e-5 of the one-matrix calls (which may add the partial sums in
     another order), and the same bits on a second batch call."""
     import torch
     for fmt in (0, 1):
@@ -421,7 +421,7 @@ def test_gemv_batch_qwen3_set(q):
         for i, (dB, dx) in enumerate(dev):
             M, K = jobs[i][3], jobs[i][4]
             one = gpu_gemv(q, fmt, dB, dx, M, K)
-            assert rel_l2(first[i], one) <= 1e-6, (fmt, i, rel_l2(first[i], one))
+            assert rel_l2(first[i], one) <= 1e-5, (fmt, i, rel_l2(first[i], one))
         say(f"gemv batch qwen3 set fmt={fmt}: second call")
         for g in guards:
             g.out.fill_(float("nan"))
@@ -435,23 +435,30 @@ def test_gemv_batch_qwen3_set(q):
 def test_gemv_batch_mixed(q, fmt):
     """Jobs of every kind in one call: rows for the row-per-wave kernel, odd
     row strides, a single row, M = 0 and K = 0 jobs, and more than 64 jobs
-    (several launches); each output within 1e-6 of the one-matrix call, the
-    same bits on a second call."""
+    (several launches); each output within the GEMV bound of the oracle and
+    close to the one-matrix call (which may add the partial sums in another
+    order: a single row's sum can differ by a few units in its last place),
+    the same bits on a second call."""
     import torch
     rng = np.random.default_rng(1300 + fmt)
+    # rows of 256-512 slices (the batched row kernel: several jobs per
+    # launch, two strip counts, a single row, ragged workgroups)
+    long_rows = [(70, 11008), (20, 8192), (33, 16384), (1, 8192), (17, 256 * 33)]
     if fmt < 2:
-        shapes = [(70, 11008), (33, 32 * 37), (1, 32 * 37), (0, 1024), (19, 0), (129, 4096),
-                  (200, 32 * 345)] + [(int(rng.integers(1, 90)), 32 * int(rng.integers(1, 200)))
-                                      for _ in range(70)]
+        shapes = long_rows + [(33, 32 * 37), (1, 32 * 37), (0, 1024), (19, 0), (129, 4096),
+                              (200, 32 * 345), (9, 32 * 257)] + \
+                 [(int(rng.integers(1, 90)), 32 * int(rng.integers(1, 200))) for _ in range(70)]
     else:
-        shapes = [(70, 11008), (9, 256 * 9), (1, 256 * 9), (0, 1024), (19, 0), (129, 4096)] + \
+        shapes = long_rows + [(9, 256 * 9), (1, 256 * 9), (0, 1024), (19, 0), (129, 4096)] + \
                  [(int(rng.integers(1, 90)), 256 * int(rng.integers(1, 40))) for _ in range(70)]
     say(f"gemv batch mixed fmt={fmt}: {len(shapes)} jobs")
-    jobs, guards, dev = [], [], []
+    jobs, guards, dev, refs = [], [], [], []
     for M, K in shapes:
         W = rng.normal(0, 0.02, (M, K)).astype(np.float32)
         x = rng.normal(0, 1, K).astype(np.float32)
-        dB = dev_tensor(oracle.quantize(fmt, W)) if M * K else torch.empty(
+        Bq = oracle.quantize(fmt, W) if M * K else None
+        refs.append(oracle.gemv(fmt, Bq, x, M, K) if M * K else np.zeros(M))
+        dB = dev_tensor(Bq) if M * K else torch.empty(
             M * oracle.row_bytes(fmt, K), dtype=torch.uint8, device="cuda")
         dx = dev_tensor(x) if K else torch.empty(0, dtype=torch.float32, device="cuda")
         g = Guarded((M,))
@@ -466,9 +473,10 @@ def test_gemv_batch_mixed(q, fmt):
             continue
         one = gpu_gemv(q, fmt, dev[i][0], dev[i][1], M, K)
         if K == 0:
-            assert np.array_equal(first[i], one), (fmt, i)
+            assert np.array_equal(first[i], one) and not first[i].any(), (fmt, i)
         else:
-            assert rel_l2(first[i], one) <= 1e-6, (fmt, i, M, K, rel_l2(first[i], one))
+            assert rel_l2(first[i], refs[i]) <= GEMV_TOL, (fmt, i, M, K)
+            assert rel_l2(first[i], one) <= 1e-4, (fmt, i, M, K, rel_l2(first[i], one))
     for g in guards:
         g.out.fill_(float("nan"))
     q.gemv_batch(fmt, jobs)
