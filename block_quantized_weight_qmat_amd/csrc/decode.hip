@@ -68,9 +68,10 @@ struct DecX {
   static constexpr int kStage = NT * kXRowBytes;
 };
 
-// Per wave: a ring of kDepth stages (weights and tokens). As many waves as 160 KB of LDS allows with a ring of
-// at least two stages (16, 12 or 8: the waves hide each other's LDS and
-// matrix-core latency), each with the deepest ring that then fits.
+// Per wave: a ring of kDepth stages (weights and tokens). As many waves as
+// 160 KB of LDS allows with a ring of at least two stages (16, 12 or 8: the
+// waves hide each other's LDS and matrix-core latency), each with the
+// deepest ring that then fits.
 template <bool kQ4, int NT>
 struct DecRing {
   static constexpr int kStage = DecW<kQ4>::kStage + DecX<NT>::kStage;
