@@ -94,7 +94,13 @@ GEMV_EXTRA = [("gemv_q4_0_1024x1024", 0, "gemv_1024"),
               ("gemv_q4_k_4096x11008_spread", 2, "q4k_1")]
 # the Qwen3-like set as one qmat_gemv_batch call, and as 196 qmat_gemv calls
 QWEN3_OPS = ["qwen3_pass_q4_0", "qwen3_pass_q8_0", "qwen3_launches_q4_0", "qwen3_launches_q8_0"]
+# prompts of a few dozen to a few hundred tokens: the same layer through
+# qmat_gemm (128 x 64 tiles, or the decode batch up to 48 tokens) and through
+# qmat_gemm_ws (tiles also split along K)
+MID_NS = (17, 64, 192)
+MID_OPS = [f"gemm_q4_0_n{n}" for n in MID_NS] + [f"gemm_ws_q4_0_n{n}" for n in MID_NS]
 EXTRA_OPS = ([f"decode_q4_0_n{n}" for n in DECODE_NS] + [g[0] for g in GEMV_EXTRA] + QWEN3_OPS
+             + MID_OPS
              + ["quantize_q6_k", "gemv_q6_k", "gemm_q8_0", "gemm_q4_k", "gemm_q6_k",
                 "quantize_act_q8_0_warm",
                 "kv_write_q4_0", "kv_write_q8_0"])
@@ -421,7 +427,7 @@ def main():
 
     need = lambda prefix: any(o.startswith(prefix) for o in only)
     cold = {f: copies(packed[f], COLD_BYTES) if need("gemv_" + f) or need("decode_" + f)
-            or need("gemm_" + f) else [packed[f]] for f in fmts}
+            or need("gemm_" + f) or need("gemm_ws_" + f) else [packed[f]] for f in fmts}
     W_rot = [Wf] + ([Wf.clone()] if need("quantize_q") else [])
     X_rot = [torch.from_numpy(X_np).to(dev) for _ in range(12 if need("quantize_act") else 1)]
     q_out = {f: torch.empty_like(packed[f]) for f in fmts}
@@ -430,6 +436,11 @@ def main():
     Y = torch.empty((N, M), dtype=torch.float32, device=dev)
     Xq_dec = {n: binding.quantize(1, X_rot[0][:n].contiguous()) for n in DECODE_NS}
     Y_dec = {n: torch.empty((n, M), dtype=torch.float32, device=dev) for n in DECODE_NS}
+    mid = [n for n in MID_NS if f"gemm_q4_0_n{n}" in only or f"gemm_ws_q4_0_n{n}" in only]
+    Xq_mid = {n: binding.quantize(1, X_rot[0][:n].contiguous()) for n in mid}
+    Y_mid = {n: torch.empty((n, M), dtype=torch.float32, device=dev) for n in mid}
+    ws_mid = {n: torch.empty(binding.gemm_workspace_bytes(0, M, K, n), dtype=torch.uint8,
+                             device=dev) for n in mid}
     src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
     # the other decode workloads, packed on the GPU, each rotated over copies
@@ -522,6 +533,12 @@ def main():
     for n in DECODE_NS:
         table[f"decode_q4_0_n{n}"] = lambda s, n=n: binding.gemm(
             0, cold["q4_0"][s % len(cold["q4_0"])], Xq_dec[n], M, K, n, out=Y_dec[n])
+    for n in mid:
+        table[f"gemm_q4_0_n{n}"] = lambda s, n=n: binding.gemm(
+            0, cold["q4_0"][s % len(cold["q4_0"])], Xq_mid[n], M, K, n, out=Y_mid[n])
+        table[f"gemm_ws_q4_0_n{n}"] = lambda s, n=n: binding.gemm_ws(
+            0, cold["q4_0"][s % len(cold["q4_0"])], Xq_mid[n], M, K, n, out=Y_mid[n],
+            workspace=ws_mid[n])
     table["copy"] = lambda s: dst.copy_(src)
     ops = [(name, table[name]) for name in only if name not in EXTRA_OPS]
     extra = [(name, table[name]) for name in only if name in EXTRA_OPS]
@@ -589,6 +606,15 @@ def main():
             gbs = dec_bytes[n] / us / 1e3
             kernels[name] = {"us": us, "bytes": dec_bytes[n], "GB/s": gbs, "bound": "hbm",
                              "frac": gbs / HBM_PEAK_GBS, "tokens_per_s": n / us * 1e6}
+        elif name in MID_OPS:
+            n = int(name.rsplit("_n", 1)[1])
+            ops_n = 2 * M * K * n
+            tops = ops_n / us / 1e6
+            splits = ws_mid[n].numel() // (4 * n * M) + 1 if name.startswith("gemm_ws") else 1
+            kernels[name] = {"us": us, "tokens": n, "int8_ops": ops_n, "TOPS": tops,
+                             "bound": "mfma", "frac": tops / INT8_PEAK_TOPS,
+                             "path": "decode batch" if n <= 48 and splits == 1 else
+                             f"tiles, {splits} K range(s)"}
         elif name.startswith("gemm_"):
             tops = gemm_ops / us / 1e6
             kernels[name] = {"us": us, "int8_ops": gemm_ops, "TOPS": tops, "bound": "mfma",
@@ -623,7 +649,7 @@ def main():
     # nominal non-packed rate
     fma_rate = peaks["fp32_fma_TFLOPs_beside_mfma"] if peaks else FP32_FMA_TFLOPS
     for name, kv in kernels.items():
-        if name.startswith("gemm_"):
+        if name.startswith("gemm_") and name not in MID_OPS:
             flops = 2 * GEMM_VALU_FMAS[name[5:]] * M * N * (K // 32)
             ceil_us = flops / fma_rate / 1e6
             kv.update({"valu_fma_flops": flops, "valu_ceiling_us": ceil_us,

@@ -7,7 +7,7 @@ The compute lives in the HIP library ``libqmat.so`` (C ABI in
 """
 from __future__ import annotations
 
-__all__ = ["quantize", "gemv", "gemv_batch", "gemv_jobs", "gemm", "prefill", "prefill_noalloc", "kv_write",
+__all__ = ["quantize", "gemv", "gemv_batch", "gemv_jobs", "gemm", "gemm_ws", "gemm_workspace_bytes", "prefill", "prefill_noalloc", "kv_write",
            "block_elems", "block_bytes", "row_bytes", "noalloc_scratch_bytes",
            "Q4_0", "Q8_0", "Q4_K", "Q6_K", "FORMATS", "QmatError", "library_path"]
 

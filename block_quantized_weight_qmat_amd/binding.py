@@ -57,6 +57,10 @@ def load_library():
     lib.qmat_gemv.restype = i32
     lib.qmat_gemm.argtypes = [i32, p, p, p, i64, i64, i64, p]
     lib.qmat_gemm.restype = i32
+    lib.qmat_gemm_workspace_bytes.argtypes = [i32, i64, i64, i64]
+    lib.qmat_gemm_workspace_bytes.restype = i64
+    lib.qmat_gemm_ws.argtypes = [i32, p, p, p, i64, i64, i64, p, i64, p]
+    lib.qmat_gemm_ws.restype = i32
     lib.qmat_prefill.argtypes = [i32, p, p, p, p, i64, i64, i64, p]
     lib.qmat_prefill.restype = i32
     lib.qmat_kv_write.argtypes = [i32, p, p, p, i64, i64, i64, i64, p]
@@ -195,6 +199,42 @@ def gemm(fmt, blocks: torch.Tensor, Xq: torch.Tensor, M: int, K: int, N: int,
         raise ValueError("out must hold N*M values")
     _check("qmat_gemm", load_library().qmat_gemm(
         f, blocks.data_ptr(), Xq.data_ptr(), out.data_ptr(), M, K, N, _stream(Xq)))
+    return out
+
+
+def gemm_workspace_bytes(fmt, M: int, K: int, N: int) -> int:
+    """Workspace bytes gemm_ws needs for this product (0: none)."""
+    n = int(load_library().qmat_gemm_workspace_bytes(_fmt(fmt), M, K, N))
+    if n < 0:
+        raise ValueError(f"invalid gemm shape M={M} K={K} N={N} for format {fmt}")
+    return n
+
+
+def gemm_ws(fmt, blocks: torch.Tensor, Xq: torch.Tensor, M: int, K: int, N: int,
+            out: torch.Tensor | None = None,
+            workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """gemm with a workspace, so that a product of few tiles is also split
+    along K; a workspace of gemm_workspace_bytes() bytes is allocated when
+    none is given."""
+    f = _fmt(fmt)
+    _gpu(blocks, "blocks", torch.uint8)
+    _gpu(Xq, "Xq", torch.uint8)
+    if blocks.numel() != M * row_bytes(f, K) or Xq.numel() != N * row_bytes(Q8_0, K):
+        raise ValueError("blocks or Xq does not match M, K, N")
+    if out is None:
+        out = torch.empty((N, M), dtype=torch.float32, device=Xq.device)
+    _gpu(out, "out", torch.float32)
+    if out.numel() != N * M:
+        raise ValueError("out must hold N*M values")
+    need = gemm_workspace_bytes(f, M, K, N)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=Xq.device)
+    if workspace is not None:
+        _gpu(workspace, "workspace", torch.uint8)
+    wp = workspace.data_ptr() if workspace is not None else None
+    wn = workspace.numel() if workspace is not None else 0
+    _check("qmat_gemm_ws", load_library().qmat_gemm_ws(
+        f, blocks.data_ptr(), Xq.data_ptr(), out.data_ptr(), M, K, N, wp, wn, _stream(Xq)))
     return out
 
 

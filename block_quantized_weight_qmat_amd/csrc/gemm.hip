@@ -642,13 +642,54 @@ __device__ __forceinline__ i32x16 magic_vec() {
   return c;
 }
 
+// K split. A product whose tiles cannot fill the GPU is also divided along
+// K into nsplit ranges of whole stages (pairs of stages for Q6_K-style, so
+// that a range starts at an even stage and keeps the stage parity its
+// 210-byte alignment cases follow). Linear tile index = (split, m-tile,
+// n-tile); each range's partial product is written whole (range 0 into Y),
+// and a second kernel adds the others into Y in range order.
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+  const uint64_t u = (uint64_t)v;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+struct SplitTile {
+  int64_t tm, tn;
+  int split, stage0, nb, nstage;
+};
+template <int FMT>
+__device__ __forceinline__ SplitTile split_tile(int64_t tile, int64_t tiles_n, int64_t tps,
+                                                int nsplit, int nbk) {
+  // every value is wave-uniform: readfirstlane keeps them in scalar
+  // registers (the divisions themselves are expanded into vector code)
+  SplitTile t;
+  // (a split product has at most 2^24 tiles in all)
+  t.split = nsplit > 1 ? __builtin_amdgcn_readfirstlane((int)((uint32_t)tile / (uint32_t)tps)) : 0;
+  const int64_t r = tile - (int64_t)t.split * tps;
+  t.tm = uniform64(r / tiles_n);
+  t.tn = r - t.tm * tiles_n;
+  constexpr int kUnit = FMT == kFmtQ6_K ? 2 : 1;  // stages per unit of a range
+  const int nst = (nbk + kKB - 1) / kKB;
+  const int units = (nst + kUnit - 1) / kUnit;  // < 2^16: K <= 2^24
+  const int u0 = t.split * units / nsplit;
+  const int u1 = (t.split + 1) * units / nsplit;
+  t.stage0 = __builtin_amdgcn_readfirstlane(u0 * kUnit);
+  const int b0 = t.stage0 * kKB, b1 = min(nbk, u1 * kUnit * kKB);
+  t.nb = __builtin_amdgcn_readfirstlane(b1 - b0);
+  t.nstage = (t.nb + kKB - 1) / kKB;
+  return t;
+}
+
 // Warp-specialized kernel: load_threads_of(FMT) loader threads fill the LDS stages,
 // threads_of(FMT) compute threads share 32 x (32 kNT) wave tiles ks_of(FMT)
 // to a tile.
 template <int FMT>
 __global__ __launch_bounds__(threads_of(FMT) + load_threads_of(FMT)) void gemm_kernel(
     const uint8_t* __restrict__ Wb, const uint8_t* __restrict__ Xb, float* __restrict__ Y,
-    int64_t M, int K, int64_t N, int64_t tiles_n, int64_t ntiles) {
+    float* __restrict__ part, int64_t M, int K, int64_t N, int64_t tiles_n, int64_t tps,
+    int nsplit) {
   __shared__ __attribute__((aligned(16))) Stage st[2];
   typedef TileLoader<FMT, load_threads_of(FMT)> TL;
   constexpr int kKS = ks_of(FMT), kPer = kKB / kKS, kThreads = threads_of(FMT);
@@ -663,11 +704,11 @@ __global__ __launch_bounds__(threads_of(FMT) + load_threads_of(FMT)) void gemm_k
   const int wv = tid >> 6;
   const int half = lane >> 5;
   const int l32 = lane & 31;
-  const int nb = K >> 5;  // 32-element blocks along K
-  const int nstage = (nb + kKB - 1) / kKB;
+  const int nbk = K >> 5;  // 32-element blocks along K
   const int64_t wrb = FMT == kFmtQ4_K || FMT == kFmtQ6_K ? (int64_t)(K >> 8) * TL::wbytes
-                                                          : (int64_t)nb * TL::wbytes;
-  const int64_t xrb = (int64_t)nb * 34;
+                                                          : (int64_t)nbk * TL::wbytes;
+  const int64_t xrb = (int64_t)nbk * 34;
+  const int64_t ntiles = tps * nsplit;
   const int64_t lin = first_tile(ntiles);
 
   // Each role runs its own tile loop (so that neither keeps the other's
@@ -675,12 +716,14 @@ __global__ __launch_bounds__(threads_of(FMT) + load_threads_of(FMT)) void gemm_k
   // before the first stage, one per stage and one after the last.
   if (loader) {
     for (int64_t tile = lin; tile < ntiles; tile += gridDim.x) {
-      const int64_t tm = tile / tiles_n, tn = tile - tm * tiles_n;
-      const int64_t m0 = tm * kBM, n0 = tn * kBN;
+      const SplitTile t = split_tile<FMT>(tile, tiles_n, tps, nsplit, nbk);
+      const int64_t m0 = t.tm * kBM, n0 = t.tn * kBN;
+      const int nb = t.nb, nstage = t.nstage;
       TL ld;
       ld.setup(M, N, m0, n0, wrb, xrb, tid, nb);
-      const __amdgpu_buffer_rsrc_t wrs = make_rsrc(Wb + m0 * wrb, (M - m0) * wrb);
-      const __amdgpu_buffer_rsrc_t xrs = make_rsrc(Xb + n0 * xrb, (N - n0) * xrb);
+      const int64_t wo = (int64_t)t.stage0 * TL::stage_wbytes, xo = (int64_t)t.stage0 * (kKB * 34);
+      const __amdgpu_buffer_rsrc_t wrs = make_rsrc(Wb + m0 * wrb + wo, (M - m0) * wrb - wo);
+      const __amdgpu_buffer_rsrc_t xrs = make_rsrc(Xb + n0 * xrb + xo, (N - n0) * xrb - xo);
       // Register set k holds stages k, k + kDepth, ...: set indices stay
       // compile-time constants by stepping kDepth stages per iteration.
       typename TL::Regs regs[kDepth];
@@ -721,8 +764,11 @@ __global__ __launch_bounds__(threads_of(FMT) + load_threads_of(FMT)) void gemm_k
     const int ks = wv / kTileWaves, tw = wv % kTileWaves;
     const int wm = tw % kRT, wn0 = (tw / kRT) * kNT;
     for (int64_t tile = lin; tile < ntiles; tile += gridDim.x) {
-      const int64_t tm = tile / tiles_n, tn = tile - tm * tiles_n;
-      const int64_t m0 = tm * kBM, n0 = tn * kBN;
+      const SplitTile t = split_tile<FMT>(tile, tiles_n, tps, nsplit, nbk);
+      const int64_t m0 = t.tm * kBM, n0 = t.tn * kBN;
+      const int nb = t.nb, nstage = t.nstage;
+      // the first K range writes Y, range s > 0 its own partial product
+      float* __restrict__ out = t.split == 0 ? Y : part + (int64_t)(t.split - 1) * N * M;
       float acc[kNT][16];
 #pragma unroll
       for (int t = 0; t < kNT; ++t)
@@ -761,10 +807,10 @@ __global__ __launch_bounds__(threads_of(FMT) + load_threads_of(FMT)) void gemm_k
 #pragma unroll
               for (int i = 0; i < 16; ++i) acc[t][i] += p[(t * 16 + i) * kWave];
           }
-          store_tile<kNT>(Y, M, N, m0, n0, wm, wn0, l32, half, acc);
+          store_tile<kNT>(out, M, N, m0, n0, wm, wn0, l32, half, acc);
         }
       } else {
-        store_tile<kNT>(Y, M, N, m0, n0, wm, wn0, l32, half, acc);
+        store_tile<kNT>(out, M, N, m0, n0, wm, wn0, l32, half, acc);
       }
       __syncthreads();
     }
@@ -772,27 +818,82 @@ __global__ __launch_bounds__(threads_of(FMT) + load_threads_of(FMT)) void gemm_k
 }
 
 constexpr int64_t kMaxGrid = 1 << 24;
+static_assert(kBM == split::kTileM && kBN == split::kTileN && kKB == split::kStageBlocks,
+              "the K-split policy assumes this kernel's tile and stage sizes");
 #ifndef QMAT_GEMM_SMALL_N
 #define QMAT_GEMM_SMALL_N 48
 #endif
 constexpr int64_t kSmallN = QMAT_GEMM_SMALL_N;
+// Y += part[0] + part[1] + ... + part[kParts - 1] (partial products of
+// count values each), added in that order for every element. All loads of
+// an element are issued before the first add.
+template <int kParts>
+__global__ __launch_bounds__(256) void splitk_add_kernel(float* __restrict__ Y,
+                                                         const float* __restrict__ part,
+                                                         int64_t count) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  if ((count & 3) == 0) {
+    const int64_t n4 = count >> 2;
+    f32x4* y4 = reinterpret_cast<f32x4*>(Y);
+    const f32x4* p4 = reinterpret_cast<const f32x4*>(part);
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
+      f32x4 a[kParts];
+#pragma unroll
+      for (int k = 0; k < kParts; ++k) a[k] = __builtin_nontemporal_load(p4 + k * n4 + i);
+      f32x4 v = y4[i];
+#pragma unroll
+      for (int k = 0; k < kParts; ++k) {
+        v[0] += a[k][0];
+        v[1] += a[k][1];
+        v[2] += a[k][2];
+        v[3] += a[k][3];
+      }
+      y4[i] = v;
+    }
+  } else {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += stride) {
+      float a[kParts];
+#pragma unroll
+      for (int k = 0; k < kParts; ++k) a[k] = part[k * count + i];
+      float v = Y[i];
+#pragma unroll
+      for (int k = 0; k < kParts; ++k) v += a[k];
+      Y[i] = v;
+    }
+  }
+}
+
+template <int kParts>
+hipError_t launch_add(float* Y, const float* part, int64_t count, int nparts, hipStream_t stream) {
+  if constexpr (kParts > 1) {
+    if (nparts < kParts) return launch_add<kParts - 1>(Y, part, count, nparts, stream);
+  }
+  const int64_t items = (count & 3) == 0 ? count >> 2 : count;
+  int64_t nblk = (items + 255) / 256;
+  nblk = nblk < 4096 ? nblk : 4096;
+  hipLaunchKernelGGL(splitk_add_kernel<kParts>, dim3((unsigned)nblk), dim3(256), 0, stream, Y,
+                     part, count);
+  return hipGetLastError();
+}
 
 }  // namespace
 
 hipError_t launch_gemm(int fmt, const void* blocks, const void* Xq8, float* Y, int64_t M,
-                       int64_t K, int64_t N, hipStream_t stream) {
+                       int64_t K, int64_t N, float* part, hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
-  // a few tokens: the weights are streamed once per 16 tokens instead (the
-  // MFMA tiles would leave most of the GPU idle)
-  if (N <= kSmallN) return launch_gemm_small(fmt, blocks, Xq8, Y, M, K, N, stream);
+  const int nsplit = part != nullptr ? gemm_splits(fmt, M, K, N) : 1;
+  // a few tokens and no K split: the weights are streamed once per 16
+  // tokens instead (the MFMA tiles would leave most of the GPU idle)
+  if (nsplit == 1 && N <= kSmallN) return launch_gemm_small(fmt, blocks, Xq8, Y, M, K, N, stream);
   const int64_t tiles_m = (M + kBM - 1) / kBM, tiles_n = (N + kBN - 1) / kBN;
-  const int64_t ntiles = tiles_m * tiles_n;
+  const int64_t tps = tiles_m * tiles_n;
+  const int64_t ntiles = tps * nsplit;
   const unsigned grid = (unsigned)(ntiles < kMaxGrid ? ntiles : kMaxGrid);
   const uint8_t* W = static_cast<const uint8_t*>(blocks);
   const uint8_t* X = static_cast<const uint8_t*>(Xq8);
 #define QMAT_GEMM_LAUNCH(F)                                                                \
   hipLaunchKernelGGL(gemm_kernel<F>, dim3(grid), dim3(threads_of(F) + load_threads_of(F)), 0, stream, W, \
-                     X, Y, M, (int)K, N, tiles_n, ntiles)
+                     X, Y, part, M, (int)K, N, tiles_n, tps, nsplit)
   switch (fmt) {
     case kFmtQ4_0:
       QMAT_GEMM_LAUNCH(kFmtQ4_0);
@@ -808,7 +909,9 @@ hipError_t launch_gemm(int fmt, const void* blocks, const void* Xq8, float* Y, i
       break;
   }
 #undef QMAT_GEMM_LAUNCH
-  return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || nsplit == 1) return e;
+  return launch_add<(int)split::kMaxSplit - 1>(Y, part, N * M, nsplit - 1, stream);
 }
 
 }  // namespace qmat

@@ -137,6 +137,8 @@ const char* qmat_strerror(int status) {
     case QMAT_E_SCRATCH:
       return "the Q8_0 activations (N * row bytes) exceed the static workspace of "
              "qmat_prefill_noalloc (qmat_noalloc_scratch_bytes())";
+    case QMAT_E_WORKSPACE:
+      return "the workspace is NULL or smaller than qmat_gemm_workspace_bytes()";
     default: return "unknown status";
   }
 }
@@ -188,19 +190,53 @@ int qmat_gemv_batch(int fmt, const qmat_gemv_job* jobs, int64_t count, void* str
                                             count, static_cast<hipStream_t>(stream)));
 }
 
-int qmat_gemm(int fmt, const void* blocks, const void* X_q8, float* Y, int64_t M, int64_t K,
-              int64_t N, void* stream) {
+namespace {
+// qmat_gemm's checks; *empty when there is nothing to read or write
+int check_gemm(int fmt, const void* blocks, const void* X_q8, const float* Y, int64_t M,
+               int64_t K, int64_t N, bool* empty) {
   if (!fmt_ok(fmt)) return QMAT_E_FMT;
   int rc = check_shape(fmt, M, K);
   if (rc != QMAT_OK) return rc;
   if ((rc = check_shape(QMAT_Q8_0, N, K)) != QMAT_OK) return rc;
   if (K > kMaxGemmK) return QMAT_E_SHAPE;
-  if (M == 0 || N == 0) return QMAT_OK;  // nothing to read or write
+  *empty = M == 0 || N == 0;
+  if (*empty) return QMAT_OK;
   if ((rc = check_buf(blocks, K > 0)) != QMAT_OK) return rc;
   if ((rc = check_buf(X_q8, K > 0)) != QMAT_OK) return rc;
-  if ((rc = check_buf(Y, true)) != QMAT_OK) return rc;
-  return hip_status(
-      qmat::launch_gemm(fmt, blocks, X_q8, Y, M, K, N, static_cast<hipStream_t>(stream)));
+  return check_buf(Y, true);
+}
+}  // namespace
+
+int qmat_gemm(int fmt, const void* blocks, const void* X_q8, float* Y, int64_t M, int64_t K,
+              int64_t N, void* stream) {
+  bool empty = false;
+  int rc = check_gemm(fmt, blocks, X_q8, Y, M, K, N, &empty);
+  if (rc != QMAT_OK || empty) return rc;
+  return hip_status(qmat::launch_gemm(fmt, blocks, X_q8, Y, M, K, N, nullptr,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+int64_t qmat_gemm_workspace_bytes(int fmt, int64_t M, int64_t K, int64_t N) {
+  if (!fmt_ok(fmt) || check_shape(fmt, M, K) != QMAT_OK ||
+      check_shape(QMAT_Q8_0, N, K) != QMAT_OK || K > kMaxGemmK)
+    return -1;
+  return qmat::gemm_workspace_bytes(fmt, M, K, N);
+}
+
+int qmat_gemm_ws(int fmt, const void* blocks, const void* X_q8, float* Y, int64_t M, int64_t K,
+                 int64_t N, void* workspace, int64_t workspace_bytes, void* stream) {
+  bool empty = false;
+  int rc = check_gemm(fmt, blocks, X_q8, Y, M, K, N, &empty);
+  if (rc != QMAT_OK || empty) return rc;
+  if (workspace_bytes < 0) return QMAT_E_SHAPE;
+  const int64_t need = qmat::gemm_workspace_bytes(fmt, M, K, N);
+  if (need > 0) {
+    if (workspace == nullptr || workspace_bytes < need) return QMAT_E_WORKSPACE;
+    if ((rc = check_buf(workspace, true)) != QMAT_OK) return rc;
+  }
+  return hip_status(qmat::launch_gemm(fmt, blocks, X_q8, Y, M, K, N,
+                                      need > 0 ? static_cast<float*>(workspace) : nullptr,
+                                      static_cast<hipStream_t>(stream)));
 }
 
 int qmat_prefill(int fmt, const void* blocks, const float* X, void* xq, float* Y, int64_t M,
@@ -216,7 +252,7 @@ int qmat_prefill(int fmt, const void* blocks, const float* X, void* xq, float* Y
   const hipStream_t st = static_cast<hipStream_t>(stream);
   if (K > 0 && (rc = hip_status(qmat::launch_quantize(QMAT_Q8_0, X, xq, N, K, st))) != QMAT_OK)
     return rc;
-  return hip_status(qmat::launch_gemm(fmt, blocks, xq, Y, M, K, N, st));
+  return hip_status(qmat::launch_gemm(fmt, blocks, xq, Y, M, K, N, nullptr, st));
 }
 
 int64_t qmat_noalloc_scratch_bytes(void) { return QMAT_NOALLOC_SCRATCH_BYTES; }
@@ -238,7 +274,7 @@ int qmat_prefill_noalloc(int fmt, const void* blocks, const float* X, float* Y, 
   const hipStream_t st = static_cast<hipStream_t>(stream);
   if (K > 0 && (rc = hip_status(qmat::launch_quantize(QMAT_Q8_0, X, xq, N, K, st))) != QMAT_OK)
     return rc;
-  return hip_status(qmat::launch_gemm(fmt, blocks, xq, Y, M, K, N, st));
+  return hip_status(qmat::launch_gemm(fmt, blocks, xq, Y, M, K, N, nullptr, st));
 }
 
 int qmat_kv_write(int fmt, const float* rows, const float* bias, void* cache, int64_t cell0,

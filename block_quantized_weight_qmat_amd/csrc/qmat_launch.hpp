@@ -1,9 +1,11 @@
 // qmat_launch.hpp — internal launchers behind the C ABI (include/qmat.h).
-// Arguments are already validated by the caller (qmat_api.hip).
+// Arguments are already validated by the caller (qmat_api.cpp).
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include "gemm_split.hpp"
 
 namespace qmat {
 
@@ -43,8 +45,11 @@ bool decode_mfma_fits(int fmt, int64_t K);
 hipError_t launch_decode_mfma(int fmt, const void* blocks, const void* Xq8, float* Y, int64_t M,
                               int64_t K, int64_t N, int64_t n0, hipStream_t stream);
 
+// Prefill product (gemm.hip). With part non-NULL (gemm_workspace_bytes()
+// bytes), it is split along K into gemm_splits() ranges (gemm_split.hpp)
+// whose partial products go to Y and to part, then added into Y.
 hipError_t launch_gemm(int fmt, const void* blocks, const void* Xq8, float* Y, int64_t M,
-                       int64_t K, int64_t N, hipStream_t stream);
+                       int64_t K, int64_t N, float* part, hipStream_t stream);
 
 
 }  // namespace qmat

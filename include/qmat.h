@@ -118,8 +118,10 @@ typedef enum qmat_status {
   QMAT_E_NULL = 3,  /* a required pointer is NULL                         */
   QMAT_E_HIP = 4,   /* the HIP launch itself failed                       */
   QMAT_E_ALIGN = 5, /* a pointer is not 16-byte aligned                   */
-  QMAT_E_SCRATCH = 6 /* qmat_prefill_noalloc: the activation workspace it
+  QMAT_E_SCRATCH = 6, /* qmat_prefill_noalloc: the activation workspace it
                         needs exceeds its static scratch                   */
+  QMAT_E_WORKSPACE = 7 /* qmat_gemm_ws: workspace NULL or smaller than
+                          qmat_gemm_workspace_bytes()                      */
 } qmat_status;
 
 /* Bytes of the static device workspace of qmat_prefill_noalloc (16 MiB):
@@ -247,6 +249,42 @@ int qmat_gemv_batch(int fmt, const qmat_gemv_job *jobs, int64_t count, void *str
  */
 int qmat_gemm(int fmt, const void *blocks, const void *X_q8, float *Y,
               int64_t M, int64_t K, int64_t N, void *stream);
+
+/*
+ * qmat_gemm_workspace_bytes — bytes of device workspace qmat_gemm_ws needs
+ *   for this product: 0 when it runs as qmat_gemm does, else
+ *   (splits - 1) * N * M * 4 (see qmat_gemm_ws). A function of the
+ *   arguments alone. -1 for an unknown format or a shape qmat_gemm rejects.
+ */
+int64_t qmat_gemm_workspace_bytes(int fmt, int64_t M, int64_t K, int64_t N);
+
+/*
+ * qmat_gemm_ws — qmat_gemm with a caller workspace, which lets a product
+ *   whose 128 x 64 output tiles are too few to occupy every compute unit
+ *   (up to a few hundred tokens) also be divided along K. [LC05
+ *   "算力决定 Prefill"] as for qmat_gemm: the same block products and
+ *   scales; only the order in which block contributions are summed
+ *   changes. The K blocks are cut into `splits` contiguous ranges (whole
+ *   stages of 8 blocks), each range's partial product is computed as
+ *   qmat_gemm computes the whole one, and the partial products are added
+ *   in range order by a second kernel on the same stream.
+ *   Arguments: as for qmat_gemm, plus
+ *   workspace: device buffer of at least qmat_gemm_workspace_bytes(fmt, M,
+ *     K, N) bytes, 16-byte aligned, owned by the caller, used only while
+ *     the call's work runs on stream (its contents are not needed before
+ *     and are garbage after); may be NULL when that size is 0.
+ *   workspace_bytes: its size in bytes (>= 0).
+ *   Results: deterministic, and identical to qmat_gemm's whenever the size
+ *   is 0; otherwise within qmat_gemm's accuracy bound of them (they differ
+ *   only in summation order).
+ *   Errors: qmat_gemm's, then QMAT_E_SHAPE for workspace_bytes < 0,
+ *   QMAT_E_WORKSPACE when a nonzero size is needed and workspace is NULL
+ *   or workspace_bytes is smaller, QMAT_E_ALIGN for a misaligned workspace.
+ *   Two calls that share a workspace must not overlap in time.
+ */
+int qmat_gemm_ws(int fmt, const void *blocks, const void *X_q8, float *Y,
+                 int64_t M, int64_t K, int64_t N, void *workspace,
+                 int64_t workspace_bytes, void *stream);
 
 /*
  * qmat_prefill — the prefill product from fp32 activations in one call:

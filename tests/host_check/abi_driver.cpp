@@ -103,6 +103,28 @@ int main() {
     jobs[0].M = INT64_MAX;
     EXPECT(qmat_gemv_batch(0, jobs, 3, NULL), QMAT_E_SHAPE, 0);
   }
+  // the K-split GEMM: the workspace size is a function of the shape, and
+  // the workspace is checked after qmat_gemm's arguments
+  {
+    const int64_t need = qmat_gemm_workspace_bytes(0, 4096, 11008, 64);
+    if (need != (int64_t)7 * 64 * 4096 * 4) ++failures;
+    if (qmat_gemm_workspace_bytes(0, 4096, 11008, 16) != 0) ++failures;
+    if (qmat_gemm_workspace_bytes(0, 4096, 11008, 512) != 0) ++failures;
+    if (qmat_gemm_workspace_bytes(9, 4096, 11008, 64) != -1) ++failures;
+    if (qmat_gemm_workspace_bytes(0, big - 1, big - 32, big - 1) != -1) ++failures;  // K limit
+    for (int64_t N : {(int64_t)0, (int64_t)17, (int64_t)1 << 20, big - 1})
+      for (int64_t M : {(int64_t)1, (int64_t)4096, big - 1})
+        if (qmat_gemm_workspace_bytes(3, M, 1 << 24, N) < 0) ++failures;
+    EXPECT(qmat_gemm_ws(7, A, A, F, 4096, 11008, 64, A, need, NULL), QMAT_E_FMT, 0);
+    EXPECT(qmat_gemm_ws(0, A, A, NULL, 4096, 11008, 64, A, need, NULL), QMAT_E_NULL, 0);
+    EXPECT(qmat_gemm_ws(0, A, A, F, 4096, 11008, 64, A, -1, NULL), QMAT_E_SHAPE, 0);
+    EXPECT(qmat_gemm_ws(0, A, A, F, 4096, 11008, 64, NULL, need, NULL), QMAT_E_WORKSPACE, 0);
+    EXPECT(qmat_gemm_ws(0, A, A, F, 4096, 11008, 64, A, need - 1, NULL), QMAT_E_WORKSPACE, 0);
+    EXPECT(qmat_gemm_ws(0, A, A, F, 4096, 11008, 64, Ab + 4, need, NULL), QMAT_E_ALIGN, 0);
+    EXPECT(qmat_gemm_ws(0, A, A, F, 4096, 11008, 64, A, need, NULL), QMAT_OK, 1);
+    EXPECT(qmat_gemm_ws(0, A, A, F, 4096, 11008, 16, NULL, 0, NULL), QMAT_OK, 1);  // no split
+    EXPECT(qmat_gemm_ws(0, NULL, NULL, NULL, 0, 11008, 64, NULL, 0, NULL), QMAT_OK, 0);
+  }
   // accepted calls reach the launchers (quantize + gemm for the prefills)
   EXPECT(qmat_quantize(3, F, A, 7, 512, NULL), QMAT_OK, 1);
   EXPECT(qmat_gemv(0, A, F, F, 4096, 11008, NULL), QMAT_OK, 1);

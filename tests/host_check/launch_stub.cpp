@@ -39,7 +39,7 @@ hipError_t launch_gemm_small(int, const void*, const void*, float*, int64_t, int
   ++g_launches;
   return hipSuccess;
 }
-hipError_t launch_gemm(int, const void*, const void*, float*, int64_t, int64_t, int64_t,
+hipError_t launch_gemm(int, const void*, const void*, float*, int64_t, int64_t, int64_t, float*,
                        hipStream_t) {
   ++g_launches;
   return hipSuccess;

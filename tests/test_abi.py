@@ -13,7 +13,7 @@ from block_quantized_weight_qmat_amd import binding
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "qmat.h")
 
-OK, E_FMT, E_SHAPE, E_NULL, E_HIP, E_ALIGN, E_SCRATCH = 0, 1, 2, 3, 4, 5, 6
+OK, E_FMT, E_SHAPE, E_NULL, E_HIP, E_ALIGN, E_SCRATCH, E_WORKSPACE = 0, 1, 2, 3, 4, 5, 6, 7
 
 
 @pytest.fixture(scope="module")
@@ -48,8 +48,9 @@ def test_enum_values_match_header():
     assert vals["QMAT_Q6_K"] == "3"
     assert binding.Q4_0 == 0 and binding.Q8_0 == 1 and binding.Q4_K == 2 and binding.Q6_K == 3
     assert [vals[k] for k in ("QMAT_OK", "QMAT_E_FMT", "QMAT_E_SHAPE", "QMAT_E_NULL",
-                              "QMAT_E_HIP", "QMAT_E_ALIGN", "QMAT_E_SCRATCH")] == \
-        ["0", "1", "2", "3", "4", "5", "6"]
+                              "QMAT_E_HIP", "QMAT_E_ALIGN", "QMAT_E_SCRATCH",
+                              "QMAT_E_WORKSPACE")] == \
+        ["0", "1", "2", "3", "4", "5", "6", "7"]
 
 
 def test_sizes_agree_with_oracle(lib):
@@ -64,7 +65,7 @@ def test_sizes_agree_with_oracle(lib):
 
 
 def test_strerror(lib):
-    for s in range(7):
+    for s in range(8):
         assert len(lib.qmat_strerror(s)) > 3
     assert lib.qmat_strerror(99) == b"unknown status"
 
@@ -238,3 +239,28 @@ def test_gemv_batch_arguments(lib):
     arr[2] = J(A, None, A, 64, 1024)
     assert f(0, p, 3, None) == E_NULL
     assert ctypes.sizeof(J) == 40
+
+
+def test_gemm_ws_arguments(lib):
+    """The workspace size is a function of the shape (0 when the product is
+    not split, (splits - 1) * N * M * 4 otherwise); qmat_gemm_ws checks
+    qmat_gemm's arguments, then the workspace, all before any HIP call."""
+    wb, f = lib.qmat_gemm_workspace_bytes, lib.qmat_gemm_ws
+    M, K = 4096, 11008
+    assert wb(0, M, K, 16) == 0 and wb(0, M, K, 512) == 0 and wb(0, 0, K, 64) == 0
+    need = wb(0, M, K, 64)
+    assert need == 7 * 64 * M * 4                      # eight K ranges
+    assert wb(1, M, K, 64) == need and wb(3, M, K, 64) == need
+    assert wb(0, 11008, 4096, 64) == 1 * 64 * 11008 * 4
+    assert wb(5, M, K, 64) == -1 and wb(2, M, 32, 64) == -1
+    assert wb(0, M, 2 ** 24 + 32, 64) == -1 and wb(0, -1, K, 64) == -1
+    assert f(7, A, A, A, M, K, 64, A, need, None) == E_FMT
+    assert f(0, A, A, A, M, K, -1, A, need, None) == E_SHAPE
+    assert f(0, A, A, None, M, K, 64, A, need, None) == E_NULL
+    assert f(0, A, A + 4, A, M, K, 64, A, need, None) == E_ALIGN
+    assert f(0, A, A, A, M, K, 64, A, -1, None) == E_SHAPE
+    assert f(0, A, A, A, M, K, 64, None, need, None) == E_WORKSPACE
+    assert f(0, A, A, A, M, K, 64, A, need - 1, None) == E_WORKSPACE
+    assert f(0, A, A, A, M, K, 64, A + 8, need, None) == E_ALIGN
+    assert f(0, None, None, None, 0, K, 64, None, 0, None) == OK   # nothing to do
+    assert b"workspace" in lib.qmat_strerror(E_WORKSPACE)

@@ -632,6 +632,91 @@ def test_gemm_k_zero(q, fmt):
         assert np.array_equal(Y, np.zeros((N, 133), np.float32))
 
 
+def gpu_gemm_ws(q, fmt, dB, dXq, M, K, N):
+    """qmat_gemm_ws into a guarded Y, with a NaN-filled, guarded workspace of
+    exactly the size it asks for: a partial product read before it is
+    written shows as NaN, a write past the workspace trips the guard.
+    Returns (Y, workspace bytes)."""
+    import torch
+    need = q.gemm_workspace_bytes(fmt, M, K, N)
+    gw = Guarded((need // 4,)) if need else None
+    g = Guarded((N, M))
+    q.gemm_ws(fmt, dB, dXq, M, K, N, out=g.out,
+              workspace=gw.out.view(torch.uint8) if gw is not None else None)
+    Y = g.get()
+    if gw is not None:
+        gw.check()
+    return Y, need
+
+
+SPLIT_SHAPES = [
+    (300, 256 * 43, 64),   # 3 tiles, 11-15 K ranges of 2-4 stages
+    (257, 4096, 17),       # the fewest tokens that split: 8 ranges of 2 stages
+    (130, 256 * 9, 100),   # 9 stages in 5 ranges (Q6_K-style: pairs, the last one single)
+    (1000, 2048, 200),     # 32 tiles x 4 ranges: the XCD-aware order, ragged last tiles
+    (200, 256 * 5, 48),    # 48 tokens: split here, the decode batch in qmat_gemm
+]
+
+
+@pytest.mark.parametrize("fmt", [0, 1, 2, 3])
+def test_gemm_ws_split(q, fmt):
+    """qmat_gemm_ws on products it splits along K: every output against the
+    oracle, against qmat_gemm's unsplit result (same block products, other
+    summation order), and bit-identical over two calls; with no workspace
+    needed it is qmat_gemm, bit for bit."""
+    rng = np.random.default_rng(900 + fmt)
+    shapes = list(SPLIT_SHAPES)
+    if fmt < 2:
+        shapes += [(64, 32 * 345, 33)]  # a last stage of one block
+    for M, K, N in shapes:
+        say(f"gemm_ws split fmt={fmt} M={M} K={K} N={N}")
+        W = mixed_matrix(rng, M, K)
+        X = rng.normal(0, 1, (N, K)).astype(np.float32)
+        B, Xq = oracle.quantize(fmt, W), oracle.quantize(1, X)
+        dB, dXq = dev_tensor(B), dev_tensor(Xq)
+        Y, need = gpu_gemm_ws(q, fmt, dB, dXq, M, K, N)
+        assert need > 0, "this shape is meant to split"
+        ref = oracle.gemm(fmt, B, Xq, M, K, N)
+        check_close(Y, ref, GEMM_TOL, f"gemm_ws fmt={fmt} M={M} K={K} N={N}")
+        Yu = gpu_gemm(q, fmt, dB, dXq, M, K, N)
+        assert rel_l2(Y, Yu) <= 1e-5, rel_l2(Y, Yu)
+        Y2, _ = gpu_gemm_ws(q, fmt, dB, dXq, M, K, N)
+        assert np.array_equal(Y.view(np.uint32), Y2.view(np.uint32)), "not deterministic"
+    for M, K, N in ((97, 2048, 16), (129, 32 * 23 if fmt < 2 else 768, 70)):
+        say(f"gemm_ws unsplit fmt={fmt} M={M} K={K} N={N}")
+        W = mixed_matrix(rng, M, K)
+        X = rng.normal(0, 1, (N, K)).astype(np.float32)
+        dB, dXq = dev_tensor(oracle.quantize(fmt, W)), dev_tensor(oracle.quantize(1, X))
+        Y, need = gpu_gemm_ws(q, fmt, dB, dXq, M, K, N)
+        assert need == 0
+        assert np.array_equal(Y.view(np.uint32), gpu_gemm(q, fmt, dB, dXq, M, K, N).view(np.uint32))
+
+
+@pytest.mark.parametrize("fmt", [0, 1, 2, 3])
+def test_gemm_ws_full_size(q, fmt):
+    """The 4096 x 11008 layer at 17, 64 and 192 tokens through qmat_gemm_ws
+    (8, 8 and 2 K ranges), weights quantized on the GPU: every output
+    against the oracle, and two calls give the same bits."""
+    import torch
+    W, _ = inputs.llama7b_layer(0)
+    M, K = W.shape
+    rng = np.random.default_rng(12)
+    Xs = rng.normal(0, 1, (192, K)).astype(np.float32)
+    dW = dev_tensor(gpu_quantize(q, fmt, W))
+    Bh = host(dW)
+    for N in (17, 64, 192):
+        dXq = dev_tensor(gpu_quantize(q, 1, Xs[:N]))
+        Xq = host(dXq)
+        Y, need = gpu_gemm_ws(q, fmt, dW, dXq, M, K, N)
+        assert need > 0
+        ref = oracle.gemm(fmt, Bh, Xq, M, K, N)
+        check_close(Y, ref, GEMM_TOL, f"gemm_ws full fmt={fmt} N={N}")
+        Y2, _ = gpu_gemm_ws(q, fmt, dW, dXq, M, K, N)
+        assert np.array_equal(Y.view(np.uint32), Y2.view(np.uint32)), "not deterministic"
+    del dW
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("fmt", [0, 1, 2, 3])
 def test_prefill_one_call(q, fmt):
     """qmat_prefill: its workspace holds the oracle's Q8_0 activation bytes,
