@@ -1538,6 +1538,242 @@ __global__ __launch_bounds__(G * kWave) void gemm_small_kernel(
   }
 }
 
+// ------------------------------------- few tokens, a row per wave (NT <= 4) --
+// The row-per-wave GEMV's structure for up to four tokens, X given as Q8_0
+// blocks. A workgroup of kRowWaves waves owns kRowWaves rows, one per wave,
+// and all of K (at most kRowMaxSlices slices). LDS holds one slot per 64-slice
+// strip with the strip's records for NT tokens: the 32 codes of each block
+// as two 16-byte halves ([token][half][slice]), dx, and for Q4_K-style
+// dx * sum(codes). At the start, wave w loads strip w's blocks of every token
+// (ahead of any weight load), requests its row's first kD strips of weight
+// blocks, writes the strip's records and raises its ready flag. Each wave
+// then streams its row strip by strip (lane = slice), waiting only for the
+// flag of the strip it uses next; each weight block is unpacked to int8 once
+// and multiplied with every token's block by v_dot4_i32_i8 (exact), then
+// scaled by the two block scales in fp32, as in gemm_small_kernel.
+template <int NT>
+struct DecRows {
+  static constexpr int kSlot = NT * (2 * kWave * 16 + 2 * kWave * 4);  // bytes per strip
+  __device__ static u32x4* q(uint8_t* slot, int n, int h, int l) {
+    return reinterpret_cast<u32x4*>(slot + (n * 2 + h) * (kWave * 16) + 16 * l);
+  }
+  __device__ static float* dx(uint8_t* slot, int n) {
+    return reinterpret_cast<float*>(slot + NT * 2 * kWave * 16 + n * kWave * 4);
+  }
+  __device__ static float* xs(uint8_t* slot, int n) {
+    return reinterpret_cast<float*>(slot + NT * 2 * kWave * 16 + (NT + n) * kWave * 4);
+  }
+};
+
+template <class F, int NT, int R, int kWaves, int kD, bool kOdd>
+__global__ __launch_bounds__(kWaves * kWave) void decode_rows_kernel(
+    const uint8_t* __restrict__ B, const uint8_t* __restrict__ Xq, float* __restrict__ Y,
+    int64_t M, int K, int64_t N, int64_t n0) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t slots[];
+  __shared__ int ready[8];
+  typedef DecRows<NT> L;
+  constexpr bool kQ4K = F::kBytes == 144;
+  constexpr bool kQ6K = F::kBytes == 210;
+  constexpr uint32_t kOut = 0x80000000u;  // an offset past the end of any row
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int ns = K >> 5;
+  const int nstrips = (ns + kWave - 1) / kWave;
+  const int64_t rb = F::row_bytes(K);
+  const int64_t xrb = (int64_t)ns * 34;
+  static_assert(kWaves >= 8, "wave w converts strip w");
+  const int64_t m0 = ((int64_t)blockIdx.x * kWaves + wv) * R;  // this wave's first row
+  // with an odd row stride, row m starts at 2 (m & 1) mod 4; a row past M
+  // re-reads the last row of the same parity (M >= 2 then)
+  __amdgpu_buffer_rsrc_t rrs[R];
+  uint32_t par[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int64_t m = m0 + r;
+    par[r] = kOdd ? (uint32_t)(m & 1) : 0u;
+    const int64_t mr = m < M ? m : (kOdd ? M - 1 - ((M - 1 - (int64_t)par[r]) & 1) : M - 1);
+    rrs[r] = make_rsrc(B + mr * rb, rb);
+  }
+
+  // LDS holds whatever the last workgroup left: clear the flags first
+  if (threadIdx.x < 8) flag_set(&ready[threadIdx.x], 0);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+
+  // strip wv of every token's blocks, first among this wave's loads
+  const bool conv = wv < nstrips;
+  const int jc = wv * kWave + lane;  // the slice this lane converts
+  u32x4 xa[NT], xb[NT];
+  uint32_t xsc[NT];
+  BlockLane XL[NT];
+  if (conv) {
+    __builtin_amdgcn_s_setprio(2);
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      const int64_t t = n0 + n < N ? n0 + n : N - 1;  // tokens past N: re-read, scaled by 0
+      const uint8_t* row = Xq + t * xrb;
+      XL[n] = block_lane((uint32_t)(jc < ns ? jc : ns - 1) * 34u, (uint32_t)(t * xrb) & 2u, 34);
+      xa[n] = *reinterpret_cast<const u32x4_a4*>(row + XL[n].o16);
+      xb[n] = *reinterpret_cast<const u32x4_a4*>(row + XL[n].o16 + 16);
+      xsc[n] = *reinterpret_cast<const uint16_t*>(row + XL[n].o2);
+    }
+  }
+  // every wave's weight loads queue behind all of the activation loads
+  asm volatile("s_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+
+  auto lane_of = [&](int st, uint32_t p) { return F::lane(st * kWave + lane, 2u * p); };
+  typename F::Raw wb[kD][R];
+  auto load_w = [&](int st, typename F::Raw (&dst)[R]) {
+    const bool ok = st < nstrips && st * kWave + lane < ns;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      BlockLane W = lane_of(st, par[r]);
+      if (!ok) W.o16 = W.o2 = W.o8 = W.od = kOut;
+      F::load(rrs[r], W, dst[r]);
+    }
+  };
+#pragma unroll
+  for (int u = 0; u < kD; ++u) {
+    load_w(u, wb[u]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  if (conv) {
+    uint8_t* const own = slots + wv * L::kSlot;
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      const uint32_t w[9] = {xa[n].x, xa[n].y, xa[n].z, xa[n].w,
+                             xb[n].x, xb[n].y, xb[n].z, xb[n].w, xsc[n]};
+      uint32_t c[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) c[i] = perm_b32(w[i + 1], w[i], XL[n].sel);
+      const uint32_t dbits = XL[n].mis ? xsc[n] : xa[n].x;
+      const bool live = jc < ns && n0 + n < N;
+      const float dx = live ? f16_bits_to_f32(dbits) : 0.0f;
+      *L::q(own, n, 0, lane) = u32x4{c[0], c[1], c[2], c[3]};
+      *L::q(own, n, 1, lane) = u32x4{c[4], c[5], c[6], c[7]};
+      L::dx(own, n)[lane] = dx;
+      if (kQ4K) {
+        int qs = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) qs = sdot4(c[i], 0x01010101u, qs);
+        L::xs(own, n)[lane] = dx * (float)qs;
+      }
+    }
+    // records first (LDS completes a wave's accesses in order once waited
+    // for), then the flag
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (lane == 0) flag_set(&ready[wv], 1);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_setprio(0);
+  }
+
+  float acc[R * NT];  // value r * NT + t
+#pragma unroll
+  for (int i = 0; i < R * NT; ++i) acc[i] = 0.0f;
+  bool lost = false;  // a flag wait gave up
+  // strip st from buffer w, then (if `next`) strip st + kD into w
+  auto step = [&](int st, typename F::Raw (&w)[R], bool next) {
+    const int j = st * kWave + lane;
+    int n = 0;
+    for (; flag_get(&ready[st]) == 0 && n < kRowSpinLimit; ++n) __builtin_amdgcn_s_sleep(1);
+    lost |= n == kRowSpinLimit;
+    asm volatile("" ::: "memory");
+    uint8_t* const slot = slots + st * L::kSlot;
+    WBlk b[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) b[r] = unpack_w(w[r], lane_of(st, par[r]), j);
+    if (next) load_w(st + kD, w);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const u32x4 qa = *L::q(slot, t, 0, lane), qb = *L::q(slot, t, 1, lane);
+      const uint32_t xq[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
+      const float dx = L::dx(slot, t)[lane];
+      const float xsv = kQ4K ? L::xs(slot, t)[lane] : 0.0f;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        float& a = acc[r * NT + t];
+        if (kQ6K) {
+          int32_t Sa = 0, Sb = 0;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            Sa = sdot4(b[r].w[i], xq[i], Sa);
+            Sb = sdot4(b[r].w[4 + i], xq[4 + i], Sb);
+          }
+          a = fmaf((float)Sb * dx, b[r].Sb, fmaf((float)Sa * dx, b[r].S, a));
+          continue;
+        }
+        int32_t S = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) S = sdot4(b[r].w[i], xq[i], S);
+        const float tt = (float)S * dx;
+        if (kQ4K)
+          a = fmaf(-b[r].O, xsv, fmaf(tt, b[r].S, a));
+        else
+          a = fmaf(tt, b[r].S, a);
+      }
+    }
+    // the next strip's arithmetic must not move above these loads
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  int s0 = 0;
+  for (; s0 + 2 * kD <= nstrips; s0 += kD) {
+#pragma unroll
+    for (int u = 0; u < kD; ++u) step(s0 + u, wb[u], true);
+  }
+#pragma unroll
+  for (int u = 0; u < kD; ++u)
+    if (s0 + u < nstrips) step(s0 + u, wb[u], s0 + u + kD < nstrips);
+#pragma unroll
+  for (int u = 0; u + 1 < kD; ++u)
+    if (s0 + kD + u < nstrips) step(s0 + kD + u, wb[u], false);
+  // value v = r * NT + t summed over the wave's 64 slices
+  constexpr int RN = R * NT;
+  constexpr int kShift = 6 - log2i<RN>();
+  const int v = (lane >> kShift) & (RN - 1);
+  const float sum = wave_reduce_rows<RN>(acc, lane);
+  const int r = v / NT, t = v % NT;
+  if ((lane & ((1 << kShift) - 1)) == 0 && m0 + r < M && n0 + t < N)
+    Y[(n0 + t) * M + m0 + r] = lost ? __builtin_nanf("") : sum;
+}
+
+#ifndef QMAT_DECODE_ROWS
+#define QMAT_DECODE_ROWS 1
+#endif
+// Chunks of up to 4 tokens take the row-per-wave kernel when K fits its LDS
+// slots: measured at 4096 x 11008 and 11008 x 4096 against gemm_small_kernel,
+// 1 and 2 tokens are faster in every format (Q4_0 4096 x 11008: 7.4 / 7.7
+// against 9.8 / 8.4 us), and 3 and 4 tokens with two rows per wave (each
+// token's records then read from LDS once per two rows) in every format but
+// Q4_K-style at 4096 x 11008, which ties (Q4_0: 8.9 against 9.6 us; 11008 x
+// 4096: 9.8 against 12.6; Q4_K-style 9.3 against 9.2 and 11.4 against 12.2).
+// One row per wave at 3-4 tokens: 10.0-10.1 us for Q4_0, 10.6 for Q4_K-style.
+constexpr int kDecodeRowsMaxTokens = 4;
+constexpr int64_t kDecodeRowsMaxLds = 65536;  // dynamic LDS of a launch (K <= 12288 at 4 tokens)
+
+#ifndef QMAT_DECODE_ROWS_R4
+#define QMAT_DECODE_ROWS_R4 2  // rows per wave at 3-4 tokens (16 / R waves per workgroup)
+#endif
+template <class F, int NT, int kD>
+hipError_t launch_decode_rows(const void* blocks, const void* Xq8, float* Y, int64_t M,
+                              int64_t K, int64_t N, int64_t n0, hipStream_t stream) {
+  constexpr int R = NT >= 4 ? QMAT_DECODE_ROWS_R4 : 1, kWaves = kRowWaves / R;
+  const int64_t ns = K / 32;
+  const int64_t nstrips = (ns + kWave - 1) / kWave;
+  const int64_t grid = (M + kWaves * R - 1) / (kWaves * R);
+  const size_t lds = (size_t)nstrips * DecRows<NT>::kSlot;
+  const bool odd = (F::row_bytes(K) & 2) != 0 && M > 1;  // rows start 2 mod 4
+  const uint8_t* Bp = static_cast<const uint8_t*>(blocks);
+  const uint8_t* Xp = static_cast<const uint8_t*>(Xq8);
+  if (odd)
+    hipLaunchKernelGGL((decode_rows_kernel<F, NT, R, kWaves, kD, true>), dim3((unsigned)grid),
+                       dim3(kWaves * kWave), lds, stream, Bp, Xp, Y, M, (int)K, N, n0);
+  else
+    hipLaunchKernelGGL((decode_rows_kernel<F, NT, R, kWaves, kD, false>), dim3((unsigned)grid),
+                       dim3(kWaves * kWave), lds, stream, Bp, Xp, Y, M, (int)K, N, n0);
+  return hipGetLastError();
+}
+
 template <class F, int NT>
 hipError_t launch_small_fmt(const void* blocks, const void* Xq8, float* Y, int64_t M, int64_t K,
                             int64_t N, int64_t n0, hipStream_t stream) {
@@ -1557,10 +1793,17 @@ hipError_t launch_small_fmt(const void* blocks, const void* Xq8, float* Y, int64
   return hipGetLastError();
 }
 
-template <class F>
+template <class F, int RD>
 hipError_t launch_small_chunk(const void* blocks, const void* Xq8, float* Y, int64_t M,
                               int64_t K, int64_t N, int64_t n0, hipStream_t stream) {
   const int64_t nt = N - n0 < 16 ? N - n0 : 16;
+  const int64_t nstrips = (K / 32 + kWave - 1) / kWave;
+  if (QMAT_DECODE_ROWS && nt <= kDecodeRowsMaxTokens && K >= 32 && nstrips <= 8 &&
+      nstrips * DecRows<4>::kSlot <= kDecodeRowsMaxLds) {
+    if (nt <= 1) return launch_decode_rows<F, 1, RD>(blocks, Xq8, Y, M, K, N, n0, stream);
+    if (nt <= 2) return launch_decode_rows<F, 2, RD>(blocks, Xq8, Y, M, K, N, n0, stream);
+    return launch_decode_rows<F, 4, RD>(blocks, Xq8, Y, M, K, N, n0, stream);
+  }
   if (nt <= 1) return launch_small_fmt<F, 1>(blocks, Xq8, Y, M, K, N, n0, stream);
   if (nt <= 2) return launch_small_fmt<F, 2>(blocks, Xq8, Y, M, K, N, n0, stream);
   if (nt <= 4) return launch_small_fmt<F, 4>(blocks, Xq8, Y, M, K, N, n0, stream);
@@ -1635,16 +1878,16 @@ hipError_t launch_gemm_small(int fmt, const void* blocks, const void* Xq8, float
     }
     switch (fmt) {
       case kFmtQ4_0:
-        e = launch_small_chunk<FmtQ4_0>(blocks, Xq8, Y, M, K, N, n0, stream);
+        e = launch_small_chunk<FmtQ4_0, QMAT_GEMV_ROW_DEPTH_Q4_0>(blocks, Xq8, Y, M, K, N, n0, stream);
         break;
       case kFmtQ8_0:
-        e = launch_small_chunk<FmtQ8_0>(blocks, Xq8, Y, M, K, N, n0, stream);
+        e = launch_small_chunk<FmtQ8_0, QMAT_GEMV_ROW_DEPTH_Q8_0>(blocks, Xq8, Y, M, K, N, n0, stream);
         break;
       case kFmtQ4_K:
-        e = launch_small_chunk<FmtQ4_K>(blocks, Xq8, Y, M, K, N, n0, stream);
+        e = launch_small_chunk<FmtQ4_K, QMAT_GEMV_ROW_DEPTH_Q4_K>(blocks, Xq8, Y, M, K, N, n0, stream);
         break;
       default:
-        e = launch_small_chunk<FmtQ6_K>(blocks, Xq8, Y, M, K, N, n0, stream);
+        e = launch_small_chunk<FmtQ6_K, QMAT_GEMV_ROW_DEPTH_Q6_K>(blocks, Xq8, Y, M, K, N, n0, stream);
         break;
     }
     if (e != hipSuccess) return e;
