@@ -1740,20 +1740,37 @@ __global__ __launch_bounds__(kWaves * kWave) void decode_rows_kernel(
 #ifndef QMAT_DECODE_ROWS
 #define QMAT_DECODE_ROWS 1
 #endif
-// Chunks of up to 4 tokens take the row-per-wave kernel when K fits its LDS
-// slots: measured at 4096 x 11008 and 11008 x 4096 against gemm_small_kernel,
-// 1 and 2 tokens are faster in every format (Q4_0 4096 x 11008: 7.4 / 7.7
-// against 9.8 / 8.4 us), and 3 and 4 tokens with two rows per wave (each
-// token's records then read from LDS once per two rows) in every format but
-// Q4_K-style at 4096 x 11008, which ties (Q4_0: 8.9 against 9.6 us; 11008 x
-// 4096: 9.8 against 12.6; Q4_K-style 9.3 against 9.2 and 11.4 against 12.2).
-// One row per wave at 3-4 tokens: 10.0-10.1 us for Q4_0, 10.6 for Q4_K-style.
-constexpr int kDecodeRowsMaxTokens = 4;
-constexpr int64_t kDecodeRowsMaxLds = 65536;  // dynamic LDS of a launch (K <= 12288 at 4 tokens)
+// Chunks of up to 8 tokens take the row-per-wave kernel when K fits its LDS
+// slots, except where another kernel measured faster. Against
+// gemm_small_kernel (4096 x 11008 and 11008 x 4096): 1 and 2 tokens are
+// faster in every format (Q4_0 4096 x 11008: 7.4 / 7.7 against 9.8 / 8.4
+// us), and 3 and 4 tokens with two rows per wave (each token's records then
+// read from LDS once per two rows) in every format but Q4_K-style at 4096 x
+// 11008, which ties (Q4_0: 8.9 against 9.6 us; 11008 x 4096: 9.8 against
+// 12.6; Q4_K-style 9.3 against 9.2 and 11.4 against 12.2; one row per wave:
+// Q4_0 10.0-10.1, Q4_K-style 10.6 us). At 5 to 8 tokens, against the
+// matrix-core kernel (Q4_0, Q8_0) or gemm_small_kernel: Q8_0 13.0 against
+// 13.1 us and 13.0 against 17.3; Q6_K-style 15.3 against 15.6 and 14.6
+// against 19.0; Q4_0 11.5 against 14.3 at 11008 x 4096 but 12.4 against
+// 11.3 at 4096 x 11008 (the matrix cores win on long rows); Q4_K-style 12.8
+// against 12.6-12.9 and 17.1 against 15.7 (left to gemm_small_kernel).
+#ifndef QMAT_DECODE_ROWS_LDS
+#define QMAT_DECODE_ROWS_LDS 160768
+#endif
+constexpr int64_t kDecodeRowsMaxLds = QMAT_DECODE_ROWS_LDS;  // dynamic LDS of a launch
+constexpr int64_t kDecodeRowsLongK = 8192;  // Q4_0 rows from here: 5-8 tokens on the matrix cores
+
+// the most tokens per chunk the row-per-wave kernel takes, by format and K
+inline int64_t decode_rows_max_tokens(int fmt, int64_t K) {
+  if (fmt == kFmtQ4_K) return 4;
+  if (fmt == kFmtQ4_0) return K < kDecodeRowsLongK ? 8 : 4;
+  return 8;
+}
 
 #ifndef QMAT_DECODE_ROWS_R4
-#define QMAT_DECODE_ROWS_R4 2  // rows per wave at 3-4 tokens (16 / R waves per workgroup)
+#define QMAT_DECODE_ROWS_R4 2  // rows per wave from 3 tokens (16 / R waves per workgroup)
 #endif
+
 template <class F, int NT, int kD>
 hipError_t launch_decode_rows(const void* blocks, const void* Xq8, float* Y, int64_t M,
                               int64_t K, int64_t N, int64_t n0, hipStream_t stream) {
@@ -1793,16 +1810,27 @@ hipError_t launch_small_fmt(const void* blocks, const void* Xq8, float* Y, int64
   return hipGetLastError();
 }
 
+// whether a chunk of nt tokens goes to the row-per-wave kernel: its LDS
+// slots (one per 64-slice strip, at most 8) must fit
+inline bool decode_rows_takes(int fmt, int64_t K, int64_t nt) {
+  const int64_t nstrips = (K / 32 + kWave - 1) / kWave;
+  const int64_t slot = nt <= 1 ? DecRows<1>::kSlot
+                       : nt <= 2 ? DecRows<2>::kSlot
+                       : nt <= 4 ? DecRows<4>::kSlot
+                                 : DecRows<8>::kSlot;
+  return QMAT_DECODE_ROWS && K >= 32 && nt <= decode_rows_max_tokens(fmt, K) && nstrips <= 8 &&
+         nstrips * slot <= kDecodeRowsMaxLds;
+}
+
 template <class F, int RD>
-hipError_t launch_small_chunk(const void* blocks, const void* Xq8, float* Y, int64_t M,
+hipError_t launch_small_chunk(int fmt, const void* blocks, const void* Xq8, float* Y, int64_t M,
                               int64_t K, int64_t N, int64_t n0, hipStream_t stream) {
   const int64_t nt = N - n0 < 16 ? N - n0 : 16;
-  const int64_t nstrips = (K / 32 + kWave - 1) / kWave;
-  if (QMAT_DECODE_ROWS && nt <= kDecodeRowsMaxTokens && K >= 32 && nstrips <= 8 &&
-      nstrips * DecRows<4>::kSlot <= kDecodeRowsMaxLds) {
+  if (decode_rows_takes(fmt, K, nt)) {
     if (nt <= 1) return launch_decode_rows<F, 1, RD>(blocks, Xq8, Y, M, K, N, n0, stream);
     if (nt <= 2) return launch_decode_rows<F, 2, RD>(blocks, Xq8, Y, M, K, N, n0, stream);
-    return launch_decode_rows<F, 4, RD>(blocks, Xq8, Y, M, K, N, n0, stream);
+    if (nt <= 4) return launch_decode_rows<F, 4, RD>(blocks, Xq8, Y, M, K, N, n0, stream);
+    return launch_decode_rows<F, 8, RD>(blocks, Xq8, Y, M, K, N, n0, stream);
   }
   if (nt <= 1) return launch_small_fmt<F, 1>(blocks, Xq8, Y, M, K, N, n0, stream);
   if (nt <= 2) return launch_small_fmt<F, 2>(blocks, Xq8, Y, M, K, N, n0, stream);
@@ -1871,23 +1899,29 @@ hipError_t launch_gemm_small(int fmt, const void* blocks, const void* Xq8, float
                              int64_t K, int64_t N, hipStream_t stream) {
   for (int64_t n0 = 0; n0 < N; n0 += 16) {
     hipError_t e;
-    if (QMAT_DECODE_MFMA && N - n0 >= kDecodeMfmaMinTokens && decode_mfma_fits(fmt, K)) {
+    const int64_t nt = N - n0 < 16 ? N - n0 : 16;
+    if (QMAT_DECODE_MFMA && nt >= kDecodeMfmaMinTokens && !decode_rows_takes(fmt, K, nt) &&
+        decode_mfma_fits(fmt, K)) {
       e = launch_decode_mfma(fmt, blocks, Xq8, Y, M, K, N, n0, stream);
       if (e != hipSuccess) return e;
       continue;
     }
     switch (fmt) {
       case kFmtQ4_0:
-        e = launch_small_chunk<FmtQ4_0, QMAT_GEMV_ROW_DEPTH_Q4_0>(blocks, Xq8, Y, M, K, N, n0, stream);
+        e = launch_small_chunk<FmtQ4_0, QMAT_GEMV_ROW_DEPTH_Q4_0>(fmt, blocks, Xq8, Y, M, K, N, n0,
+                                                                stream);
         break;
       case kFmtQ8_0:
-        e = launch_small_chunk<FmtQ8_0, QMAT_GEMV_ROW_DEPTH_Q8_0>(blocks, Xq8, Y, M, K, N, n0, stream);
+        e = launch_small_chunk<FmtQ8_0, QMAT_GEMV_ROW_DEPTH_Q8_0>(fmt, blocks, Xq8, Y, M, K, N, n0,
+                                                                stream);
         break;
       case kFmtQ4_K:
-        e = launch_small_chunk<FmtQ4_K, QMAT_GEMV_ROW_DEPTH_Q4_K>(blocks, Xq8, Y, M, K, N, n0, stream);
+        e = launch_small_chunk<FmtQ4_K, QMAT_GEMV_ROW_DEPTH_Q4_K>(fmt, blocks, Xq8, Y, M, K, N, n0,
+                                                                stream);
         break;
       default:
-        e = launch_small_chunk<FmtQ6_K, QMAT_GEMV_ROW_DEPTH_Q6_K>(blocks, Xq8, Y, M, K, N, n0, stream);
+        e = launch_small_chunk<FmtQ6_K, QMAT_GEMV_ROW_DEPTH_Q6_K>(fmt, blocks, Xq8, Y, M, K, N, n0,
+                                                                stream);
         break;
     }
     if (e != hipSuccess) return e;

@@ -598,8 +598,9 @@ def test_gemm_decode_small_n(q, fmt):
 
 @pytest.mark.parametrize("fmt", [0, 1, 2, 3])
 def test_gemm_decode_full_size(q, fmt):
-    """The 4096 x 11008 layer with 4, 16 and 48 tokens (the decode batch
-    path), weights quantized on the GPU: every output against the oracle,
+    """The 4096 x 11008 layer with 4, 8, 16 and 48 tokens (the decode batch
+    path: the row-per-wave kernel, the matrix cores or the strip kernel by
+    format), weights quantized on the GPU: every output against the oracle,
     and two calls into separately NaN-filled buffers give the same bits."""
     import torch
     W, _ = inputs.llama7b_layer(0)
@@ -608,7 +609,7 @@ def test_gemm_decode_full_size(q, fmt):
     Xs = rng.normal(0, 1, (48, K)).astype(np.float32)
     dW = dev_tensor(gpu_quantize(q, fmt, W))
     Bh = host(dW)
-    for N in (4, 16, 48):
+    for N in (4, 8, 16, 48):
         dXq = dev_tensor(gpu_quantize(q, 1, Xs[:N]))
         Xq = host(dXq)
         Y = gpu_gemm(q, fmt, dW, dXq, M, K, N)
