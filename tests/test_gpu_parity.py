@@ -597,6 +597,29 @@ def test_gemm_decode_small_n(q, fmt):
 
 
 @pytest.mark.parametrize("fmt", [0, 1, 2, 3])
+def test_gemm_decode_rows_limits(q, fmt):
+    """The few-token row-per-wave kernel at the edges of what it takes: one
+    slice per row, rows of 8 strips at 4 tokens (80 KB of LDS), 7 strips at
+    8 tokens (140 KB), 8 strips at 8 tokens (too large: another kernel), odd
+    row strides, a single row, and a row count that leaves the last
+    workgroup's second row empty."""
+    rng = np.random.default_rng(950 + fmt)
+    if fmt < 2:
+        cases = [(40, 32, 3), (1, 32, 8), (33, 32 * 17, 6), (17, 16384, 4), (9, 14336, 8),
+                 (9, 16384, 8), (31, 16384 - 32, 2)]
+    else:
+        cases = [(40, 256, 3), (1, 256, 8), (17, 16384, 4), (9, 14336, 8), (9, 16384, 8),
+                 (33, 256 * 7, 6)]
+    for M, K, N in cases:
+        say(f"gemm decode rows fmt={fmt} M={M} K={K} N={N}")
+        W = mixed_matrix(rng, M, K) if M > 2 else rng.normal(0, 0.02, (M, K)).astype(np.float32)
+        X = rng.normal(0, 1, (N, K)).astype(np.float32)
+        Y, ref = gemm_case(q, fmt, W, X)
+        assert Y.shape == (N, M)
+        check_close(Y, ref, GEMM_TOL, f"gemm decode rows fmt={fmt} M={M} K={K} N={N}")
+
+
+@pytest.mark.parametrize("fmt", [0, 1, 2, 3])
 def test_gemm_decode_full_size(q, fmt):
     """The 4096 x 11008 layer with 4, 8, 16 and 48 tokens (the decode batch
     path: the row-per-wave kernel, the matrix cores or the strip kernel by
