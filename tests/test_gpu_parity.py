@@ -717,6 +717,30 @@ def test_gemm_ws_split(q, fmt):
 
 
 @pytest.mark.parametrize("fmt", [0, 1, 2, 3])
+def test_gemm_random_shapes(q, fmt):
+    """Seeded random shapes across every path a product can take (decode
+    batch kernels, unsplit and K-split tiles): qmat_gemm and qmat_gemm_ws
+    against the oracle, each output buffer NaN-filled and guarded."""
+    rng = np.random.default_rng(1000 + fmt)
+    be = 256 if fmt >= 2 else 32
+    for i in range(14):
+        M = int(rng.integers(1, 700))
+        K = be * int(rng.integers(1, 6144 // be + 1))
+        N = int(rng.choice([int(rng.integers(1, 17)), int(rng.integers(17, 80)),
+                            int(rng.integers(80, 300))]))
+        say(f"gemm random fmt={fmt} case {i}: M={M} K={K} N={N}")
+        W = rng.normal(0, 0.05, (M, K)).astype(np.float32)
+        X = rng.normal(0, 1, (N, K)).astype(np.float32)
+        B, Xq = oracle.quantize(fmt, W), oracle.quantize(1, X)
+        dB, dXq = dev_tensor(B), dev_tensor(Xq)
+        ref = oracle.gemm(fmt, B, Xq, M, K, N)
+        Y = gpu_gemm(q, fmt, dB, dXq, M, K, N)
+        check_close(Y, ref, GEMM_TOL, f"gemm random fmt={fmt} M={M} K={K} N={N}")
+        Yw, _ = gpu_gemm_ws(q, fmt, dB, dXq, M, K, N)
+        check_close(Yw, ref, GEMM_TOL, f"gemm_ws random fmt={fmt} M={M} K={K} N={N}")
+
+
+@pytest.mark.parametrize("fmt", [0, 1, 2, 3])
 def test_gemm_ws_full_size(q, fmt):
     """The 4096 x 11008 layer at 17, 64 and 192 tokens through qmat_gemm_ws
     (8, 8 and 2 K ranges), weights quantized on the GPU: every output
