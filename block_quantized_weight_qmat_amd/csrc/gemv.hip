@@ -56,6 +56,11 @@
 //     multiplied with v_dot4_i32_i8 against the int8 codes.
 //   * Per (row, slice) the exact integer is converted to fp32, scaled by the
 //     block scale and 2^-s, and accumulated in fp32.
+//
+// The file also holds the batched GEMV (many GEMVs per launch, the job taken
+// from blockIdx.y) and the few-token products of the decode batch that do
+// not run on the matrix cores (decode_rows_kernel, gemm_small_kernel), each
+// described where it is defined.
 #include "qmat_device.hpp"
 #include "qmat_launch.hpp"
 
