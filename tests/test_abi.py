@@ -264,3 +264,33 @@ def test_gemm_ws_arguments(lib):
     assert f(0, A, A, A, M, K, 64, A + 8, need, None) == E_ALIGN
     assert f(0, None, None, None, 0, K, 64, None, 0, None) == OK   # nothing to do
     assert b"workspace" in lib.qmat_strerror(E_WORKSPACE)
+
+
+def test_gemm_split_policy_properties(lib):
+    """The K-split policy on seeded random shapes (host code only): the
+    workspace holds whole partial products, at most 16 ranges of at least
+    two stages each (Q6_K-style: whole pairs of stages), none below 17
+    tokens, and the tiles of all ranges stay within 2^24."""
+    import numpy as np
+    rng = np.random.default_rng(7)
+    wb = lib.qmat_gemm_workspace_bytes
+    for _ in range(3000):
+        f = int(rng.integers(0, 4))
+        be = 256 if f >= 2 else 32
+        M = int(rng.integers(1, 40000))
+        K = be * int(rng.integers(1, 2 ** 24 // be // 64))
+        N = int(rng.integers(1, 4000))
+        b = wb(f, M, K, N)
+        assert b >= 0 and b % (4 * N * M) == 0, (f, M, K, N, b)
+        splits = b // (4 * N * M) + 1
+        nst = -(-(K // 32) // 8)
+        unit = 2 if f == 3 else 1
+        assert splits <= 16
+        if N < 17:
+            assert splits == 1
+        if splits > 1:
+            units = -(-nst // unit)
+            assert -(-units // splits) * unit >= 2          # stages of the longest range
+            assert splits <= units
+            tiles = -(-M // 128) * -(-N // 64)
+            assert tiles * splits <= 2 ** 24
