@@ -1,5 +1,6 @@
 // decode.hip — the decode batch on the int8 matrix cores: Y = W X^T for 5 to
-// 16 tokens per launch, W in Q4_0 or Q8_0 blocks, X in Q8_0 blocks.
+// 16 tokens per launch, W in Q4_0, Q8_0 or Q4_K-style blocks, X in Q8_0
+// blocks.
 //
 // Source: "05. llama.cpp：从 GGUF 文件到本地推理服务", sections "槽位、连续批处理与
 // 上下文切分" (several requests decoded at once) and "性能直觉：带宽决定 Decode，
@@ -23,7 +24,9 @@
 // of the block: for Q4_0 these are the two nibbles of code bytes 4q..4q+3,
 // read as one dword and turned into 16 (c - 8) with an XOR and two masks;
 // for Q8_0 (and X) two dwords of codes, realigned when the block starts at
-// 0 mod 4 (codes at 2 mod 4). The MFMA accumulates onto 1.5 * 2^23, so each
+// 0 mod 4 (codes at 2 mod 4); for Q4_K-style the unsigned nibbles of the
+// sub-block's code bytes 4q..4q+3, whose offset term (the sub-block's min
+// times the token's block sum) takes a second MFMA with all-ones weights. The MFMA accumulates onto 1.5 * 2^23, so each
 // integer sum C comes out as the float 1.5 * 2^23 + C (|C| < 2^22) and
 // fma(F, dx, -1.5 * 2^23 * dx) is C * dx rounded once (1.5 dx is exact for
 // an fp16 dx); a second fma adds C * dx * dw to the lane's fp32 sums of rows
@@ -49,9 +52,11 @@ constexpr int kDecRows = 16;   // rows of W per workgroup: the MFMA's A rows
 constexpr int kGroup = 8;      // blocks per stage
 constexpr int kXRowBytes = kGroup * 34;
 
-template <bool kQ4>
+// Weight formats: Q4_0, Q8_0, or Q4_K-style (a stage is one 144-byte
+// superblock per row).
+template <int kFmt>
 struct DecW {
-  static constexpr int kBytes = kQ4 ? 18 : 34;
+  static constexpr int kBytes = kFmt == kFmtQ8_0 ? 34 : 18;  // per block (Q4_K: on average)
   static constexpr int kRowBytes = kGroup * kBytes;  // one row's share of a stage
   static constexpr int kPiecesPerRow = kRowBytes / 16;
   static constexpr int kPieces = kDecRows * kPiecesPerRow;
@@ -72,14 +77,14 @@ struct DecX {
 // 160 KB of LDS allows with a ring of at least two stages (16, 12 or 8: the
 // waves hide each other's LDS and matrix-core latency), each with the
 // deepest ring that then fits.
-template <bool kQ4, int NT>
+template <int kFmt, int NT>
 struct DecRing {
-  static constexpr int kStage = DecW<kQ4>::kStage + DecX<NT>::kStage;
+  static constexpr int kStage = DecW<kFmt>::kStage + DecX<NT>::kStage;
   static constexpr int depth_for(int waves) { return 163840 / waves / kStage; }
   static constexpr int kWaves = depth_for(16) >= 2 ? 16 : depth_for(12) >= 2 ? 12 : 8;
   static constexpr int kDepth0 = depth_for(kWaves);
   static constexpr int kDepth = kDepth0 > 6 ? 6 : kDepth0;
-  static constexpr int kLoads = DecW<kQ4>::kLoads + DecX<NT>::kLoads;
+  static constexpr int kLoads = DecW<kFmt>::kLoads + DecX<NT>::kLoads;
   static constexpr int kWaveLds = kDepth * kStage;
   static_assert(kDepth >= 2 && (kDepth - 1) * kLoads < 64, "ring");
   static_assert(kWaves * 4 * kWave * 4 <= kWaves * kWaveLds, "final sums fit");
@@ -122,31 +127,41 @@ struct BlockWords {
   uint32_t dxb, swb;
 };
 
-template <bool kQ4>
-__device__ __forceinline__ void fetch_words(const uint8_t* wb, const uint8_t* xb, bool odd, int q,
-                                            BlockWords& o) {
+// The token's words (Q8_0, as for a Q8_0 weight block).
+__device__ __forceinline__ void fetch_x(const uint8_t* xb, bool odd, int q, BlockWords& o) {
   if (!odd) {
-    const uint32_t* pw = reinterpret_cast<const uint32_t*>(wb + 4 * q);
-    o.w[0] = pw[0];
-    o.w[1] = pw[1];
-    if (!kQ4) {
-      o.w[2] = pw[4];
-      o.w[3] = pw[5];
-    }
     const uint32_t* px = reinterpret_cast<const uint32_t*>(xb + 4 * q);
     o.x[0] = px[0];
     o.x[1] = px[1];
     o.x[2] = px[4];
     o.x[3] = px[5];
   } else {
-    const uint32_t* pw = reinterpret_cast<const uint32_t*>(wb + 2 + 4 * q);
-    o.w[0] = pw[0];
-    if (!kQ4) o.w[1] = pw[4];
     const uint32_t* px = reinterpret_cast<const uint32_t*>(xb + 2 + 4 * q);
     o.x[0] = px[0];
     o.x[1] = px[4];
   }
   o.dxb = *reinterpret_cast<const uint16_t*>(xb);
+}
+
+// The weight row's words: Q4_0 / Q8_0 block wb (at 0 mod 4 when !odd);
+// Q4_K-style: wb is the sub-block's 16 code bytes, always aligned.
+template <int kFmt>
+__device__ __forceinline__ void fetch_w(const uint8_t* wb, bool odd, int q, BlockWords& o) {
+  if (kFmt == kFmtQ4_K) {
+    o.w[0] = reinterpret_cast<const uint32_t*>(wb + 4 * q)[0];
+  } else if (!odd) {
+    const uint32_t* pw = reinterpret_cast<const uint32_t*>(wb + 4 * q);
+    o.w[0] = pw[0];
+    o.w[1] = pw[1];
+    if (kFmt == kFmtQ8_0) {
+      o.w[2] = pw[4];
+      o.w[3] = pw[5];
+    }
+  } else {
+    const uint32_t* pw = reinterpret_cast<const uint32_t*>(wb + 2 + 4 * q);
+    o.w[0] = pw[0];
+    if (kFmt == kFmtQ8_0) o.w[1] = pw[4];
+  }
 }
 
 // Q8_0 codes of the lane's 8 elements as the MFMA operand (low dword:
@@ -168,6 +183,23 @@ __device__ __forceinline__ uint64_t q4_operand(const uint32_t (&w)[4], bool odd)
   return (uint64_t)hi << 32 | lo;
 }
 
+// The same elements of a Q4_K-style sub-block as unsigned codes 0..15 (byte
+// t of its 16 code bytes: element t low, element t + 16 high).
+__device__ __forceinline__ uint64_t q4k_operand(uint32_t c) {
+  const uint32_t lo = c & 0x0F0F0F0Fu;
+  const uint32_t hi = (c >> 4) & 0x0F0F0F0Fu;
+  return (uint64_t)hi << 32 | lo;
+}
+
+// 6-bit field f of a Q4_K-style superblock's 96-bit scale word (header
+// words 1..3): bits 6f .. 6f + 5.
+__device__ __forceinline__ uint32_t field6(uint32_t w1, uint32_t w2, uint32_t w3, int f) {
+  const int p = 6 * f;
+  const uint32_t lo = p < 32 ? w1 : p < 64 ? w2 : w3;
+  const uint32_t hi = p < 32 ? w2 : p < 64 ? w3 : 0u;
+  return __builtin_amdgcn_alignbit(hi, lo, (uint32_t)(p & 31)) & 63u;
+}
+
 // The value of s held by lane v of this lane's 16-lane row (DPP
 // row_newbcast:v).
 template <int v>
@@ -176,13 +208,14 @@ __device__ __forceinline__ float row_bcast(float s) {
                                                                0x150 + v, 0xF, 0xF, false));
 }
 
-template <bool kQ4, int NT>
-__global__ __launch_bounds__((DecRing<kQ4, NT>::kWaves * kWave)) void decode_mfma_kernel(
+template <int kFmt, int NT>
+__global__ __launch_bounds__((DecRing<kFmt, NT>::kWaves * kWave)) void decode_mfma_kernel(
     const uint8_t* __restrict__ Wb, const uint8_t* __restrict__ Xq, float* __restrict__ Y,
     int64_t M, int K, int64_t N, int64_t n0) {
-  using WS = DecW<kQ4>;
+  constexpr bool kQ4 = kFmt == kFmtQ4_0, kQ4K = kFmt == kFmtQ4_K;
+  using WS = DecW<kFmt>;
   using XS = DecX<NT>;
-  using RG = DecRing<kQ4, NT>;
+  using RG = DecRing<kFmt, NT>;
   constexpr int kWaves = RG::kWaves;
   __shared__ __attribute__((aligned(16))) uint8_t lds[kWaves * RG::kWaveLds];
   const int lane = (int)(threadIdx.x & 63);
@@ -252,10 +285,39 @@ __global__ __launch_bounds__((DecRing<kQ4, NT>::kWaves * kWave)) void decode_mfm
     const uint8_t* sr = ws + srow * WS::kRowBytes;
     // every LDS word of the stage's 8 blocks first, so the reads overlap
     BlockWords bw[kGroup];
+    u32x4 hd = {0u, 0u, 0u, 0u};  // Q4_K-style: the scale row's header
+    if (kQ4K) hd = *reinterpret_cast<const u32x4*>(sr);
 #pragma unroll
     for (int k = 0; k < kGroup; ++k) {
-      fetch_words<kQ4>(wr + k * WS::kBytes, xr + 34 * k, (k & 1) != 0, q, bw[k]);
-      bw[k].swb = *reinterpret_cast<const uint16_t*>(sr + k * WS::kBytes);
+      fetch_w<kFmt>(kQ4K ? wr + 16 + 16 * k : wr + k * WS::kBytes, (k & 1) != 0, q, bw[k]);
+      fetch_x(xr + 34 * k, (k & 1) != 0, q, bw[k]);
+      if (!kQ4K) bw[k].swb = *reinterpret_cast<const uint16_t*>(sr + k * WS::kBytes);
+    }
+    if (kQ4K) {
+      // sub-block k of the scale row: weight = (d sc_k) c - dmin mn_k;
+      // sum_i w_i x_i = S_k sum c x - O_k sum x, and sum x comes from a
+      // second MFMA with all-ones weights
+      const float d = f16_bits_to_f32(hd.x), dmin = f16_bits_to_f32(hd.x >> 16);
+      constexpr long kOnes = 0x0101010101010101L;
+#pragma unroll
+      for (int k = 0; k < kGroup; ++k) {
+        const float S = d * (float)field6(hd.y, hd.z, hd.w, k);
+        const float O = dmin * (float)field6(hd.y, hd.z, hd.w, 8 + k);
+        const bool odd = (k & 1) != 0;
+        const uint64_t b = q8_operand(bw[k].x, odd);
+        const i32x4 c =
+            __builtin_amdgcn_mfma_i32_16x16x32_i8((long)q4k_operand(bw[k].w[0]), (long)b, cmagic, 0, 0, 0);
+        const i32x4 cs = __builtin_amdgcn_mfma_i32_16x16x32_i8(kOnes, (long)b, cmagic, 0, 0, 0);
+        const float dx = f16_bits_to_f32(bw[k].dxb);
+        const float mdx = -kDecMagicF * dx;
+        const f32x4 F = __builtin_bit_cast(f32x4, c);
+        const float u = fmaf(__builtin_bit_cast(float, cs[0]), dx, mdx);  // dx * sum(xq)
+        acc[0] = fmaf(-row_bcast<0>(O), u, fmaf(fmaf(F.x, dx, mdx), row_bcast<0>(S), acc[0]));
+        acc[1] = fmaf(-row_bcast<1>(O), u, fmaf(fmaf(F.y, dx, mdx), row_bcast<1>(S), acc[1]));
+        acc[2] = fmaf(-row_bcast<2>(O), u, fmaf(fmaf(F.z, dx, mdx), row_bcast<2>(S), acc[2]));
+        acc[3] = fmaf(-row_bcast<3>(O), u, fmaf(fmaf(F.w, dx, mdx), row_bcast<3>(S), acc[3]));
+      }
+      return;
     }
 #pragma unroll
     for (int k = 0; k < kGroup; ++k) {
@@ -305,35 +367,45 @@ __global__ __launch_bounds__((DecRing<kQ4, NT>::kWaves * kWave)) void decode_mfm
   }
 }
 
-template <bool kQ4, int NT>
+template <int kFmt, int NT>
 hipError_t launch_dec(const void* blocks, const void* Xq8, float* Y, int64_t M, int64_t K,
                       int64_t N, int64_t n0, hipStream_t stream) {
   const int64_t grid = (M + kDecRows - 1) / kDecRows;
-  hipLaunchKernelGGL((decode_mfma_kernel<kQ4, NT>), dim3((unsigned)grid),
-                     dim3(DecRing<kQ4, NT>::kWaves * kWave), 0, stream, static_cast<const uint8_t*>(blocks),
+  hipLaunchKernelGGL((decode_mfma_kernel<kFmt, NT>), dim3((unsigned)grid),
+                     dim3(DecRing<kFmt, NT>::kWaves * kWave), 0, stream, static_cast<const uint8_t*>(blocks),
                      static_cast<const uint8_t*>(Xq8), Y, M, (int)K, N, n0);
   return hipGetLastError();
 }
 
-template <bool kQ4>
+template <int kFmt>
 hipError_t launch_dec_fmt(const void* blocks, const void* Xq8, float* Y, int64_t M, int64_t K,
                           int64_t N, int64_t n0, hipStream_t stream) {
   const int64_t nt = N - n0;
-  if (nt <= 8) return launch_dec<kQ4, 8>(blocks, Xq8, Y, M, K, N, n0, stream);
-  return launch_dec<kQ4, 16>(blocks, Xq8, Y, M, K, N, n0, stream);
+  if (nt <= 8) return launch_dec<kFmt, 8>(blocks, Xq8, Y, M, K, N, n0, stream);
+  return launch_dec<kFmt, 16>(blocks, Xq8, Y, M, K, N, n0, stream);
 }
 
 }  // namespace
 
+#ifndef QMAT_DECODE_MFMA_Q4K
+#define QMAT_DECODE_MFMA_Q4K 1
+#endif
 bool decode_mfma_fits(int fmt, int64_t K) {
-  return (fmt == kFmtQ4_0 || fmt == kFmtQ8_0) && K >= 32 * kGroup && K % (32 * kGroup) == 0;
+  return (fmt == kFmtQ4_0 || fmt == kFmtQ8_0 || (QMAT_DECODE_MFMA_Q4K && fmt == kFmtQ4_K)) &&
+         K >= 32 * kGroup && K % (32 * kGroup) == 0;
 }
 
 hipError_t launch_decode_mfma(int fmt, const void* blocks, const void* Xq8, float* Y, int64_t M,
                               int64_t K, int64_t N, int64_t n0, hipStream_t stream) {
   if (M == 0 || N <= n0) return hipSuccess;
-  return fmt == kFmtQ4_0 ? launch_dec_fmt<true>(blocks, Xq8, Y, M, K, N, n0, stream)
-                         : launch_dec_fmt<false>(blocks, Xq8, Y, M, K, N, n0, stream);
+  switch (fmt) {
+    case kFmtQ4_0:
+      return launch_dec_fmt<kFmtQ4_0>(blocks, Xq8, Y, M, K, N, n0, stream);
+    case kFmtQ8_0:
+      return launch_dec_fmt<kFmtQ8_0>(blocks, Xq8, Y, M, K, N, n0, stream);
+    default:
+      return launch_dec_fmt<kFmtQ4_K>(blocks, Xq8, Y, M, K, N, n0, stream);
+  }
 }
 
 }  // namespace qmat

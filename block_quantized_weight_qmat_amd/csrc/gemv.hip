@@ -1920,18 +1920,21 @@ namespace qmat {
 #define QMAT_DECODE_MFMA 1
 #endif
 // Chunks of at least this many tokens go to the matrix-core kernel when it
-// takes the format and K. Measured at 4096 x 11008 (Q4_0 / Q8_0): up to 4
-// tokens this kernel is faster (9.5 / 12.4 us at 4 against 10.4 / 12.8), from
-// 5 the matrix cores are (8 tokens: 11.4 / 13.3 us against 12.8 / 13.7; 16:
-// 12.8 / 15.3 against 20.7 / 21.4).
-constexpr int64_t kDecodeMfmaMinTokens = 5;
+// takes the format and K (and the row-per-wave kernel does not). Measured
+// at 4096 x 11008 against gemm_small_kernel: Q4_0 / Q8_0 from 5 tokens (8
+// tokens: 11.4 / 13.3 us against 12.8 / 13.7; 16: 12.8 / 15.3 against 20.7
+// / 21.4); Q4_K-style from 9 (8 tokens: 13.8 against 13.0 us; 12: 15.0
+// against 20.5; 16: 15.2 against 22.1, and 19.6 against 24.8 at 11008 x
+// 4096), its two matrix-core products per block (codes, and the block sums
+// of the tokens for the offset term) costing more arithmetic.
+inline int64_t decode_mfma_min_tokens(int fmt) { return fmt == kFmtQ4_K ? 9 : 5; }
 
 hipError_t launch_gemm_small(int fmt, const void* blocks, const void* Xq8, float* Y, int64_t M,
                              int64_t K, int64_t N, hipStream_t stream) {
   for (int64_t n0 = 0; n0 < N; n0 += 16) {
     hipError_t e;
     const int64_t nt = N - n0 < 16 ? N - n0 : 16;
-    if (QMAT_DECODE_MFMA && nt >= kDecodeMfmaMinTokens && !decode_rows_takes(fmt, K, nt) &&
+    if (QMAT_DECODE_MFMA && nt >= decode_mfma_min_tokens(fmt) && !decode_rows_takes(fmt, K, nt) &&
         decode_mfma_fits(fmt, K)) {
       e = launch_decode_mfma(fmt, blocks, Xq8, Y, M, K, N, n0, stream);
       if (e != hipSuccess) return e;
