@@ -824,6 +824,9 @@ static_assert(kBM == split::kTileM && kBN == split::kTileN && kKB == split::kSta
 #define QMAT_GEMM_SMALL_N 48
 #endif
 constexpr int64_t kSmallN = QMAT_GEMM_SMALL_N;
+#ifndef QMAT_GEMM_DECODE_MODEL
+#define QMAT_GEMM_DECODE_MODEL 1
+#endif
 // Y += part[0] + part[1] + ... + part[kParts - 1] (partial products of
 // count values each), added in that order for every element. All loads of
 // an element are issued before the first add.
@@ -884,7 +887,8 @@ hipError_t launch_gemm(int fmt, const void* blocks, const void* Xq8, float* Y, i
   const int nsplit = part != nullptr ? gemm_splits(fmt, M, K, N) : 1;
   // a few tokens and no K split: the weights are streamed once per 16
   // tokens instead (the MFMA tiles would leave most of the GPU idle)
-  if (nsplit == 1 && N <= kSmallN) return launch_gemm_small(fmt, blocks, Xq8, Y, M, K, N, stream);
+  if (nsplit == 1 && (QMAT_GEMM_DECODE_MODEL ? gemm_uses_decode(fmt, M, K, N) : N <= kSmallN))
+    return launch_gemm_small(fmt, blocks, Xq8, Y, M, K, N, stream);
   const int64_t tiles_m = (M + kBM - 1) / kBM, tiles_n = (N + kBN - 1) / kBN;
   const int64_t tps = tiles_m * tiles_n;
   const int64_t ntiles = tps * nsplit;

@@ -78,6 +78,40 @@ inline int gemm_splits(int fmt, int64_t M, int64_t K, int64_t N) {
   return best_s;
 }
 
+// Without a K split: whether N tokens go to the decode batch's kernels (the
+// weights streamed once per 16 tokens) instead of the 128 x 64 tiles. A
+// model of the two, in microseconds: the tiles take
+//   ceil(tiles / kSplitTarget) * (stages + kFillStages) * s_fmt
+// (s_fmt about 1.3 us per stage for Q4_0 while at most one round of
+// workgroups runs, scaled by the formats' measured GEMM times), and each
+// chunk of up to 16 tokens of the decode batch
+//   ceil(M / 16 / kSplitTarget) * (0.25 * stages + 2) * d_fmt
+// (one 16-row workgroup per CU and round; 12.9 us per 16-token chunk at
+// 4096 x 11008, 17.4 at 11008 x 4096), half that for chunks of up to 4
+// tokens (the row-per-wave kernel). Measured against a fixed limit of 48
+// tokens: 4096 x 11008 at 56 / 64 tokens 59.0 -> 43.5 / 44.9 us (Q4_0) and
+// 87.6 -> 53.2 / 53.6 (Q4_K-style); 11008 x 4096 Q4_0 at 24 / 48 tokens
+// 28.5 / 48.2 -> 25.8 / 26.4.
+constexpr int64_t kDecodeMaxN = 64;
+inline bool gemm_uses_decode(int fmt, int64_t M, int64_t K, int64_t N) {
+  using namespace split;
+  if (N <= 16) return true;
+  if (N > kDecodeMaxN) return false;
+  static constexpr double kStageUs[4] = {1.3, 1.35, 1.7, 2.2};  // Q4_0, Q8_0, Q4_K, Q6_K
+  static constexpr double kChunk[4] = {1.0, 1.2, 1.2, 1.75};
+  const int f = fmt >= 0 && fmt < 4 ? fmt : 0;
+  const int64_t tiles = ((M + kTileM - 1) / kTileM) * ((N + kTileN - 1) / kTileN);
+  const int64_t nst = (K / 32 + kStageBlocks - 1) / kStageBlocks;
+  const double t_tiles =
+      (double)((tiles + kSplitTarget - 1) / kSplitTarget) * (double)(nst + kFillStages) * kStageUs[f];
+  const double chunk = (double)(((M + 15) / 16 + kSplitTarget - 1) / kSplitTarget) *
+                       (0.25 * (double)nst + 2.0);
+  const int64_t tail = N % 16;
+  const double t_dec = (double)(N / 16) * chunk * kChunk[f] +
+                       (tail == 0 ? 0.0 : tail <= 4 ? 0.5 * chunk : chunk * kChunk[f]);
+  return t_dec < t_tiles;
+}
+
 // Workspace for the partial products of ranges 1 .. splits-1 (range 0 is
 // written to Y): (splits - 1) * N * M fp32 values.
 inline int64_t gemm_workspace_bytes(int fmt, int64_t M, int64_t K, int64_t N) {

@@ -237,9 +237,10 @@ int qmat_gemv_batch(int fmt, const qmat_gemv_job *jobs, int64_t count, void *str
  *   Y: fp32 [N][M] (token-major), overwritten.
  *   K is at most 2^24 here (QMAT_E_SHAPE above that): the kernel addresses
  *   a 128-row tile with 32-bit byte offsets.
- *   Up to 48 tokens (a decode batch) the weights are instead streamed once
- *   per 16 tokens and each weight block is applied to every token's block
- *   with int8 dot products; the
+ *   For a few tokens (a decode batch: up to 16, and up to 64 where a model
+ *   of the two paths' times favours it, e.g. long rows) the weights are
+ *   instead streamed once per 16 tokens and each weight block is applied
+ *   to every token's block with int8 dot products; the
  *   arithmetic (exact block sums, the fp16 block scales applied in fp32;
  *   Q6_K: per 16-weight half) and the accuracy bound are the same.
  *   Accuracy: relative L2 error against the exact (fp64) product of the

@@ -573,9 +573,9 @@ def test_gemm_small_and_ragged(q, fmt):
 
 @pytest.mark.parametrize("fmt", [0, 1, 2, 3])
 def test_gemm_decode_small_n(q, fmt):
-    """Few-token products (the decode batch path, up to 48 tokens, in chunks
-    of 16): every token count around the chunk sizes, odd row strides,
-    ragged row counts, and the switch to the MFMA path after 48 tokens."""
+    """Few-token products (the decode batch path, in chunks of 16 tokens):
+    every token count around the chunk sizes, odd row strides, ragged row
+    counts, and token counts around the switch to the prefill tiles."""
     rng = np.random.default_rng(700 + fmt)
     K1 = 256 * 9 if fmt >= 2 else 32 * 345  # odd block count per row
     cases = [(97, K1, n) for n in (1, 2, 3, 4, 5, 7, 8, 9, 15, 16, 17, 31, 33, 48, 49)]
