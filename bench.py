@@ -613,8 +613,8 @@ def main():
             splits = ws_mid[n].numel() // (4 * n * M) + 1 if name.startswith("gemm_ws") else 1
             kernels[name] = {"us": us, "tokens": n, "int8_ops": ops_n, "TOPS": tops,
                              "bound": "mfma", "frac": tops / INT8_PEAK_TOPS,
-                             "path": "decode batch" if n <= 48 and splits == 1 else
-                             f"tiles, {splits} K range(s)"}
+                             "path": f"qmat_gemm_ws, {splits} K range(s)"
+                             if name.startswith("gemm_ws") else "qmat_gemm (no workspace)"}
         elif name.startswith("gemm_"):
             tops = gemm_ops / us / 1e6
             kernels[name] = {"us": us, "int8_ops": gemm_ops, "TOPS": tops, "bound": "mfma",
