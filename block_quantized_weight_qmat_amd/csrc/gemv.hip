@@ -1087,24 +1087,42 @@ StripShape strip_shape(int64_t M, int64_t K) {
   return {waves, odd, ns <= kWave / 2 && M > 1};
 }
 
+template <class F, int RR, int RD>
+hipError_t launch_rows(const void* blocks, const float* x, float* y, int64_t M, int64_t K,
+                       hipStream_t stream) {
+  const int64_t ns = K / 32;
+  const int64_t grid = (M + kRowWaves * RR - 1) / (kRowWaves * RR);
+  const size_t lds = (size_t)((ns + kWave - 1) / kWave) * kRowSlot;
+  const bool odd = (F::row_bytes(K) & 2) != 0 && M > 1;  // rows start 2 mod 4
+  if (odd)
+    hipLaunchKernelGGL((gemv_rows_kernel<F, RR, RD, true>), dim3((unsigned)grid),
+                       dim3(kRowWaves * kWave), lds, stream, static_cast<const uint8_t*>(blocks),
+                       x, y, M, (int)K);
+  else
+    hipLaunchKernelGGL((gemv_rows_kernel<F, RR, RD, false>), dim3((unsigned)grid),
+                       dim3(kRowWaves * kWave), lds, stream, static_cast<const uint8_t*>(blocks),
+                       x, y, M, (int)K);
+  return hipGetLastError();
+}
+
+// Two rows per wave (32 rows per workgroup) for the 4-bit formats in tall
+// matrices: with one row per wave they would queue more than three 16-row
+// workgroups per CU. Measured (one against two rows per wave): Q4_0 14336 x
+// 4096 9.6 -> 8.4 us, 14336 x 8192 15.5 -> 14.7, 28672 x 4096 18.0 -> 15.1;
+// Q4_K-style 14336 x 4096 12.6 -> 10.6, 28672 x 4096 21.7 -> 20.3; Q8_0 and
+// Q6_K-style no better (11008 x 8192 Q8_0: 18.4 -> 21.8), nor shorter 4-bit
+// matrices (Q4_0 4096 x 11008: 7.45 -> 9.42, 11008 x 8192: 13.2 -> 13.6).
+constexpr int64_t kRows2MinM = 12288;
+
 template <class F, int R, int G, int D, int RD>
 hipError_t launch_fmt(const void* blocks, const float* x, float* y, int64_t M, int64_t K,
                       hipStream_t stream) {
   const int64_t ns = K / 32;
   if (rows_kernel_takes(M, ns)) {
-    constexpr int RR = QMAT_GEMV_ROW_R;
-    const int64_t grid = (M + kRowWaves * RR - 1) / (kRowWaves * RR);
-    const size_t lds = (size_t)((ns + kWave - 1) / kWave) * kRowSlot;
-    const bool odd = (F::row_bytes(K) & 2) != 0 && M > 1;  // rows start 2 mod 4
-    if (odd)
-      hipLaunchKernelGGL((gemv_rows_kernel<F, RR, RD, true>), dim3((unsigned)grid),
-                         dim3(kRowWaves * kWave), lds, stream,
-                         static_cast<const uint8_t*>(blocks), x, y, M, (int)K);
-    else
-      hipLaunchKernelGGL((gemv_rows_kernel<F, RR, RD, false>), dim3((unsigned)grid),
-                         dim3(kRowWaves * kWave), lds, stream,
-                         static_cast<const uint8_t*>(blocks), x, y, M, (int)K);
-    return hipGetLastError();
+    constexpr bool k4bit = F::kBytes == 18 || F::kBytes == 144;
+    if (k4bit && QMAT_GEMV_ROW_R == 1 && M > kRows2MinM)
+      return launch_rows<F, 2, RD>(blocks, x, y, M, K, stream);
+    return launch_rows<F, QMAT_GEMV_ROW_R, RD>(blocks, x, y, M, K, stream);
   }
   const StripShape sh = strip_shape<F>(M, K);
   const int64_t grid = (M + sh.rows(R * G) - 1) / sh.rows(R * G);

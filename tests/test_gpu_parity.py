@@ -362,6 +362,34 @@ def test_gemv_k_zero_and_tall(q):
         assert rel_l2(y, ref) <= GEMV_TOL
 
 
+@pytest.mark.parametrize("fmt", [0, 2])
+def test_gemv_tall_two_rows_per_wave(q, fmt):
+    """Tall 4-bit matrices take the row kernel with two rows per wave: rows
+    past M in the last workgroup, an odd row stride (Q4_0, K = 32 * 131),
+    and a row count just past the switch; within the bound, with one-hot x
+    giving a column exactly."""
+    rng = np.random.default_rng(40 + fmt)
+    shapes = [(12289, 4096), (14336 + 17, 256 * 17)]
+    if fmt == 0:
+        shapes.append((12300, 32 * 131))
+    for M, K in shapes:
+        say(f"gemv tall two rows fmt={fmt} M={M} K={K}")
+        W = rng.normal(0, 0.02, (M, K)).astype(np.float32)
+        x = rng.normal(0, 1, K).astype(np.float32)
+        y, ref, _ = gemv_case(q, fmt, W, x)
+        check_close(y, ref, GEMV_TOL, f"gemv tall fmt={fmt} M={M} K={K}")
+    M, K = 12345, 4096
+    W = rng.normal(0, 0.02, (M, K)).astype(np.float32)
+    x = np.zeros(K, np.float32)
+    x[1234] = 1.0
+    y, _, B = gemv_case(q, fmt, W, x)
+    col = oracle.dequant(fmt, B, M, K)[:, 1234]
+    if fmt == 2:  # S*q - O may round once in fp32
+        assert np.allclose(y.astype(np.float64), col, rtol=2 ** -23, atol=0)
+    else:
+        assert np.array_equal(y.astype(np.float64), col), "one-hot"
+
+
 def test_gemv_workloads_full(q):
     """Every matrix of the decode workloads, every output row."""
     W, x = inputs.gemv_1024()
