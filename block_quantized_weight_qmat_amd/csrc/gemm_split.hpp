@@ -30,24 +30,15 @@ namespace qmat {
 namespace split {
 
 constexpr int64_t kTileM = 128, kTileN = 64, kStageBlocks = 8;  // gemm.hip's tile and stage
-#ifndef QMAT_GEMM_SPLIT_TARGET
-#define QMAT_GEMM_SPLIT_TARGET 256
-#endif
-#ifndef QMAT_GEMM_SPLIT_MIN_STAGES
-#define QMAT_GEMM_SPLIT_MIN_STAGES 2
-#endif
-#ifndef QMAT_GEMM_FILL_STAGES
-#define QMAT_GEMM_FILL_STAGES 3
-#endif
+// The policy is plain constants, not build options: the launcher and the
+// argument checks (qmat_gemm_workspace_bytes) are separate translation
+// units and must agree on the workspace a shape needs.
+constexpr int64_t kSplitTarget = 256;
+constexpr int64_t kMinSplitStages = 2;
+constexpr int64_t kFillStages = 3;
 // measured at 4096 x 11008 and 11008 x 4096 in every format: from 17 to 32
 // tokens a split product beats the decode batch
-#ifndef QMAT_GEMM_SPLIT_MIN_N
-#define QMAT_GEMM_SPLIT_MIN_N 17
-#endif
-constexpr int64_t kSplitTarget = QMAT_GEMM_SPLIT_TARGET;
-constexpr int64_t kMinSplitStages = QMAT_GEMM_SPLIT_MIN_STAGES;
-constexpr int64_t kFillStages = QMAT_GEMM_FILL_STAGES;
-constexpr int64_t kSplitMinN = QMAT_GEMM_SPLIT_MIN_N;
+constexpr int64_t kSplitMinN = 17;
 constexpr double kAddBytesPerStage = 6.8e6;
 constexpr int64_t kMaxSplit = 16;
 constexpr int64_t kMaxSplitTiles = 1 << 24;  // tiles of all ranges together
