@@ -172,6 +172,27 @@ def test_quantize_bytes_identical_small(q, fmt):
         assert_bytes(gpu_quantize(q, fmt, W), oracle.quantize(fmt, W), f"fmt {fmt} {rows}x{K}")
 
 
+
+def random_shape(rng, be, max_elems, max_rows=20000, max_k=32768):
+    """A seeded (rows, K) pair: rows log-uniform in [1, max_rows], K a
+    log-uniform multiple of the block size be, rows * K <= max_elems."""
+    K = be * int(np.exp(rng.uniform(0, np.log(max_k // be))))
+    rows = int(np.exp(rng.uniform(0, np.log(min(max_rows, max(1, max_elems // K))))))
+    return max(1, rows), max(be, K)
+
+
+@pytest.mark.parametrize("fmt", [0, 1, 2, 3])
+def test_quantize_random_shapes(q, fmt):
+    """Seeded random shapes: the quantizer's launch shape (lanes per block,
+    blocks per wave, workgroups) follows rows and K."""
+    rng = np.random.default_rng(150 + fmt)
+    be = 256 if fmt >= 2 else 32
+    for i in range(10):
+        rows, K = random_shape(rng, be, 3_000_000)
+        say(f"quantize random fmt={fmt} case {i}: rows={rows} K={K}")
+        W = mixed_matrix(rng, rows, K)
+        assert_bytes(gpu_quantize(q, fmt, W), oracle.quantize(fmt, W), f"fmt {fmt} {rows}x{K}")
+
 def test_quantize_edge_values(q):
     say("quantize edge values")
     # exact ties, fp16-subnormal and fp16-overflow-adjacent scales, +-0
@@ -292,6 +313,22 @@ def test_gemv_small_and_ragged(q, fmt):
         y, ref, _ = gemv_case(q, fmt, W, x)
         assert rel_l2(y, ref) <= GEMV_TOL, (M, K, rel_l2(y, ref))
 
+
+
+@pytest.mark.parametrize("fmt", [0, 1, 2, 3])
+def test_gemv_random_shapes(q, fmt):
+    """Seeded random shapes across the GEMV's routes, which depend on rows
+    and K: the strip kernel in its row-group shapes, the row-per-wave kernel
+    with one or two rows per wave (tall matrices), ragged strips and tails."""
+    rng = np.random.default_rng(250 + fmt)
+    be = 256 if fmt >= 2 else 32
+    for i in range(16):
+        M, K = random_shape(rng, be, 24_000_000)
+        say(f"gemv random fmt={fmt} case {i}: M={M} K={K}")
+        W = rng.normal(0, 0.02, (M, K)).astype(np.float32)
+        x = rng.normal(0, 1, K).astype(np.float32)
+        y, ref, _ = gemv_case(q, fmt, W, x)
+        check_close(y, ref, GEMV_TOL, f"gemv random fmt={fmt} M={M} K={K}")
 
 @pytest.mark.parametrize("fmt", [0, 1, 2, 3])
 def test_gemv_one_hot_gives_the_column(q, fmt):
