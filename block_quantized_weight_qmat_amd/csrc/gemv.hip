@@ -772,7 +772,7 @@ __global__ __launch_bounds__(kMaxStrips * kWave) void gemv_batch_kernel(GemvBatc
 
 // -------------------------------------------------- GEMV, a row per wave --
 // A workgroup of kRowWaves waves owns kRowWaves rows, one per wave, and all
-// of K (at most kRowMaxSlices slices, 8 strips of 64). LDS holds one 8 KB
+// of K (at most kRowMaxSlices slices, kRowMaxStrips strips of 64). LDS holds one 8 KB
 // slot per strip. At the start, wave w copies strip w of the activations
 // from memory into slot w (all copies ahead of any weight load), requests
 // the weight blocks of its row's first kD strips, and then converts the slot
@@ -819,8 +819,20 @@ __device__ __forceinline__ void flag_set(int* f, int v) {
 __device__ __forceinline__ int flag_get(int* f) {
   return __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
-constexpr int kRowMaxSlices = 8 * kWave;  // 8 slots: the 64 KB a workgroup may allocate
-static_assert(kRowWaves >= 8, "wave w converts strip w");
+#ifndef QMAT_GEMV_ROW_STRIPS
+#define QMAT_GEMV_ROW_STRIPS 8
+#endif
+// Strips (LDS slots) of the longest row the kernel takes, at most one per
+// wave (wave w converts strip w). The slots are dynamic LDS, so 16 (128 KB)
+// would fit; measured against the strip kernel on rows of 640 to 1024
+// slices, 16 won only where the grid is one workgroup per CU (Q4_0
+// 4096 x 20480: 11.4 against 12.7 us) and tied or lost elsewhere (8192 x
+// 28672: Q4_0 30.9 against 32.6, Q4_K-style 32.0 against 30.5; 2048 x 32768:
+// 14.6 against 11.1 with half the CUs idle), so longer rows stay with the
+// strip kernel.
+constexpr int kRowMaxStrips = QMAT_GEMV_ROW_STRIPS;
+constexpr int kRowMaxSlices = kRowMaxStrips * kWave;
+static_assert(kRowWaves >= kRowMaxStrips, "wave w converts strip w");
 
 // Records of the 64 slices of a slot (they replace the activations). Nibble
 // digits: word t of digit i of slice l at byte 1024 i + 16 l + 4 t (a lane
@@ -910,7 +922,7 @@ __device__ __forceinline__ void gemv_rows(const uint8_t* __restrict__ B,
   }
 
   // LDS holds whatever the last workgroup left: clear the flags first
-  if (threadIdx.x < 8) flag_set(&ready[threadIdx.x], 0);
+  if (threadIdx.x < kRowMaxStrips) flag_set(&ready[threadIdx.x], 0);
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
   // strip wv of the activations into slot wv, first among this wave's loads
@@ -1010,7 +1022,7 @@ __global__ __launch_bounds__(kRowWaves * kWave) void gemv_rows_kernel(
     const uint8_t* __restrict__ B, const float* __restrict__ x, float* __restrict__ y,
     int64_t M, int K) {
   extern __shared__ __attribute__((aligned(16))) uint8_t slots[];
-  __shared__ int ready[8];
+  __shared__ int ready[kRowMaxStrips];
   gemv_rows<F, R, kD, kOdd>(B, x, y, M, K, blockIdx.x, slots, ready);
 }
 
@@ -1021,7 +1033,7 @@ __global__ __launch_bounds__(kRowWaves * kWave) void gemv_rows_kernel(
 template <class F, int R, int kD, bool kOdd>
 __global__ __launch_bounds__(kRowWaves * kWave) void gemv_rows_batch_kernel(GemvBatchArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t slots[];
-  __shared__ int ready[8];
+  __shared__ int ready[kRowMaxStrips];
   const int j = blockIdx.y;
   const int64_t M = a.M[j];
   if ((int64_t)blockIdx.x * kRowWaves * R >= M) return;  // the whole workgroup
@@ -1587,10 +1599,11 @@ __global__ __launch_bounds__(G * kWave) void gemm_small_kernel(
   }
 }
 
-// ------------------------------------- few tokens, a row per wave (NT <= 4) --
-// The row-per-wave GEMV's structure for up to four tokens, X given as Q8_0
-// blocks. A workgroup of kRowWaves waves owns kRowWaves rows, one per wave,
-// and all of K (at most kRowMaxSlices slices). LDS holds one slot per 64-slice
+// ------------------------------------- few tokens, a row per wave (NT <= 8) --
+// The row-per-wave GEMV's structure for up to eight tokens, X given as Q8_0
+// blocks. A workgroup owns kRowWaves rows and all of K (at most 8 strips of
+// 64 slices): 16 waves of one row each, or from four tokens 8 waves of two
+// rows each, which halves the LDS reads per row. LDS holds one slot per 64-slice
 // strip with the strip's records for NT tokens: the 32 codes of each block
 // as two 16-byte halves ([token][half][slice]), dx, and for Q4_K-style
 // dx * sum(codes). At the start, wave w loads strip w's blocks of every token
