@@ -24,15 +24,15 @@
 // tiles (two 32 x 32 MFMA tiles each). Each wave tile is shared by two
 // compute waves on the same SIMD, which take the first and the second half
 // of every stage's K-blocks and add their accumulators through LDS at the
-// end of the tile (Q4_K-style: one compute wave per wave tile, see ks_of).
+// end of the tile.
 // The scale step is fp32 VALU work and a single wave issues independent
 // fp32 FMAs at only about half the SIMD's rate, so two waves per SIMD split
 // it; every operand and scale is still read from LDS once. A stage holds 8
 // K-blocks of W and X in LDS, unpacked to int8 rows of 32 bytes plus fp32
 // scales, so every MFMA operand is one 16-byte LDS read.
 //
-// Pipeline: a workgroup has eight compute waves and eight loader waves
-// (Q4_K-style: four and four). Loader waves hold kDepth stages of raw blocks
+// Pipeline: a workgroup has eight compute waves and eight loader waves.
+// Loader waves hold kDepth stages of raw blocks
 // in registers (stage s+1+kDepth is requested while stage s is computed),
 // unpack stage s+1 into the free half of a two-stage LDS buffer, and meet the
 // compute waves at one barrier per stage. Compute waves keep only
@@ -66,16 +66,13 @@ constexpr int kKB = 8;  // K-blocks per stage
 constexpr int kNT = QMAT_GEMM_NT;  // 32-column MFMA tiles per compute wave
 constexpr int kTileWaves = kRT * kCT / kNT;  // wave tiles per workgroup tile
 // Compute waves per wave tile (each takes kKB / ks_of(FMT) blocks of every
-// stage). Q4_K-style stays at one, with the pipelined stage below: its min
-// term needs registers that a split leaves it without (measured: it spills).
-constexpr int ks_of(int fmt) { return fmt == kFmtQ4_K ? 1 : 2; }
+// stage).
+constexpr int ks_of(int) { return 2; }
 constexpr int threads_of(int fmt) { return kWave * kTileWaves * ks_of(fmt); }  // compute threads
-// Loader waves. The loaders' unpacking and LDS writes are the critical path
-// of a stage (they reach the stage barrier last), so the split formats use
-// eight: two per SIMD, each with half the items, at four waves per SIMD and
-// 128 registers. Q4_K-style's single compute wave per tile needs more
-// registers than a third wave per SIMD would leave.
-constexpr int loaders_of(int fmt) { return fmt == kFmtQ4_K ? 4 : 8; }
+// Loader waves: eight, two per SIMD, each with half the items of a stage
+// (with four, their unpacking and LDS writes ran behind the compute waves and
+// set the stage length), at four waves per SIMD and 128 registers.
+constexpr int loaders_of(int) { return 8; }
 constexpr int load_threads_of(int fmt) { return kWave * loaders_of(fmt); }
 constexpr int kDepth = QMAT_GEMM_DEPTH;  // stages a loader thread holds in registers
 constexpr uint32_t kMagicI = 0x4B400000u;  // 1.5 * 2^23 as fp32 bits
@@ -194,39 +191,6 @@ __device__ __forceinline__ void load_ops(const Stage& cur, int bb, int wm, int w
     op.b[t] = *reinterpret_cast<const i32x4*>(cur.x(bb, half, (wn0 + t) * 32 + l32));
 }
 
-template <int NT>
-__device__ __forceinline__ void load_dw(const Stage& cur, int bb, int wm, int half,
-                                        float (&dw)[16]) {
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const f32x4 t = *reinterpret_cast<const f32x4*>(&cur.wd[bb][wm * 32 + 8 * q + 4 * half]);
-    dw[4 * q + 0] = t.x;
-    dw[4 * q + 1] = t.y;
-    dw[4 * q + 2] = t.z;
-    dw[4 * q + 3] = t.w;
-  }
-}
-
-// acc += dw * (S * dx): S * dx = fma(F, dx, c1) with c1 = -1.5 * 2^23 * dx
-// (see apply_scales); two passes of independent instructions.
-template <int NT>
-__device__ __forceinline__ void apply_block(const float (&dw)[16], const float (&dx)[NT],
-                                            const float (&c1)[NT], const i32x16 (&d)[NT],
-                                            float (&acc)[NT][16]) {
-  f32x16 df[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    df[t] = __builtin_bit_cast(f32x16, d[t]);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) df[t][i] = fmaf(df[t][i], dx[t], c1[t]);
-  }
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int t = 0; t < NT; ++t)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) acc[t][i] = fmaf(df[t][i], dw[i], acc[t][i]);
-}
-
 // Per-block scales a lane needs: dw of its 16 rows and dx of its column in
 // each of the NT tiles.
 template <int NT>
@@ -279,11 +243,13 @@ __device__ __forceinline__ void apply_scales(const Scales<NT>& sc, const i32x16 
 // acc -= O[m, b] * xs[n, b] summed over the two blocks, as one fp32 MFMA
 // (32 x 32 x 2) whose output layout is that of the int8 MFMA. Lane l gives
 // A[row l % 32][block l / 32] = -O and B[block l / 32][column l % 32] = xs.
-template <int NT>
+// kGuard = false where both blocks are known to exist: the guarded reads
+// become branches whose registers made the split kernel spill.
+template <int NT, bool kGuard = true>
 __device__ __forceinline__ void min_term(const Stage& cur, int b0, int nbs, int wm, int wn0,
                                          int l32, int half, float (&acc)[NT][16]) {
   const int b = b0 + half;
-  const bool ok = b < nbs;
+  const bool ok = !kGuard || b < nbs;
   const float a = ok ? cur.wo[b][wm * 32 + l32] : 0.0f;
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
@@ -528,46 +494,6 @@ __device__ __forceinline__ void compute_range(const Stage& cur, int b0, int b1, 
                                               float (&acc)[NT][16]) {
   if (FMT == kFmtQ6_K) {
     compute_range_q6<NT>(cur, b0, b1, wm, wn0, l32, half, cmagic, acc);
-  } else if (PER == kKB && b1 - b0 == kKB) {
-    // Full stage, software-pipelined: the column scales of all 8 blocks are
-    // read up front; in step bb the MFMAs of block bb+1 are issued
-    // (operands read one step earlier), the operands of block bb+2 and the
-    // row scales of block bb+1 are requested, and block bb is scaled into
-    // the accumulators, so that the LDS, the matrix core and the VALU
-    // overlap.
-    float dxs[kKB][NT], c1s[kKB][NT];
-#pragma unroll
-    for (int bb = 0; bb < kKB; ++bb)
-#pragma unroll
-      for (int t = 0; t < NT; ++t) dxs[bb][t] = cur.xd[bb][(wn0 + t) * 32 + l32];
-    Ops<NT> op[2];
-    float dw[2][16];
-    i32x16 d[2][NT];
-    load_ops(cur, 0, wm, wn0, l32, half, op[0]);
-    load_ops(cur, 1, wm, wn0, l32, half, op[1]);
-    load_dw<NT>(cur, 0, wm, half, dw[0]);
-#pragma unroll
-    for (int bb = 0; bb < kKB; ++bb)
-#pragma unroll
-      for (int t = 0; t < NT; ++t) c1s[bb][t] = -kMagicF * dxs[bb][t];
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-      d[0][t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(op[0].a, op[0].b[t], cmagic, 0, 0, 0);
-#pragma unroll
-    for (int bb = 0; bb < kKB; ++bb) {
-      __builtin_amdgcn_sched_barrier(0);
-      if (bb + 1 < kKB) {
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-          d[(bb + 1) & 1][t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
-              op[(bb + 1) & 1].a, op[(bb + 1) & 1].b[t], cmagic, 0, 0, 0);
-      }
-      if (bb + 2 < kKB) load_ops(cur, bb + 2, wm, wn0, l32, half, op[bb & 1]);
-      if (bb + 1 < kKB) load_dw<NT>(cur, bb + 1, wm, half, dw[(bb + 1) & 1]);
-      __builtin_amdgcn_sched_barrier(0);
-      apply_block(dw[bb & 1], dxs[bb], c1s[bb], d[bb & 1], acc);
-      if (FMT == kFmtQ4_K && (bb & 1)) min_term(cur, bb - 1, kKB, wm, wn0, l32, half, acc);
-    }
   } else if (b1 - b0 == PER) {
     // A full share, unrolled. The other compute wave of the SIMD covers
     // this wave's waits for the LDS and the matrix core (reading block j+1's
@@ -583,7 +509,8 @@ __device__ __forceinline__ void compute_range(const Stage& cur, int b0, int b1, 
         d[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(op.a, op.b[t], cmagic, 0, 0, 0);
       load_scales(cur, b0 + j, wm, wn0, l32, half, sc);
       apply_scales(sc, d, acc);
-      if (FMT == kFmtQ4_K && (j & 1)) min_term(cur, b0 + j - 1, b1, wm, wn0, l32, half, acc);
+      if (FMT == kFmtQ4_K && (j & 1))
+        min_term<NT, false>(cur, b0 + j - 1, b1, wm, wn0, l32, half, acc);
     }
   } else {
     for (int bb = b0; bb < b1; ++bb) {

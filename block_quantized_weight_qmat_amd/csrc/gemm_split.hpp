@@ -81,8 +81,8 @@ inline int gemm_splits(int fmt, int64_t M, int64_t K, int64_t N) {
 // 4096 x 11008, 17.4 at 11008 x 4096), half that for chunks of up to 4
 // tokens (the row-per-wave kernel). Measured against a fixed limit of 48
 // tokens: 4096 x 11008 at 56 / 64 tokens 59.0 -> 43.5 / 44.9 us (Q4_0) and
-// 87.6 -> 53.2 / 53.6 (Q4_K-style); 11008 x 4096 Q4_0 at 24 / 48 tokens
-// 28.5 / 48.2 -> 25.8 / 26.4.
+// 79.8 / 80.0 -> 53.0 / 53.5 (Q4_K-style); 11008 x 4096 Q4_0 at 24 / 48
+// tokens 28.5 / 48.2 -> 25.8 / 26.4.
 constexpr int64_t kDecodeMaxN = 64;
 inline bool gemm_uses_decode(int fmt, int64_t M, int64_t K, int64_t N) {
   using namespace split;
