@@ -23,7 +23,9 @@ Timing, two passes:
     first filled with a GPU sleep long enough for the host to enqueue the
     whole batch behind it (checked, and lengthened if the sleep ended first),
     so the events see the GPU's own time per launch, which agrees with
-    rocprofv3's kernel durations.
+    rocprofv3's kernel durations. Each kernel is timed in three such
+    batches, interleaved with the others; its time is their median
+    (``us``), their spread ``us_range``.
 
 Beside the step, every other workload of the measurement plan is timed per
 kernel (``kernels``): the 1024x1024 Q4_0 GEMV (latency); the 196-matrix
@@ -57,6 +59,7 @@ import json
 import math
 import os
 import re
+import statistics
 import sys
 import time
 
@@ -93,6 +96,7 @@ GEMV_EXTRA = [("gemv_q4_0_1024x1024", 0, "gemv_1024"),
               ("gemv_q4_k_4096x4096_spread", 2, "q4k_0"),
               ("gemv_q4_k_4096x11008_spread", 2, "q4k_1")]
 # the Qwen3-like set as one qmat_gemv_batch call, and as 196 qmat_gemv calls
+TIMING_BATCHES = 3  # timed batches per kernel; the median is reported
 QWEN3_OPS = ["qwen3_pass_q4_0", "qwen3_pass_q8_0", "qwen3_launches_q4_0", "qwen3_launches_q8_0"]
 # prompts of a few dozen to a few hundred tokens: the same layer through
 # qmat_gemm (128 x 64 tiles, or the decode batch up to 48 tokens) and through
@@ -558,10 +562,22 @@ def main():
     # ------------------------------------------------------------ kernels
     nb = args.batch if args.batch > 0 else max(args.steps, 50)
     nq = len(inputs.qwen3_shapes())
-    mean_us = {name: (timed_batch(torch, fn, max(4, nb // 10),
-                                  nq if name.startswith("qwen3_launches") else 8)
-                      if name in QWEN3_OPS else timed_batch(torch, fn, nb))
-               for name, fn in ops + extra if name != "copy"}
+
+    def batch_us(name, fn):
+        if name in QWEN3_OPS:
+            return timed_batch(torch, fn, max(4, nb // 10),
+                               nq if name.startswith("qwen3_launches") else 8)
+        return timed_batch(torch, fn, nb)
+
+    # every kernel: the median of TIMING_BATCHES batches (one batch can
+    # catch the clocks settling), the spread kept beside it
+    runs_us = {name: [] for name, _ in ops + extra if name != "copy"}
+    for rep in range(TIMING_BATCHES):
+        for name, fn in ops + extra:
+            if name != "copy":
+                runs_us[name].append(batch_us(name, fn))
+        print(f"[bench] timing batches {rep + 1}/{TIMING_BATCHES} done", file=sys.stderr, flush=True)
+    mean_us = {name: statistics.median(r) for name, r in runs_us.items()}
 
     kernels = {}
     for name, us in mean_us.items():
@@ -619,6 +635,9 @@ def main():
             tops = gemm_ops / us / 1e6
             kernels[name] = {"us": us, "int8_ops": gemm_ops, "TOPS": tops, "bound": "mfma",
                              "frac": tops / INT8_PEAK_TOPS}
+
+    for name, k in kernels.items():
+        k["us_range"] = [round(min(runs_us[name]), 3), round(max(runs_us[name]), 3)]
 
     # ------------------------------------------------------------ parity
     parity = {}
