@@ -1,6 +1,6 @@
 // decode.hip — the decode batch on the int8 matrix cores: Y = W X^T for 5 to
-// 16 tokens per launch, W in Q4_0, Q8_0 or Q4_K-style blocks, X in Q8_0
-// blocks.
+// 16 tokens per launch, W in Q4_0, Q8_0, Q4_K-style or Q6_K-style blocks, X
+// in Q8_0 blocks.
 //
 // Source: "05. llama.cpp：从 GGUF 文件到本地推理服务", sections "槽位、连续批处理与
 // 上下文切分" (several requests decoded at once) and "性能直觉：带宽决定 Decode，
@@ -26,7 +26,13 @@
 // for Q8_0 (and X) two dwords of codes, realigned when the block starts at
 // 0 mod 4 (codes at 2 mod 4); for Q4_K-style the unsigned nibbles of the
 // sub-block's code bytes 4q..4q+3, whose offset term (the sub-block's min
-// times the token's block sum) takes a second MFMA with all-ones weights. The MFMA accumulates onto 1.5 * 2^23, so each
+// times the token's block sum) takes a second MFMA with all-ones weights;
+// for Q6_K-style the 6-bit codes c - 32 of the same elements, rebuilt from
+// the low nibbles and the high-bit words, one MFMA per 16-element half
+// (each half has its own scale; the other half's operand bytes are zero).
+// A Q6_K-style superblock (210 bytes) is not 16-byte aligned in memory: a
+// row's stage is the 14 aligned pieces that cover it, and the lanes read
+// their words at the superblock's offset inside them. The MFMA accumulates onto 1.5 * 2^23, so each
 // integer sum C comes out as the float 1.5 * 2^23 + C (|C| < 2^22) and
 // fma(F, dx, -1.5 * 2^23 * dx) is C * dx rounded once (1.5 dx is exact for
 // an fp16 dx); a second fma adds C * dx * dw to the lane's fp32 sums of rows
@@ -52,12 +58,15 @@ constexpr int kDecRows = 16;   // rows of W per workgroup: the MFMA's A rows
 constexpr int kGroup = 8;      // blocks per stage
 constexpr int kXRowBytes = kGroup * 34;
 
-// Weight formats: Q4_0, Q8_0, or Q4_K-style (a stage is one 144-byte
-// superblock per row).
+// Weight formats: Q4_0, Q8_0, Q4_K-style (a stage is one 144-byte
+// superblock per row) or Q6_K-style (one 210-byte superblock per row, held
+// in LDS as the 224 bytes of 16-byte pieces that cover it).
 template <int kFmt>
 struct DecW {
+  static constexpr bool kQ6 = kFmt == kFmtQ6_K;
   static constexpr int kBytes = kFmt == kFmtQ8_0 ? 34 : 18;  // per block (Q4_K: on average)
-  static constexpr int kRowBytes = kGroup * kBytes;  // one row's share of a stage
+  static constexpr int kGlobalRowBytes = kQ6 ? 210 : kGroup * kBytes;  // a row's stage in memory
+  static constexpr int kRowBytes = kQ6 ? 224 : kGroup * kBytes;  // its LDS slot
   static constexpr int kPiecesPerRow = kRowBytes / 16;
   static constexpr int kPieces = kDecRows * kPiecesPerRow;
   static constexpr int kLoads = (kPieces + kWave - 1) / kWave;
@@ -226,12 +235,16 @@ __global__ __launch_bounds__((DecRing<kFmt, NT>::kWaves * kWave)) void decode_mf
   const int ga = (int)((int64_t)wv * ngroups / kWaves);
   const int gb = (int)((int64_t)(wv + 1) * ngroups / kWaves);
   const int64_t m0 = (int64_t)blockIdx.x * kDecRows;
-  const int64_t rb = (int64_t)ns * WS::kBytes, xrb = (int64_t)ns * 34;
+  const int64_t rb = (int64_t)ngroups * WS::kGlobalRowBytes, xrb = (int64_t)ns * 34;
 
   // Copy sources: piece p = lane + 64 d of a stage is 16 bytes of row (or
   // token) p / pieces-per-row. Rows past M and tokens past N copy the last
   // valid one; their results are not stored.
+  // (Q6_K-style: the row's start and the piece's offset inside the window
+  // of aligned pieces that covers the stage's superblock)
   const uint8_t* wsrc[WS::kLoads];
+  int64_t wrow[WS::kLoads];
+  int wpiece[WS::kLoads];
 #pragma unroll
   for (int d = 0; d < WS::kLoads; ++d) {
     const int p = lane + kWave * d;
@@ -239,6 +252,8 @@ __global__ __launch_bounds__((DecRing<kFmt, NT>::kWaves * kWave)) void decode_mf
     int64_t m = m0 + (r < kDecRows ? r : kDecRows - 1);
     if (m >= M) m = M - 1;
     wsrc[d] = Wb + m * rb + 16 * u;
+    wrow[d] = m * rb;
+    wpiece[d] = 16 * u;
   }
   const uint8_t* xsrc[XS::kLoads];
 #pragma unroll
@@ -257,9 +272,15 @@ __global__ __launch_bounds__((DecRing<kFmt, NT>::kWaves * kWave)) void decode_mf
     const int64_t woff = (int64_t)g * WS::kRowBytes, xoff = (int64_t)g * kXRowBytes;
 #pragma unroll
     for (int d = 0; d < WS::kLoads; ++d)
-      if (lane + kWave * d < WS::kPieces)
-        __builtin_amdgcn_global_load_lds((const void*)(wsrc[d] + woff),
-                                         (lds_ptr_t)(dst + 1024 * d), 16, 0, 0);
+      if (lane + kWave * d < WS::kPieces) {
+        // Q6_K-style: the 14 pieces from the 16-byte boundary at or below
+        // the superblock's start; the last one ends at most 14 bytes past
+        // the superblock, inside the 16-byte granule of its last byte
+        const uint8_t* src =
+            WS::kQ6 ? Wb + ((wrow[d] + (int64_t)g * WS::kGlobalRowBytes) & ~(int64_t)15) + wpiece[d]
+                    : wsrc[d] + woff;
+        __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr_t)(dst + 1024 * d), 16, 0, 0);
+      }
 #pragma unroll
     for (int d = 0; d < XS::kLoads; ++d)
       if (lane + kWave * d < XS::kPieces)
@@ -277,7 +298,65 @@ __global__ __launch_bounds__((DecRing<kFmt, NT>::kWaves * kWave)) void decode_mf
   const int srow = 4 * q + (lane & 3);
   const i32x4 cmagic = {(int)kDecMagicI, (int)kDecMagicI, (int)kDecMagicI, (int)kDecMagicI};
 
+  // Q6_K-style: where the rows of this lane's A operand and of its scales
+  // start (mod 16, all a superblock's offset inside its window depends on)
+  const uint32_t rowA16 = (uint32_t)(((m0 + i16 < M ? m0 + i16 : M - 1) * rb) & 15);
+  const uint32_t rowS16 = (uint32_t)(((m0 + srow < M ? m0 + srow : M - 1) * rb) & 15);
+
   auto compute = [&](int g) {
+    if constexpr (WS::kQ6) {
+      // byte offsets into lds (kept as integers so that the accesses stay
+      // LDS accesses): the lane's A row's superblock and its scale row's
+      const int slot = (int)(ring - lds) + (g % RG::kDepth) * RG::kStage;
+      const int offA = slot + i16 * WS::kRowBytes + (int)((rowA16 + 210u * (uint32_t)g) & 15u);
+      const int offS = slot + srow * WS::kRowBytes + (int)((rowS16 + 210u * (uint32_t)g) & 15u);
+      const uint8_t* xr = lds + slot + WS::kStage + tj * kXRowBytes;
+      const uint32_t* L = reinterpret_cast<const uint32_t*>(lds);
+      // the 4 bytes at an even offset o
+      auto rd = [&](int o) {
+        const int w = o >> 2;
+        return __builtin_amdgcn_alignbyte(L[w + 1], L[w], (uint32_t)(o & 3));
+      };
+      BlockWords bw[kGroup];
+      uint32_t nib[kGroup], h0[kGroup], h1[kGroup], scw[kGroup];
+#pragma unroll
+      for (int k = 0; k < kGroup; ++k) {
+        const int ga = offA + 2 + 26 * k;  // group k of the A row
+        nib[k] = rd(ga + 2 + 4 * q);
+        const int hb = ga + 18, hw = hb >> 2;
+        const uint32_t s3 = (uint32_t)(hb & 3);
+        const uint32_t t0 = L[hw], t1 = L[hw + 1], t2 = L[hw + 2];
+        h0[k] = __builtin_amdgcn_alignbyte(t1, t0, s3);
+        h1[k] = __builtin_amdgcn_alignbyte(t2, t1, s3);
+        scw[k] = *reinterpret_cast<const uint16_t*>(lds + offS + 2 + 26 * k);
+        fetch_x(xr + 34 * k, (k & 1) != 0, q, bw[k]);
+      }
+      const float d = f16_bits_to_f32(*reinterpret_cast<const uint16_t*>(lds + offS));
+#pragma unroll
+      for (int k = 0; k < kGroup; ++k) {
+        // codes 0..63 of elements 4q..4q+3 (low nibbles and H0) and
+        // 16+4q..16+4q+3 (high nibbles and H1), then c - 32 per byte (c + 96
+        // has no carry out of its byte; flipping bit 7 gives c - 32 mod 256)
+        const uint32_t sh = 2u * (uint32_t)q;
+        const uint32_t lo = (nib[k] & 0x0F0F0F0Fu) | (((h0[k] >> sh) & 0x03030303u) << 4);
+        const uint32_t hi = ((nib[k] >> 4) & 0x0F0F0F0Fu) | (((h1[k] >> sh) & 0x03030303u) << 4);
+        const uint64_t a0 = (uint64_t)((lo + 0x60606060u) ^ 0x80808080u);
+        const uint64_t a1 = (uint64_t)((hi + 0x60606060u) ^ 0x80808080u) << 32;
+        const uint64_t b = q8_operand(bw[k].x, (k & 1) != 0);
+        const i32x4 c0 = __builtin_amdgcn_mfma_i32_16x16x32_i8((long)a0, (long)b, cmagic, 0, 0, 0);
+        const i32x4 c1 = __builtin_amdgcn_mfma_i32_16x16x32_i8((long)a1, (long)b, cmagic, 0, 0, 0);
+        const float dx = f16_bits_to_f32(bw[k].dxb);
+        const float mdx = -kDecMagicF * dx;
+        const float S0 = d * (float)(int8_t)(scw[k] & 0xFFu);
+        const float S1 = d * (float)(int8_t)(scw[k] >> 8);
+        const f32x4 F0 = __builtin_bit_cast(f32x4, c0), F1 = __builtin_bit_cast(f32x4, c1);
+        acc[0] = fmaf(fmaf(F1.x, dx, mdx), row_bcast<0>(S1), fmaf(fmaf(F0.x, dx, mdx), row_bcast<0>(S0), acc[0]));
+        acc[1] = fmaf(fmaf(F1.y, dx, mdx), row_bcast<1>(S1), fmaf(fmaf(F0.y, dx, mdx), row_bcast<1>(S0), acc[1]));
+        acc[2] = fmaf(fmaf(F1.z, dx, mdx), row_bcast<2>(S1), fmaf(fmaf(F0.z, dx, mdx), row_bcast<2>(S0), acc[2]));
+        acc[3] = fmaf(fmaf(F1.w, dx, mdx), row_bcast<3>(S1), fmaf(fmaf(F0.w, dx, mdx), row_bcast<3>(S0), acc[3]));
+      }
+      return;
+    }
     const uint8_t* ws = ring + (g % RG::kDepth) * RG::kStage;
     const uint8_t* xs = ws + WS::kStage;
     const uint8_t* wr = ws + i16 * WS::kRowBytes;
@@ -390,8 +469,12 @@ hipError_t launch_dec_fmt(const void* blocks, const void* Xq8, float* Y, int64_t
 #ifndef QMAT_DECODE_MFMA_Q4K
 #define QMAT_DECODE_MFMA_Q4K 1
 #endif
+#ifndef QMAT_DECODE_MFMA_Q6K
+#define QMAT_DECODE_MFMA_Q6K 1
+#endif
 bool decode_mfma_fits(int fmt, int64_t K) {
-  return (fmt == kFmtQ4_0 || fmt == kFmtQ8_0 || (QMAT_DECODE_MFMA_Q4K && fmt == kFmtQ4_K)) &&
+  return (fmt == kFmtQ4_0 || fmt == kFmtQ8_0 || (QMAT_DECODE_MFMA_Q4K && fmt == kFmtQ4_K) ||
+          (QMAT_DECODE_MFMA_Q6K && fmt == kFmtQ6_K)) &&
          K >= 32 * kGroup && K % (32 * kGroup) == 0;
 }
 
@@ -403,8 +486,10 @@ hipError_t launch_decode_mfma(int fmt, const void* blocks, const void* Xq8, floa
       return launch_dec_fmt<kFmtQ4_0>(blocks, Xq8, Y, M, K, N, n0, stream);
     case kFmtQ8_0:
       return launch_dec_fmt<kFmtQ8_0>(blocks, Xq8, Y, M, K, N, n0, stream);
-    default:
+    case kFmtQ4_K:
       return launch_dec_fmt<kFmtQ4_K>(blocks, Xq8, Y, M, K, N, n0, stream);
+    default:
+      return launch_dec_fmt<kFmtQ6_K>(blocks, Xq8, Y, M, K, N, n0, stream);
   }
 }
 

@@ -78,8 +78,10 @@ inline int gemm_splits(int fmt, int64_t M, int64_t K, int64_t N) {
 // chunk of up to 16 tokens of the decode batch
 //   ceil(M / 16 / kSplitTarget) * (0.25 * stages + 2) * d_fmt
 // (one 16-row workgroup per CU and round; 12.9 us per 16-token chunk at
-// 4096 x 11008, 17.4 at 11008 x 4096), half that for chunks of up to 4
-// tokens (the row-per-wave kernel). Measured against a fixed limit of 48
+// 4096 x 11008, 17.4 at 11008 x 4096, for Q4_0; d_fmt scales that by the
+// formats' measured chunk times: 1, 1.2, 1.2 and 1.55 for Q4_0, Q8_0,
+// Q4_K-style and Q6_K-style), half that for chunks of up to 4 tokens (the
+// row-per-wave kernel). Measured against a fixed limit of 48
 // tokens: 4096 x 11008 at 56 / 64 tokens 59.0 -> 43.5 / 44.9 us (Q4_0) and
 // 79.8 / 80.0 -> 53.0 / 53.5 (Q4_K-style); 11008 x 4096 Q4_0 at 24 / 48
 // tokens 28.5 / 48.2 -> 25.8 / 26.4.
@@ -89,7 +91,7 @@ inline bool gemm_uses_decode(int fmt, int64_t M, int64_t K, int64_t N) {
   if (N <= 16) return true;
   if (N > kDecodeMaxN) return false;
   static constexpr double kStageUs[4] = {1.3, 1.35, 1.7, 2.2};  // Q4_0, Q8_0, Q4_K, Q6_K
-  static constexpr double kChunk[4] = {1.0, 1.2, 1.2, 1.75};
+  static constexpr double kChunk[4] = {1.0, 1.2, 1.2, 1.55};
   const int f = fmt >= 0 && fmt < 4 ? fmt : 0;
   const int64_t tiles = ((M + kTileM - 1) / kTileM) * ((N + kTileN - 1) / kTileN);
   const int64_t nst = (K / 32 + kStageBlocks - 1) / kStageBlocks;

@@ -1957,8 +1957,14 @@ namespace qmat {
 // / 21.4); Q4_K-style from 9 (8 tokens: 13.8 against 13.0 us; 12: 15.0
 // against 20.5; 16: 15.2 against 22.1, and 19.6 against 24.8 at 11008 x
 // 4096), its two matrix-core products per block (codes, and the block sums
-// of the tokens for the offset term) costing more arithmetic.
-inline int64_t decode_mfma_min_tokens(int fmt) { return fmt == kFmtQ4_K ? 9 : 5; }
+// of the tokens for the offset term) costing more arithmetic. Q6_K-style
+// (two products per block, one per half) also from 9: 4096 x 11008 at 9 / 16
+// tokens 19.3 / 19.9 us against 23.8 / 25.6; at 5-8 tokens on rows too long
+// for the row-per-wave kernel it loses (4096 x 20480, 8 tokens: 30.6 against
+// 24.5).
+inline int64_t decode_mfma_min_tokens(int fmt) {
+  return fmt == kFmtQ4_K || fmt == kFmtQ6_K ? 9 : 5;
+}
 
 hipError_t launch_gemm_small(int fmt, const void* blocks, const void* Xq8, float* Y, int64_t M,
                              int64_t K, int64_t N, hipStream_t stream) {

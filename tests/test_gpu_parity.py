@@ -652,6 +652,13 @@ def test_gemm_decode_small_n(q, fmt):
         # wrap many times (K = 16384)
         cases += [(97, 256 * 9, n) for n in (1, 2, 3, 4, 5, 8, 9, 15, 16, 17, 33, 48)]
         cases += [(16, 2048, 16), (40, 768, 9), (17, 16384, 16), (300, 256 * 43, 7)]
+    else:
+        # 9 to 16 tokens take the matrix-core kernel (K a multiple of 256):
+        # fewer stages than waves, rings that wrap many times, ragged rows,
+        # and for Q6_K-style superblocks at every offset in their 16-byte
+        # windows (odd superblock counts put rows at every even offset)
+        cases += [(16, 2048, 16), (40, 768, 9), (17, 16384, 16), (300, 256 * 43, 12),
+                  (33, 256 * 43, 16), (21, 256 * 7, 10)]
     for M, K, N in cases:
         say(f"gemm decode fmt={fmt} M={M} K={K} N={N}")
         W = mixed_matrix(rng, M, K) if M > 2 else rng.normal(0, 0.02, (M, K)).astype(np.float32)
