@@ -32,8 +32,9 @@ kernel (``kernels``): the 1024x1024 Q4_0 GEMV (latency); the 196-matrix
 Qwen3-0.6B-like decode set, Q4_0 and Q8_0, as one pass: one qmat_gemv_batch
 call (a few launches), and beside it the same 196 products as 196 qmat_gemv
 launches, each rotating over copies of the whole set; the 11008x4096
-orientation of the 7B layer (the strip kernel); the Q4_K-style GEMV at
-4096x4096 and 4096x11008 with per-row scale spread; the decode batch, the
+orientation of the 7B layer; the Q4_K-style GEMV at 4096x4096 and
+4096x11008 with per-row scale spread; that model's Q6_K-style output head
+(151936x1024, one token's logits); the decode batch, the
 Q6_K-style kernels, the other GEMM formats, the KV-cache write, and the
 activation quantizer on a warm X (what a GEMM prologue would repeat once per
 128-row m-tile). The prefill GEMM reads a different copy of W at every
@@ -94,7 +95,10 @@ DECODE_NS = (4, 16)
 GEMV_EXTRA = [("gemv_q4_0_1024x1024", 0, "gemv_1024"),
               ("gemv_q4_0_11008x4096", 0, "llama7b_1"), ("gemv_q8_0_11008x4096", 1, "llama7b_1"),
               ("gemv_q4_k_4096x4096_spread", 2, "q4k_0"),
-              ("gemv_q4_k_4096x11008_spread", 2, "q4k_1")]
+              ("gemv_q4_k_4096x11008_spread", 2, "q4k_1"),
+              # the Qwen3-0.6B-like output head (tied embedding, q6_K in the
+              # pages' model file): one token's logits over the vocabulary
+              ("gemv_q6_k_lm_head_151936x1024", 3, "lm_head")]
 # the Qwen3-like set as one qmat_gemv_batch call, and as 196 qmat_gemv calls
 TIMING_BATCHES = 3  # timed batches per kernel; the median is reported
 QWEN3_OPS = ["qwen3_pass_q4_0", "qwen3_pass_q8_0", "qwen3_launches_q4_0", "qwen3_launches_q8_0"]
@@ -457,6 +461,8 @@ def main():
             Wn, xn = inputs.gemv_1024()
         elif wl.startswith("llama7b_"):
             Wn, xn = inputs.llama7b_layer(int(wl[-1]))
+        elif wl == "lm_head":
+            Wn, xn = inputs.qwen3_lm_head()
         else:
             Wn, xn = inputs.q4k_rows(int(wl[-1]))
         pk = binding.quantize(fi, torch.from_numpy(Wn).to(dev))

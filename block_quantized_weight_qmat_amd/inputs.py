@@ -20,6 +20,9 @@ themselves are not available, so these stand in for them):
     with 1% of the 32-element blocks of each matrix holding one outlier of
     +-10 standard deviations (+-0.2) at a uniformly drawn position; one
     x ~ N(0, 1) per matrix.
+  * ``qwen3_lm_head``: that model's output head, the tied token embedding
+    (vocabulary 151936 x hidden 1024, a q6_K tensor in the pages' model
+    file), W ~ N(0, 0.02^2) with the same 1% outlier blocks, x ~ N(0, 1).
   * ``llama7b_layer``: W 4096x11008 and 11008x4096 ~ N(0, 0.02^2),
     x ~ N(0, 1).
   * ``q4k_rows``: W 4096x4096 and 4096x11008, N(0, 0.02^2) times a per-row
@@ -99,6 +102,17 @@ def qwen3_matrix(i: int, seed: int = 0):
     W = with_outlier_blocks(W, seed, 3 * i + 1)
     x = normal((K,), 1.0, seed, 3 * i + 2)
     return name, W, x
+
+
+QWEN3_VOCAB = 151936
+
+
+def qwen3_lm_head(seed: int = 0):
+    """(W, x) of the Qwen3-0.6B-like output head: vocabulary x hidden."""
+    W = normal((QWEN3_VOCAB, 1024), WEIGHT_STD, seed, 600)
+    W = with_outlier_blocks(W, seed, 601)
+    x = normal((1024,), 1.0, seed, 602)
+    return W, x
 
 
 LLAMA7B_SHAPES = ((4096, 11008), (11008, 4096))

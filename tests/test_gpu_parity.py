@@ -444,6 +444,18 @@ def test_gemv_workloads_full(q):
             check_close(y, ref, GEMV_TOL, f"gemv q4k_rows {W.shape} fmt={fmt}")
 
 
+def test_gemv_lm_head_full(q):
+    """The Qwen3-like output head, 151936 x 1024 (a q6_K tensor in the pages'
+    model file; Q4_0 as well): every row against the oracle, and the GPU
+    quantizer's bytes against the oracle's."""
+    W, x = inputs.qwen3_lm_head()
+    for fmt in (3, 0):
+        say(f"gemv lm_head fmt={fmt}")
+        y, ref, B = gemv_case(q, fmt, W, x)
+        check_close(y, ref, GEMV_TOL, f"gemv lm_head fmt={fmt}")
+        assert_bytes(gpu_quantize(q, fmt, W), B, f"quantize lm_head fmt={fmt}")
+
+
 def test_gemv_qwen3_decode_set(q):
     worst = {0: 0.0, 1: 0.0}
     for i in range(len(inputs.qwen3_shapes())):
