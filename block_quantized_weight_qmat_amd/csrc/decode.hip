@@ -82,17 +82,25 @@ struct DecX {
   static constexpr int kStage = NT * kXRowBytes;
 };
 
-// Per wave: a ring of kDepth stages (weights and tokens). As many waves as
-// 160 KB of LDS allows with a ring of at least two stages (16, 12 or 8: the
-// waves hide each other's LDS and matrix-core latency), each with the
-// deepest ring that then fits.
-template <int kFmt, int NT>
+// Per wave: a ring of kDepth stages (weights and tokens). Up to one
+// workgroup per CU (at most 256 workgroups): as many waves as 160 KB of LDS
+// allows with a ring of at least two stages (16, 12 or 8: the waves hide
+// each other's LDS and matrix-core latency), each with the deepest ring
+// that then fits. Taller matrices (kTall: more 16-row workgroups than CUs)
+// take 4 waves with rings of 2 stages instead, 27-70 KB per workgroup, so
+// that two or more workgroups share a CU and hide each other's copy
+// latency; measured at 16 tokens, 11008 x 4096: Q4_0 17.7 -> 13.4 us, Q8_0
+// 21.1 -> 16.6, Q4_K-style 19.4 -> 15.2, Q6_K-style 28.0 -> 23.9 (also
+// 14336 and 28672 x 4096, 11008 x 2048, 8192 x 8192); with 4096 rows the
+// one-workgroup shape stays ahead (Q4_0 4096 x 11008: 12.9 against 14.8).
+template <int kFmt, int NT, bool kTall>
 struct DecRing {
   static constexpr int kStage = DecW<kFmt>::kStage + DecX<NT>::kStage;
   static constexpr int depth_for(int waves) { return 163840 / waves / kStage; }
-  static constexpr int kWaves = depth_for(16) >= 2 ? 16 : depth_for(12) >= 2 ? 12 : 8;
+  static constexpr int kWaves =
+      kTall ? 4 : depth_for(16) >= 2 ? 16 : depth_for(12) >= 2 ? 12 : 8;
   static constexpr int kDepth0 = depth_for(kWaves);
-  static constexpr int kDepth = kDepth0 > 6 ? 6 : kDepth0;
+  static constexpr int kDepth = kTall ? 2 : kDepth0 > 6 ? 6 : kDepth0;
   static constexpr int kLoads = DecW<kFmt>::kLoads + DecX<NT>::kLoads;
   static constexpr int kWaveLds = kDepth * kStage;
   static_assert(kDepth >= 2 && (kDepth - 1) * kLoads < 64, "ring");
@@ -217,14 +225,14 @@ __device__ __forceinline__ float row_bcast(float s) {
                                                                0x150 + v, 0xF, 0xF, false));
 }
 
-template <int kFmt, int NT>
-__global__ __launch_bounds__((DecRing<kFmt, NT>::kWaves * kWave)) void decode_mfma_kernel(
+template <int kFmt, int NT, bool kTall>
+__global__ __launch_bounds__((DecRing<kFmt, NT, kTall>::kWaves * kWave)) void decode_mfma_kernel(
     const uint8_t* __restrict__ Wb, const uint8_t* __restrict__ Xq, float* __restrict__ Y,
     int64_t M, int K, int64_t N, int64_t n0) {
   constexpr bool kQ4 = kFmt == kFmtQ4_0, kQ4K = kFmt == kFmtQ4_K;
   using WS = DecW<kFmt>;
   using XS = DecX<NT>;
-  using RG = DecRing<kFmt, NT>;
+  using RG = DecRing<kFmt, NT, kTall>;
   constexpr int kWaves = RG::kWaves;
   __shared__ __attribute__((aligned(16))) uint8_t lds[kWaves * RG::kWaveLds];
   const int lane = (int)(threadIdx.x & 63);
@@ -446,13 +454,22 @@ __global__ __launch_bounds__((DecRing<kFmt, NT>::kWaves * kWave)) void decode_mf
   }
 }
 
+constexpr int64_t kDecOneRound = 256;  // workgroups of one round (the CUs of an MI355X)
+
 template <int kFmt, int NT>
 hipError_t launch_dec(const void* blocks, const void* Xq8, float* Y, int64_t M, int64_t K,
                       int64_t N, int64_t n0, hipStream_t stream) {
   const int64_t grid = (M + kDecRows - 1) / kDecRows;
-  hipLaunchKernelGGL((decode_mfma_kernel<kFmt, NT>), dim3((unsigned)grid),
-                     dim3(DecRing<kFmt, NT>::kWaves * kWave), 0, stream, static_cast<const uint8_t*>(blocks),
-                     static_cast<const uint8_t*>(Xq8), Y, M, (int)K, N, n0);
+  if (grid > kDecOneRound)
+    hipLaunchKernelGGL((decode_mfma_kernel<kFmt, NT, true>), dim3((unsigned)grid),
+                       dim3(DecRing<kFmt, NT, true>::kWaves * kWave), 0, stream,
+                       static_cast<const uint8_t*>(blocks), static_cast<const uint8_t*>(Xq8), Y, M,
+                       (int)K, N, n0);
+  else
+    hipLaunchKernelGGL((decode_mfma_kernel<kFmt, NT, false>), dim3((unsigned)grid),
+                       dim3(DecRing<kFmt, NT, false>::kWaves * kWave), 0, stream,
+                       static_cast<const uint8_t*>(blocks), static_cast<const uint8_t*>(Xq8), Y, M,
+                       (int)K, N, n0);
   return hipGetLastError();
 }
 

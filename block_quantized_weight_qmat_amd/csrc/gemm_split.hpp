@@ -76,12 +76,13 @@ inline int gemm_splits(int fmt, int64_t M, int64_t K, int64_t N) {
 // (s_fmt about 1.3 us per stage for Q4_0 while at most one round of
 // workgroups runs, scaled by the formats' measured GEMM times), and each
 // chunk of up to 16 tokens of the decode batch
-//   ceil(M / 16 / kSplitTarget) * (0.25 * stages + 2) * d_fmt
-// (one 16-row workgroup per CU and round; 12.9 us per 16-token chunk at
-// 4096 x 11008, 17.4 at 11008 x 4096, for Q4_0; d_fmt scales that by the
-// formats' measured chunk times: 1, 1.2, 1.2 and 1.55 for Q4_0, Q8_0,
-// Q4_K-style and Q6_K-style), half that for chunks of up to 4 tokens (the
-// row-per-wave kernel). Measured against a fixed limit of 48
+//   (3.5 + 0.2 * M * K / 10^6) * d_fmt
+// (a fit of the matrix-core kernel's Q4_0 times at 16 tokens: 12.9 us at
+// 4096 x 11008, 6.3 at 4096 x 4096, 13.4 at 11008 x 4096, 16.9 at
+// 14336 x 4096, 26.5 at 28672 x 4096, 7.9 at 11008 x 2048, 16.0 at
+// 8192 x 8192; d_fmt scales it by the formats' measured chunk times: 1,
+// 1.2, 1.2 and 1.55 for Q4_0, Q8_0, Q4_K-style and Q6_K-style), half that
+// for chunks of up to 4 tokens (the row-per-wave kernel). Measured against a fixed limit of 48
 // tokens: 4096 x 11008 at 56 / 64 tokens 59.0 -> 43.5 / 44.9 us (Q4_0) and
 // 79.8 / 80.0 -> 53.0 / 53.5 (Q4_K-style); 11008 x 4096 Q4_0 at 24 / 48
 // tokens 28.5 / 48.2 -> 25.8 / 26.4.
@@ -97,8 +98,7 @@ inline bool gemm_uses_decode(int fmt, int64_t M, int64_t K, int64_t N) {
   const int64_t nst = (K / 32 + kStageBlocks - 1) / kStageBlocks;
   const double t_tiles =
       (double)((tiles + kSplitTarget - 1) / kSplitTarget) * (double)(nst + kFillStages) * kStageUs[f];
-  const double chunk = (double)(((M + 15) / 16 + kSplitTarget - 1) / kSplitTarget) *
-                       (0.25 * (double)nst + 2.0);
+  const double chunk = 3.5 + 0.2e-6 * (double)M * (double)K;
   const int64_t tail = N % 16;
   const double t_dec = (double)(N / 16) * chunk * kChunk[f] +
                        (tail == 0 ? 0.0 : tail <= 4 ? 0.5 * chunk : chunk * kChunk[f]);
