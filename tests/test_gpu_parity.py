@@ -681,6 +681,25 @@ def test_gemm_decode_small_n(q, fmt):
 
 
 @pytest.mark.parametrize("fmt", [0, 1, 2, 3])
+def test_gemm_decode_tall(q, fmt):
+    """The matrix-core decode kernel's shape for matrices of more than 4096
+    rows (more 16-row workgroups than CUs: 4 waves, 2-stage rings): just
+    past the switch, ragged rows, 9 and 16 tokens, the 11008x4096 layer, and
+    for Q4_0 an 8-token chunk on rows too long for the row-per-wave kernel;
+    every output against the oracle."""
+    rng = np.random.default_rng(760 + fmt)
+    cases = [(4097, 1024, 16), (4200, 2304, 9), (5003, 256 * 7, 12), (11008, 4096, 16)]
+    if fmt == 0:
+        cases += [(5000, 8192, 8), (4352, 8192, 5)]
+    for M, K, N in cases:
+        say(f"gemm decode tall fmt={fmt} M={M} K={K} N={N}")
+        W = rng.normal(0, 0.02, (M, K)).astype(np.float32)
+        X = rng.normal(0, 1, (N, K)).astype(np.float32)
+        Y, ref = gemm_case(q, fmt, W, X)
+        check_close(Y, ref, GEMM_TOL, f"gemm decode tall fmt={fmt} M={M} K={K} N={N}")
+
+
+@pytest.mark.parametrize("fmt", [0, 1, 2, 3])
 def test_gemm_decode_rows_limits(q, fmt):
     """The few-token row-per-wave kernel at the edges of what it takes: one
     slice per row, rows of 8 strips at 4 tokens (80 KB of LDS), 7 strips at
