@@ -9,7 +9,8 @@
 // per-token arithmetic stays off the critical path.
 //
 // Work split. A workgroup owns 16 rows of W and all of K; its waves (16, 12
-// or 8, as LDS allows) take contiguous shares of the rows' stages. A stage
+// or 8, as LDS allows; 4 with shallow rings when there are more workgroups
+// than CUs, see DecRing) take contiguous shares of the rows' stages. A stage
 // is 8 blocks of every row (144 or 272 bytes per row) and of every token
 // (272 bytes): both are whole 16-byte pieces, so the copies go from memory
 // straight into LDS (global_load_lds, 64 pieces per instruction). Each wave keeps its own ring
