@@ -298,7 +298,9 @@ def test_gemv_small_and_ragged(q, fmt):
               # and last sizes, an odd strip count, and just past its limit
               (33, 8192), (20, 16384), (18, 256 * 33), (7, 256 * 65),
               # rows of at most 32 slices: both halves of a wave take rows
-              (40, 256), (33, 768), (16, 1024), (2, 1024), (100, 512)]
+              (40, 256), (33, 768), (16, 1024), (2, 1024), (100, 512),
+              # a million elements per row: many passes of the strip kernel
+              (3, 1 << 20), (70, 1 << 17)]
     if fmt < 2:
         shapes += [(1, 32), (5, 32 * 37), (2, 64), (40, 32 * 1001), (100, 32 * 345),
                    (65, 32 * 1001), (130, 32 * 65), (19, 32 * 257), (21, 32 * 511),
@@ -633,7 +635,10 @@ def test_gemm_small_and_ragged(q, fmt):
               # 8 and 16 tiles of 128 x 64: the XCD-aware tile order
               (256, 1024, 256), (1024, 512, 128),
               # a few hundred tokens: part of the GPU idle, ragged last tiles
-              (1000, 768, 300)]
+              (1000, 768, 300),
+              # long rows: 128 stages per tile; and a decode-batch chunk
+              # with 256 stages per row
+              (200, 32768, 80), (130, 65536, 20)]
     if fmt < 2:
         shapes += [(1, 32, 1), (33, 32 * 37, 5), (65, 32 * 5, 66)]
         # last stages of 3, 4 and 7 blocks: the two compute waves of a tile
