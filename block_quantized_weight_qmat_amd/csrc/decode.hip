@@ -94,14 +94,24 @@ struct DecX {
 // 21.1 -> 16.6, Q4_K-style 19.4 -> 15.2, Q6_K-style 28.0 -> 23.9 (also
 // 14336 and 28672 x 4096, 11008 x 2048, 8192 x 8192); with 4096 rows the
 // one-workgroup shape stays ahead (Q4_0 4096 x 11008: 12.9 against 14.8).
-template <int kFmt, int NT, bool kTall>
+// kLong: the 4-bit formats at 16 tokens on rows of at least 24 stages
+// (K >= 6144) take 8 waves instead of 12, with 3 or more stages each:
+// 4096 x 11008 Q4_0 13.3 -> 12.6 us, Q4_K-style 15.4 -> 14.6 (4096 x 6144
+// to 4096 x 14336 and 3072 x 11008 alike, 4-6% for Q4_K-style); at
+// K = 4096 the 12 waves stay ahead (Q4_0 6.3 against 6.6 us).
+enum DecShape { kDecOne = 0, kDecTall = 1, kDecLong = 2 };
+template <int kFmt, int NT, int kShape>
 struct DecRing {
+  static constexpr bool kTall = kShape == kDecTall;
   static constexpr int kStage = DecW<kFmt>::kStage + DecX<NT>::kStage;
   static constexpr int depth_for(int waves) { return 163840 / waves / kStage; }
-  static constexpr int kWaves =
-      kTall ? 4 : depth_for(16) >= 2 ? 16 : depth_for(12) >= 2 ? 12 : 8;
+  static constexpr int kWaves = kTall ? 4
+                                : kShape == kDecLong ? 8
+                                : depth_for(16) >= 2 ? 16
+                                : depth_for(12) >= 2 ? 12
+                                                     : 8;
   static constexpr int kDepth0 = depth_for(kWaves);
-  static constexpr int kDepth = kTall ? 2 : kDepth0 > 6 ? 6 : kDepth0;
+  static constexpr int kDepth = kTall || kShape == kDecLong ? 2 : kDepth0 > 6 ? 6 : kDepth0;
   static constexpr int kLoads = DecW<kFmt>::kLoads + DecX<NT>::kLoads;
   static constexpr int kWaveLds = kDepth * kStage;
   static_assert(kDepth >= 2 && (kDepth - 1) * kLoads < 64, "ring");
@@ -226,14 +236,14 @@ __device__ __forceinline__ float row_bcast(float s) {
                                                                0x150 + v, 0xF, 0xF, false));
 }
 
-template <int kFmt, int NT, bool kTall>
-__global__ __launch_bounds__((DecRing<kFmt, NT, kTall>::kWaves * kWave)) void decode_mfma_kernel(
+template <int kFmt, int NT, int kShape>
+__global__ __launch_bounds__((DecRing<kFmt, NT, kShape>::kWaves * kWave)) void decode_mfma_kernel(
     const uint8_t* __restrict__ Wb, const uint8_t* __restrict__ Xq, float* __restrict__ Y,
     int64_t M, int K, int64_t N, int64_t n0) {
   constexpr bool kQ4 = kFmt == kFmtQ4_0, kQ4K = kFmt == kFmtQ4_K;
   using WS = DecW<kFmt>;
   using XS = DecX<NT>;
-  using RG = DecRing<kFmt, NT, kTall>;
+  using RG = DecRing<kFmt, NT, kShape>;
   constexpr int kWaves = RG::kWaves;
   __shared__ __attribute__((aligned(16))) uint8_t lds[kWaves * RG::kWaveLds];
   const int lane = (int)(threadIdx.x & 63);
@@ -457,21 +467,29 @@ __global__ __launch_bounds__((DecRing<kFmt, NT, kTall>::kWaves * kWave)) void de
 
 constexpr int64_t kDecOneRound = 256;  // workgroups of one round (the CUs of an MI355X)
 
+constexpr int64_t kDecLongK = 6144;
+
+template <int kFmt, int NT, int kShape>
+hipError_t launch_dec_shape(const void* blocks, const void* Xq8, float* Y, int64_t M, int64_t K,
+                            int64_t N, int64_t n0, int64_t grid, hipStream_t stream) {
+  hipLaunchKernelGGL((decode_mfma_kernel<kFmt, NT, kShape>), dim3((unsigned)grid),
+                     dim3(DecRing<kFmt, NT, kShape>::kWaves * kWave), 0, stream,
+                     static_cast<const uint8_t*>(blocks), static_cast<const uint8_t*>(Xq8), Y, M,
+                     (int)K, N, n0);
+  return hipGetLastError();
+}
+
 template <int kFmt, int NT>
 hipError_t launch_dec(const void* blocks, const void* Xq8, float* Y, int64_t M, int64_t K,
                       int64_t N, int64_t n0, hipStream_t stream) {
   const int64_t grid = (M + kDecRows - 1) / kDecRows;
   if (grid > kDecOneRound)
-    hipLaunchKernelGGL((decode_mfma_kernel<kFmt, NT, true>), dim3((unsigned)grid),
-                       dim3(DecRing<kFmt, NT, true>::kWaves * kWave), 0, stream,
-                       static_cast<const uint8_t*>(blocks), static_cast<const uint8_t*>(Xq8), Y, M,
-                       (int)K, N, n0);
-  else
-    hipLaunchKernelGGL((decode_mfma_kernel<kFmt, NT, false>), dim3((unsigned)grid),
-                       dim3(DecRing<kFmt, NT, false>::kWaves * kWave), 0, stream,
-                       static_cast<const uint8_t*>(blocks), static_cast<const uint8_t*>(Xq8), Y, M,
-                       (int)K, N, n0);
-  return hipGetLastError();
+    return launch_dec_shape<kFmt, NT, kDecTall>(blocks, Xq8, Y, M, K, N, n0, grid, stream);
+  if constexpr ((kFmt == kFmtQ4_0 || kFmt == kFmtQ4_K) && NT == 16) {
+    if (K >= kDecLongK)
+      return launch_dec_shape<kFmt, NT, kDecLong>(blocks, Xq8, Y, M, K, N, n0, grid, stream);
+  }
+  return launch_dec_shape<kFmt, NT, kDecOne>(blocks, Xq8, Y, M, K, N, n0, grid, stream);
 }
 
 template <int kFmt>
