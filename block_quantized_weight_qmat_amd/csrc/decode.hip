@@ -94,11 +94,13 @@ struct DecX {
 // 21.1 -> 16.6, Q4_K-style 19.4 -> 15.2, Q6_K-style 28.0 -> 23.9 (also
 // 14336 and 28672 x 4096, 11008 x 2048, 8192 x 8192); with 4096 rows the
 // one-workgroup shape stays ahead (Q4_0 4096 x 11008: 12.9 against 14.8).
-// kLong: the 4-bit formats at 16 tokens on rows of at least 24 stages
-// (K >= 6144) take 8 waves instead of 12, with 3 or more stages each:
-// 4096 x 11008 Q4_0 13.3 -> 12.6 us, Q4_K-style 15.4 -> 14.6 (4096 x 6144
-// to 4096 x 14336 and 3072 x 11008 alike, 4-6% for Q4_K-style); at
-// K = 4096 the 12 waves stay ahead (Q4_0 6.3 against 6.6 us).
+// kDecLong: rows of at least 24 stages (K >= 6144) take 8 waves with 2-stage
+// rings (3 or more stages per wave) where the one-round shape would run
+// 12 or 16: 16 tokens at 4096 x 11008 Q4_0 13.3 -> 12.6 us, Q4_K-style
+// 15.4 -> 14.6 (4096 x 6144 to 4096 x 14336 and 3072 x 11008 alike); 5-8
+// tokens of Q4_0, 4096 x 14336: 14.3 -> 12.9; Q8_0 and Q6_K-style at 16
+// tokens run 8 waves either way. At K = 4096 the 12 waves stay ahead (Q4_0
+// 6.3 against 6.6 us).
 enum DecShape { kDecOne = 0, kDecTall = 1, kDecLong = 2 };
 template <int kFmt, int NT, int kShape>
 struct DecRing {
@@ -485,10 +487,8 @@ hipError_t launch_dec(const void* blocks, const void* Xq8, float* Y, int64_t M, 
   const int64_t grid = (M + kDecRows - 1) / kDecRows;
   if (grid > kDecOneRound)
     return launch_dec_shape<kFmt, NT, kDecTall>(blocks, Xq8, Y, M, K, N, n0, grid, stream);
-  if constexpr ((kFmt == kFmtQ4_0 || kFmt == kFmtQ4_K) && NT == 16) {
-    if (K >= kDecLongK)
-      return launch_dec_shape<kFmt, NT, kDecLong>(blocks, Xq8, Y, M, K, N, n0, grid, stream);
-  }
+  if (K >= kDecLongK)
+    return launch_dec_shape<kFmt, NT, kDecLong>(blocks, Xq8, Y, M, K, N, n0, grid, stream);
   return launch_dec_shape<kFmt, NT, kDecOne>(blocks, Xq8, Y, M, K, N, n0, grid, stream);
 }
 
