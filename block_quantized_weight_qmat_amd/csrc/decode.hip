@@ -485,7 +485,7 @@ template <int kFmt, int NT>
 hipError_t launch_dec(const void* blocks, const void* Xq8, float* Y, int64_t M, int64_t K,
                       int64_t N, int64_t n0, hipStream_t stream) {
   const int64_t grid = (M + kDecRows - 1) / kDecRows;
-  if (grid > kDecOneRound)
+  if (decode_mfma_tall(M))
     return launch_dec_shape<kFmt, NT, kDecTall>(blocks, Xq8, Y, M, K, N, n0, grid, stream);
   if (K >= kDecLongK)
     return launch_dec_shape<kFmt, NT, kDecLong>(blocks, Xq8, Y, M, K, N, n0, grid, stream);
@@ -513,6 +513,8 @@ bool decode_mfma_fits(int fmt, int64_t K) {
           (QMAT_DECODE_MFMA_Q6K && fmt == kFmtQ6_K)) &&
          K >= 32 * kGroup && K % (32 * kGroup) == 0;
 }
+
+bool decode_mfma_tall(int64_t M) { return (M + kDecRows - 1) / kDecRows > kDecOneRound; }
 
 hipError_t launch_decode_mfma(int fmt, const void* blocks, const void* Xq8, float* Y, int64_t M,
                               int64_t K, int64_t N, int64_t n0, hipStream_t stream) {

@@ -1961,9 +1961,12 @@ namespace qmat {
 // (two products per block, one per half) also from 9: 4096 x 11008 at 9 / 16
 // tokens 19.3 / 19.9 us against 23.8 / 25.6; at 5-8 tokens on rows too long
 // for the row-per-wave kernel it loses (4096 x 20480, 8 tokens: 30.6 against
-// 24.5).
-inline int64_t decode_mfma_min_tokens(int fmt) {
-  return fmt == kFmtQ4_K || fmt == kFmtQ6_K ? 9 : 5;
+// 24.5). On tall matrices (the kernel's shape with several workgroups per
+// CU) Q4_K-style takes it from 5 tokens too: 11008 x 4096 at 5 / 8 tokens
+// 13.1 / 13.4 us against the strip kernel's 15.6 / 16.0.
+inline int64_t decode_mfma_min_tokens(int fmt, int64_t M) {
+  if (fmt == kFmtQ4_K) return decode_mfma_tall(M) ? 5 : 9;
+  return fmt == kFmtQ6_K ? 9 : 5;
 }
 
 hipError_t launch_gemm_small(int fmt, const void* blocks, const void* Xq8, float* Y, int64_t M,
@@ -1971,7 +1974,7 @@ hipError_t launch_gemm_small(int fmt, const void* blocks, const void* Xq8, float
   for (int64_t n0 = 0; n0 < N; n0 += 16) {
     hipError_t e;
     const int64_t nt = N - n0 < 16 ? N - n0 : 16;
-    if (QMAT_DECODE_MFMA && nt >= decode_mfma_min_tokens(fmt) && !decode_rows_takes(fmt, K, nt) &&
+    if (QMAT_DECODE_MFMA && nt >= decode_mfma_min_tokens(fmt, M) && !decode_rows_takes(fmt, K, nt) &&
         decode_mfma_fits(fmt, K)) {
       e = launch_decode_mfma(fmt, blocks, Xq8, Y, M, K, N, n0, stream);
       if (e != hipSuccess) return e;

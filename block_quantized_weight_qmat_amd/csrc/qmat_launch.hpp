@@ -38,10 +38,13 @@ hipError_t launch_gemv_batch(int fmt, const GemvJob* jobs, int64_t count, hipStr
 hipError_t launch_gemm_small(int fmt, const void* blocks, const void* Xq8, float* Y, int64_t M,
                              int64_t K, int64_t N, hipStream_t stream);
 
-// The decode batch on the matrix cores (decode.hip): Q4_0 or Q8_0 rows of
-// whole 256-element groups (K a positive multiple of 256); tokens n0 ..
-// min(N, n0 + 16) - 1 of one launch (sized for 5 to 16 of them).
+// The decode batch on the matrix cores (decode.hip): rows of whole
+// 256-element groups (K a positive multiple of 256) in any format; tokens
+// n0 .. min(N, n0 + 16) - 1 of one launch (sized for 5 to 16 of them).
+// decode_mfma_tall: whether M rows take its tall-matrix shape (more 16-row
+// workgroups than CUs).
 bool decode_mfma_fits(int fmt, int64_t K);
+bool decode_mfma_tall(int64_t M);
 hipError_t launch_decode_mfma(int fmt, const void* blocks, const void* Xq8, float* Y, int64_t M,
                               int64_t K, int64_t N, int64_t n0, hipStream_t stream);
 

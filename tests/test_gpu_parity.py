@@ -699,6 +699,9 @@ def test_gemm_decode_tall(q, fmt):
     if fmt == 1:
         # 5-8 tokens on rows too long for the row-per-wave kernel's LDS
         cases += [(4500, 20480, 8), (300, 20480, 6)]
+    if fmt == 2:
+        # Q4_K-style takes this shape from 5 tokens on tall matrices
+        cases += [(4200, 2304, 5), (5003, 4096, 8)]
     for M, K, N in cases:
         say(f"gemm decode tall fmt={fmt} M={M} K={K} N={N}")
         W = rng.normal(0, 0.02, (M, K)).astype(np.float32)
