@@ -87,7 +87,7 @@ struct DecX {
 // workgroup per CU (at most 256 workgroups): as many waves as 160 KB of LDS
 // allows with a ring of at least two stages (16, 12 or 8: the waves hide
 // each other's LDS and matrix-core latency), each with the deepest ring
-// that then fits. Taller matrices (kTall: more 16-row workgroups than CUs)
+// that then fits. Taller matrices (kDecTall: more 16-row workgroups than CUs)
 // take 4 waves with rings of 2 stages instead, 27-70 KB per workgroup, so
 // that two or more workgroups share a CU and hide each other's copy
 // latency; measured at 16 tokens, 11008 x 4096: Q4_0 17.7 -> 13.4 us, Q8_0
